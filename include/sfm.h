@@ -1,0 +1,161 @@
+/*
+ * sfm.h -- C ABI of libsfm: the folded, segmented selective scan of SF-Mamba
+ * and its companions, as hand-written HIP kernels for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Plain C: extern "C", only pointers, integers and enums; no C++ exception and
+ * no torch type crosses it.  Device pointers point to memory the CALLER owns
+ * (the library never allocates, frees or keeps a reference to device memory,
+ * and needs no workspace).  Every entry point that touches the GPU only
+ * enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ * returns without synchronising: device faults surface at the caller's next
+ * synchronisation.  Arguments are validated BEFORE any launch; a violation
+ * returns a non-zero status, launches nothing, and leaves a description for
+ * sfm_last_error() (thread-local).
+ *
+ * Page citations (the method has no published code; these web pages describe it):
+ *  [SBW] "Seeing Both Ways, Running One Way" (sungsoo.github.io), section 3.1
+ *        (selective SSM recurrence), 3.2 (aux head/tail tokens and their swap),
+ *        3.3 (batch folding and the periodic state reset), 8.1 (method list).
+ *  [TL]  "SF-Mamba：重新思考视觉 Mamba 的信息流与并行效率" (techloop.online),
+ *        sections "第一个模块：Auxiliary Patch Swapping", "第二个模块：Batch
+ *        Folding with Periodic State Reset" (incl. its conv-boundary part) and
+ *        "还有一个工程补充：Adaptive B1".
+ *  [GS]  "SF-Mamba: Rethinking State Space Model for Vision" (gist.science),
+ *        Technische Zusammenfassung 2.B.
+ *
+ * Layout conventions (channel-first, as the pages write the tensors):
+ *  - io tensors are C-contiguous; `io_dtype` says whether they hold float32 or
+ *    bfloat16 (raw IEEE bfloat16 bits).  Base pointers of io tensors must be
+ *    16-byte aligned (any tensor from a PyTorch allocation is).
+ *  - parameter tensors (A, D, biases, conv weights) are float32, C-contiguous.
+ *  - sample b of a batch of B = B1*B2 samples is the j-th segment of folded row
+ *    b1 when b = b1*B2 + j ([SBW] 3.3 leaves the order open; any fixed order
+ *    gives the same per-sample result).  The fold is never materialised.
+ */
+#ifndef SFM_H
+#define SFM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SFM_OK = 0,
+    SFM_ERR_NULL = 1,         /* a required pointer is NULL                        */
+    SFM_ERR_SHAPE = 2,        /* a size is out of range or inconsistent            */
+    SFM_ERR_DTYPE = 3,        /* io_dtype not one of sfm_dtype                     */
+    SFM_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement       */
+    SFM_ERR_HIP = 5,          /* the HIP runtime reported an error at launch       */
+    SFM_ERR_ALIAS = 6,        /* an output overlaps an input it must not overlap   */
+    SFM_ERR_ALIGN = 7         /* an io base pointer is not 16-byte aligned         */
+} sfm_status;
+
+typedef enum { SFM_F32 = 0, SFM_BF16 = 1 } sfm_dtype;
+typedef enum { SFM_ACT_NONE = 0, SFM_ACT_SILU = 1 } sfm_act;
+typedef enum { SFM_AUX_PAD = 0, SFM_AUX_SWAP = 1 } sfm_aux_mode;
+
+/* Largest state size and conv width the kernels are built for. */
+#define SFM_MAX_N 16
+#define SFM_MAX_K 8
+
+/*
+ * sfm_selective_scan_fwd -- selective scan over batch-folded rows with the
+ * periodic state reset.  [SBW] 3.1: h_t = Abar_t h_{t-1} + Bbar_t x_t,
+ * y_t = C_t h_t; [SBW] 3.3 / [TL] "第二个模块": the batch is folded into
+ * B1 rows of length B2*L and Abar is zero at every sample start (t mod L == 0),
+ * which keeps the samples independent ([GS] 2.B).  Discretization (zero-order
+ * hold of Mamba): Abar = exp(Delta*A[d,n]), Bbar*x = Delta*B[b,n,t]*u[b,d,t];
+ * Delta = softplus(delta + delta_bias[d]) (beta 1, threshold 20) when
+ * delta_softplus != 0, else delta + delta_bias[d]; y += Dskip[d]*u.
+ * The reset is applied as a state re-initialisation, so non-finite values in
+ * one sample never reach another.
+ *
+ * Optional fused conv ([TL] conv-boundary part, [SBW] 8.1 item 5): when
+ * conv_w != NULL, `u` holds the conv INPUT x and the scan uses
+ *   u[b,d,t] = act(conv_b[d] + sum_{j<conv_k} conv_w[d,j] * x[b,d,t+j-conv_pad_left])
+ * with taps outside the sample ([0, L)) reading zero; u stays in fp32 registers.
+ *
+ * Arguments (device pointers unless noted):
+ *   u          [B1*B2, D, L] io   scan input, or the conv input if conv_w != NULL
+ *   delta      [B1*B2, D, L] io   raw step input (before bias and softplus)
+ *   A          [D, N] f32         state matrix diagonal (normally negative)
+ *   Bm, Cm     [B1*B2, N, L] io   input and output projections, shared by all D
+ *   Dskip      [D] f32 or NULL    skip weight (NULL = 0)
+ *   delta_bias [D] f32 or NULL    (NULL = 0)
+ *   delta_softplus                0 or 1
+ *   conv_w     [D, conv_k] f32 or NULL (NULL = no fused conv)
+ *   conv_b     [D] f32 or NULL
+ *   conv_k     1..SFM_MAX_K (ignored without conv); conv_pad_left in [0, conv_k)
+ *   conv_act   sfm_act
+ *   y          [B1*B2, D, L] io   output; must not overlap any input
+ *   B1, B2     folded rows and samples per row (B = B1*B2), >= 1
+ *   D          channels >= 1;  N  state size 1..SFM_MAX_N;  L  per-sample length (T+2) >= 1
+ *   io_dtype   sfm_dtype of u, delta, Bm, Cm and y
+ *   stream     hipStream_t or NULL
+ * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN (nothing launched) or HIP.
+ */
+sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                                  const void* Cm, const float* Dskip, const float* delta_bias,
+                                  int delta_softplus, const float* conv_w, const float* conv_b,
+                                  int conv_k, int conv_pad_left, int conv_act, void* y, int64_t B1,
+                                  int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype, void* stream);
+
+/*
+ * sfm_dwconv1d_fold -- boundary-masked depthwise conv1d over folded rows
+ * ([TL] "第二个模块", conv-boundary part; [SBW] 8.1 item 5):
+ *   out[b,d,t] = act(bias[d] + sum_{j<K} w[d,j] * x[b,d,t+j-pad_left]),
+ * a tap counting only when it stays inside the same sample's segment of the
+ * folded row (t+j-pad_left in [0, L)); otherwise it reads zero.
+ *   x, out [B1*B2, D, L] io (out must not overlap x);  w [D, K] f32;
+ *   bias [D] f32 or NULL;  K 1..SFM_MAX_K;  pad_left in [0, K);  act sfm_act.
+ */
+sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, void* out, int64_t B1,
+                             int64_t B2, int64_t D, int64_t L, int K, int pad_left, int act, int io_dtype,
+                             void* stream);
+
+/*
+ * sfm_aux_pad_swap -- the auxiliary head/tail tokens ([SBW] 3.2, [TL]
+ * "第一个模块").
+ *  mode SFM_AUX_PAD:  in [B, D, T] -> out [B, D, T+2]; out[..,0] = out[..,T+1] =
+ *      mean over the T patch tokens (float64 sum in index order, divided by T,
+ *      rounded once to the io type, ties to even); out[..,1+t] = in[..,t].
+ *      out must not overlap in.  T >= 1.
+ *  mode SFM_AUX_SWAP: in, out [B, D, T+2] with T here meaning L-2 (T >= -1 so
+ *      L = T+2 >= 1): out = in with positions 0 and L-1 exchanged (the next
+ *      layer's head is this layer's tail output and vice versa).  out == in
+ *      performs the two-element exchange in place; otherwise out must not
+ *      overlap in.
+ * Bit-exact in both modes.
+ */
+sfm_status sfm_aux_pad_swap(const void* in, void* out, int64_t B, int64_t D, int64_t T, int mode,
+                            int io_dtype, void* stream);
+
+/*
+ * sfm_pick_b1 -- adaptive fold ratio ([TL] "还有一个工程补充：Adaptive B1";
+ * [SBW] 8.1 item 6): an offline lookup table keyed by batch size, sequence
+ * length, channels and state size, here built by timing the scan on MI355X.
+ * Host only (no device call).  Writes B1 (a divisor of B) to *B1_out.
+ * Lookup: exact key, else the nearest key in (log2 B, log2 L, log2 D, N); the
+ * table's B2 is then reduced to the largest divisor of B not above it.
+ * The environment variable SFM_B1_TABLE may name a text file of lines
+ * "B L D N B2" that is consulted before the built-in table.
+ */
+sfm_status sfm_pick_b1(int64_t B, int64_t L, int64_t D, int64_t N, int64_t* B1_out);
+
+/* Static text for a status code. */
+const char* sfm_status_string(sfm_status s);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* sfm_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int sfm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFM_H */

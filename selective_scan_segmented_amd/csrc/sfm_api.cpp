@@ -1,0 +1,261 @@
+// sfm_api.cpp -- the C ABI of libsfm (declared in include/sfm.h): argument
+// validation, dispatch to the HIP kernels, error reporting and the adaptive-B1
+// lookup table.  Nothing here allocates device memory or synchronises.
+#include "sfm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "sfm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sfm_status fail(sfm_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+sfm_status ok() {
+    g_last_error.clear();
+    return SFM_OK;
+}
+
+sfm_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(SFM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int io_bytes(int io_dtype) { return io_dtype == SFM_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;
+};
+
+Range rng(const char* name, const void* p, int64_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// products of positive sizes that must stay well inside int32 indexing of one
+// (sample, channel) row and int64 element counts overall
+bool sane(int64_t v, int64_t hi) { return v >= 1 && v <= hi; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sfm_status_string(sfm_status s) {
+    switch (s) {
+        case SFM_OK: return "ok";
+        case SFM_ERR_NULL: return "null pointer";
+        case SFM_ERR_SHAPE: return "invalid shape";
+        case SFM_ERR_DTYPE: return "invalid dtype";
+        case SFM_ERR_UNSUPPORTED: return "unsupported";
+        case SFM_ERR_HIP: return "HIP runtime error";
+        case SFM_ERR_ALIAS: return "output overlaps an input";
+        case SFM_ERR_ALIGN: return "io pointer not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+const char* sfm_last_error(void) { return g_last_error.c_str(); }
+
+int sfm_version(void) { return 100; }
+
+sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                                  const void* Cm, const float* Dskip, const float* delta_bias,
+                                  int delta_softplus, const float* conv_w, const float* conv_b, int conv_k,
+                                  int conv_pad_left, int conv_act, void* y, int64_t B1, int64_t B2, int64_t D,
+                                  int64_t N, int64_t L, int io_dtype, void* stream) {
+    if (!u || !delta || !A || !Bm || !Cm || !y)
+        return fail(SFM_ERR_NULL, "sfm_selective_scan_fwd: u, delta, A, Bm, Cm and y are required");
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16)
+        return fail(SFM_ERR_DTYPE, "sfm_selective_scan_fwd: io_dtype %d", io_dtype);
+    if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24))
+        return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: B1=%lld B2=%lld D=%lld L=%lld out of range",
+                    (long long)B1, (long long)B2, (long long)D, (long long)L);
+    if (N < 1 || N > SFM_MAX_N)
+        return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: N=%lld not in [1, %d]", (long long)N, SFM_MAX_N);
+    if (B2 * L > (1LL << 30))
+        return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: folded row B2*L=%lld too long", (long long)(B2 * L));
+    if (B1 * B2 * D * L > (1LL << 40))
+        return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: tensor too large");
+    if (delta_softplus != 0 && delta_softplus != 1)
+        return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: delta_softplus must be 0 or 1");
+    if (conv_w) {
+        if (conv_k < 1 || conv_k > SFM_MAX_K)
+            return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: conv_k=%d not in [1, %d]", conv_k, SFM_MAX_K);
+        if (conv_pad_left < 0 || conv_pad_left >= conv_k)
+            return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: conv_pad_left=%d not in [0, %d)", conv_pad_left,
+                        conv_k);
+        if (conv_act != SFM_ACT_NONE && conv_act != SFM_ACT_SILU)
+            return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd: conv_act=%d", conv_act);
+    }
+    if (!aligned16(u) || !aligned16(delta) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(y))
+        return fail(SFM_ERR_ALIGN, "sfm_selective_scan_fwd: io base pointers must be 16-byte aligned");
+    const int64_t B = B1 * B2;
+    const int eb = io_bytes(io_dtype);
+    const Range ry = rng("y", y, B * D * L * eb);
+    const Range ins[] = {rng("u", u, B * D * L * eb), rng("delta", delta, B * D * L * eb),
+                         rng("Bm", Bm, B * N * L * eb), rng("Cm", Cm, B * N * L * eb),
+                         rng("A", A, D * N * 4)};
+    for (const Range& r : ins)
+        if (overlap(ry, r)) return fail(SFM_ERR_ALIAS, "sfm_selective_scan_fwd: y overlaps %s", r.name);
+
+    sfm::ScanParams p{};
+    p.u = u;
+    p.delta = delta;
+    p.A = A;
+    p.Bm = Bm;
+    p.Cm = Cm;
+    p.Dskip = Dskip;
+    p.dbias = delta_bias;
+    p.conv_w = conv_w;
+    p.conv_b = conv_w ? conv_b : nullptr;
+    p.y = y;
+    p.B1 = (int)B1;
+    p.B2 = (int)B2;
+    p.D = (int)D;
+    p.N = (int)N;
+    p.L = (int)L;
+    p.K = conv_w ? conv_k : 1;
+    p.P = conv_w ? conv_pad_left : 0;
+    p.act = conv_w ? conv_act : 0;
+    p.softplus = delta_softplus;
+    int waves_hint = 0, ch_hint = 0;
+    if (const char* e = std::getenv("SFM_SCAN_WAVES")) waves_hint = std::atoi(e);
+    if (const char* e = std::getenv("SFM_SCAN_CHUNK")) ch_hint = std::atoi(e);
+    if (!sfm::plan_scan(p, eb, waves_hint, ch_hint))
+        return fail(SFM_ERR_UNSUPPORTED, "sfm_selective_scan_fwd: no launch plan fits LDS for this shape");
+    return hip_status(sfm::launch_scan(p, io_dtype, static_cast<hipStream_t>(stream)), "sfm_selective_scan_fwd");
+}
+
+sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, void* out, int64_t B1, int64_t B2,
+                             int64_t D, int64_t L, int K, int pad_left, int act, int io_dtype, void* stream) {
+    if (!x || !w || !out) return fail(SFM_ERR_NULL, "sfm_dwconv1d_fold: x, w and out are required");
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16)
+        return fail(SFM_ERR_DTYPE, "sfm_dwconv1d_fold: io_dtype %d", io_dtype);
+    if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24) ||
+        B1 * B2 * D * L > (1LL << 40))
+        return fail(SFM_ERR_SHAPE, "sfm_dwconv1d_fold: B1=%lld B2=%lld D=%lld L=%lld out of range",
+                    (long long)B1, (long long)B2, (long long)D, (long long)L);
+    if (K < 1 || K > SFM_MAX_K) return fail(SFM_ERR_SHAPE, "sfm_dwconv1d_fold: K=%d not in [1, %d]", K, SFM_MAX_K);
+    if (pad_left < 0 || pad_left >= K)
+        return fail(SFM_ERR_SHAPE, "sfm_dwconv1d_fold: pad_left=%d not in [0, %d)", pad_left, K);
+    if (act != SFM_ACT_NONE && act != SFM_ACT_SILU) return fail(SFM_ERR_SHAPE, "sfm_dwconv1d_fold: act=%d", act);
+    if (!aligned16(x) || !aligned16(out))
+        return fail(SFM_ERR_ALIGN, "sfm_dwconv1d_fold: io base pointers must be 16-byte aligned");
+    const int64_t bytes = B1 * B2 * D * L * io_bytes(io_dtype);
+    if (overlap(rng("out", out, bytes), rng("x", x, bytes)))
+        return fail(SFM_ERR_ALIAS, "sfm_dwconv1d_fold: out overlaps x");
+    return hip_status(sfm::launch_dwconv1d(x, w, bias, out, B1, B2, D, L, K, pad_left, act, io_dtype,
+                                           static_cast<hipStream_t>(stream)),
+                      "sfm_dwconv1d_fold");
+}
+
+sfm_status sfm_aux_pad_swap(const void* in, void* out, int64_t B, int64_t D, int64_t T, int mode, int io_dtype,
+                            void* stream) {
+    if (!in || !out) return fail(SFM_ERR_NULL, "sfm_aux_pad_swap: in and out are required");
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16)
+        return fail(SFM_ERR_DTYPE, "sfm_aux_pad_swap: io_dtype %d", io_dtype);
+    if (mode != SFM_AUX_PAD && mode != SFM_AUX_SWAP) return fail(SFM_ERR_SHAPE, "sfm_aux_pad_swap: mode %d", mode);
+    if (!sane(B, 1 << 24) || !sane(D, 1 << 20))
+        return fail(SFM_ERR_SHAPE, "sfm_aux_pad_swap: B=%lld D=%lld out of range", (long long)B, (long long)D);
+    if (mode == SFM_AUX_PAD ? (T < 1 || T > (1 << 24)) : (T < -1 || T > (1 << 24)))
+        return fail(SFM_ERR_SHAPE, "sfm_aux_pad_swap: T=%lld out of range for mode %d", (long long)T, mode);
+    if (B * D * (T + 2) > (1LL << 40)) return fail(SFM_ERR_SHAPE, "sfm_aux_pad_swap: tensor too large");
+    if (!aligned16(in) || !aligned16(out))
+        return fail(SFM_ERR_ALIGN, "sfm_aux_pad_swap: io base pointers must be 16-byte aligned");
+    const int eb = io_bytes(io_dtype);
+    const int64_t L = T + 2;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mode == SFM_AUX_PAD) {
+        if (overlap(rng("out", out, B * D * L * eb), rng("in", in, B * D * T * eb)))
+            return fail(SFM_ERR_ALIAS, "sfm_aux_pad_swap: PAD output overlaps its input");
+        return hip_status(sfm::launch_aux_pad(in, out, B * D, T, io_dtype, s), "sfm_aux_pad_swap(PAD)");
+    }
+    if (in != out && overlap(rng("out", out, B * D * L * eb), rng("in", in, B * D * L * eb)))
+        return fail(SFM_ERR_ALIAS, "sfm_aux_pad_swap: SWAP output partially overlaps its input");
+    return hip_status(sfm::launch_aux_swap(in, out, B * D, L, io_dtype, s), "sfm_aux_pad_swap(SWAP)");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ adaptive B1
+namespace {
+
+struct B1Entry {
+    int64_t B, L, D, N, B2;
+};
+
+#include "b1_table.inc"
+
+std::vector<B1Entry> load_env_table() {
+    std::vector<B1Entry> v;
+    const char* path = std::getenv("SFM_B1_TABLE");
+    if (!path || !*path) return v;
+    FILE* f = std::fopen(path, "r");
+    if (!f) return v;
+    char line[256];
+    while (std::fgets(line, sizeof(line), f)) {
+        long long b, l, d, n, b2;
+        if (line[0] == '#') continue;
+        if (std::sscanf(line, "%lld %lld %lld %lld %lld", &b, &l, &d, &n, &b2) == 5 && b2 >= 1)
+            v.push_back(B1Entry{b, l, d, n, b2});
+    }
+    std::fclose(f);
+    return v;
+}
+
+double key_distance(const B1Entry& e, int64_t B, int64_t L, int64_t D, int64_t N) {
+    auto lg = [](double v) { return std::log2(v); };
+    const double db = lg((double)e.B) - lg((double)B);
+    const double dl = lg((double)e.L) - lg((double)L);
+    const double dd = lg((double)e.D) - lg((double)D);
+    const double dn = ((double)e.N - (double)N) / 4.0;
+    return db * db + dl * dl + dd * dd + dn * dn;
+}
+
+}  // namespace
+
+extern "C" sfm_status sfm_pick_b1(int64_t B, int64_t L, int64_t D, int64_t N, int64_t* B1_out) {
+    if (!B1_out) return fail(SFM_ERR_NULL, "sfm_pick_b1: B1_out is required");
+    if (!sane(B, 1 << 24) || !sane(L, 1 << 24) || !sane(D, 1 << 20) || N < 1 || N > SFM_MAX_N)
+        return fail(SFM_ERR_SHAPE, "sfm_pick_b1: B=%lld L=%lld D=%lld N=%lld out of range", (long long)B,
+                    (long long)L, (long long)D, (long long)N);
+    std::vector<B1Entry> table = load_env_table();
+    for (const B1Entry& e : kB1Table) table.push_back(e);
+    int64_t want_b2 = 1;
+    double best = 1e300;
+    for (const B1Entry& e : table) {  // first entry wins ties: the env file precedes the built-in table
+        const double dist = key_distance(e, B, L, D, N);
+        if (dist < best) {
+            best = dist;
+            want_b2 = e.B2;
+        }
+    }
+    int64_t b2 = 1;
+    for (int64_t c = 1; c <= want_b2 && c <= B; ++c)
+        if (B % c == 0) b2 = c;
+    *B1_out = B / b2;
+    return ok();
+}

@@ -1,0 +1,85 @@
+// sfm_device.h -- device-side helpers shared by the libsfm HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfm {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- io element types
+// io tensors hold float32 or bfloat16; kernels are instantiated for both and do
+// all arithmetic in float32 (state, accumulation) or float64 (pad mean).
+template <typename T> struct Io;
+template <> struct Io<float> {
+    static __device__ __forceinline__ float load(const float* p) { return *p; }
+    static __device__ __forceinline__ float to_f32(float v) { return v; }
+    static __device__ __forceinline__ float from_f32(float v) { return v; }
+    static __device__ __forceinline__ float from_f64(double v) { return (float)v; }  // RNE
+    static __device__ __forceinline__ float zero() { return 0.0f; }
+};
+template <> struct Io<__bf16> {
+    static __device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
+    static __device__ __forceinline__ __bf16 from_f32(float v) { return (__bf16)v; }  // RNE (v_cvt_pk_bf16_f32)
+    // float64 -> bfloat16 in one rounding: round to float32 with round-to-odd
+    // (truncate, then set the last bit when inexact), then to bfloat16 with
+    // round-to-nearest-even.  24 >= 8 + 2 bits makes the two-step result equal
+    // to a direct rounding (Boldo & Melquiond, "Emulation of FMA and correctly
+    // rounded sums: proved algorithms using rounding to odd", 2008).
+    static __device__ __forceinline__ __bf16 from_f64(double v) {
+        float f = (float)v;
+        double back = (double)f;
+        if (back != v && f == f) {
+            uint32_t bits = __float_as_uint(f);
+            if (__builtin_fabs(back) > __builtin_fabs(v)) bits -= 1u;  // step toward zero
+            bits |= 1u;
+            f = __uint_as_float(bits);
+        }
+        return (__bf16)f;
+    }
+    static __device__ __forceinline__ __bf16 zero() { return (__bf16)0.0f; }
+};
+
+template <typename T> __device__ __forceinline__ float to_f32(T v) { return Io<T>::to_f32(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v) { return Io<T>::from_f32(v); }
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// softplus(v) = log(1 + e^v) (PyTorch's beta = 1; its threshold 20 changes the
+// float32 result by less than half an ulp, so the identity branch is implied).
+// Evaluated as max(v, 0) + log1p(e^{-|v|}): the exponent never overflows, and
+// log1p(e) for e in (0, 1] is log(w) + c with w = fl(1 + e) and c = e - (w - 1)
+// the exact rounding error of that sum (first-order correction; |c| <= 2^-24,
+// and dividing it by w in [1, 2] would change the result by less than 2^-25).
+// Returns softplus(v) * log2(e), the form the exp2-based discretization uses.
+__device__ __forceinline__ float softplus_log2e(float v) {
+    const float e = exp2_fast(-__builtin_fabsf(v) * kLog2e);
+    const float w = 1.0f + e;
+    const float c = e - (w - 1.0f);
+    const float l2 = log2_fast(w) + c * kLog2e;
+    return __builtin_fmaf(__builtin_fmaxf(v, 0.0f), kLog2e, l2);
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + exp2_fast(-v * kLog2e)); }
+
+// Compiler-level ordering point for LDS traffic between lanes of ONE wave
+// (a wavefront's LDS operations execute in issue order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// floor(e / len) for 0 <= e < 2^22 and len >= 1, via a float reciprocal: the
+// true quotient (e + 0.5) / len is at least 0.5 / len away from an integer,
+// while the float32 error of the product is at most (e / len) * 2^-23.
+__device__ __forceinline__ int div_small(int e, float inv_len) {
+    return (int)(((float)e + 0.5f) * inv_len);
+}
+
+}  // namespace sfm

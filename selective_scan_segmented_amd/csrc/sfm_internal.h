@@ -1,0 +1,46 @@
+// sfm_internal.h -- host/device contract between the C-ABI layer (sfm_api.cpp)
+// and the HIP kernels of libsfm.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfm {
+
+// Launch description of one selective-scan call (see scan.hip for the mapping).
+struct ScanParams {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const float* dbias;
+    const float* conv_w;
+    const float* conv_b;
+    void* y;
+    int B1, B2, D, N, L;
+    int K, P, act, softplus;
+    // plan (filled by plan_scan)
+    int ns;          // compiled state count (4, 8 or 16) >= N
+    int tiles;       // ceil(D / 64)
+    int waves;       // waves per workgroup = pieces per folded row
+    int piece;       // folded positions per wave
+    int need_carry;  // 1 when some piece starts inside a sample
+    int ch;          // positions per LDS chunk
+    int flat;        // 1: a chunk holds whole sample rows (contiguous slabs)
+    int xrs, drs;    // LDS row strides (elements) of the x and delta/y stages
+    int xs_bytes, ds_bytes, stage_bytes, lds_bytes;
+};
+
+// Fills the plan fields; waves_hint / ch_hint <= 0 select automatically.
+bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint);
+hipError_t launch_scan(const ScanParams& p, int io_dtype, hipStream_t stream);
+
+hipError_t launch_dwconv1d(const void* x, const float* w, const float* bias, void* out, int64_t B1, int64_t B2,
+                           int64_t D, int64_t L, int K, int pad_left, int act, int io_dtype, hipStream_t stream);
+
+hipError_t launch_aux_pad(const void* in, void* out, int64_t rows, int64_t T, int io_dtype, hipStream_t stream);
+hipError_t launch_aux_swap(const void* in, void* out, int64_t rows, int64_t L, int io_dtype, hipStream_t stream);
+
+}  // namespace sfm

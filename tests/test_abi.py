@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every symbol include/sfm.h declares, and
+rejects invalid arguments before any launch (host-only paths; no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import selective_scan_segmented_amd as sfm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfm.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, HIP, ALIAS, ALIGN = range(8)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sfm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sfm.library_path()):
+        from selective_scan_segmented_amd import build
+        build.build(verbose=False)
+    return sfm.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert {"sfm_selective_scan_fwd", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1"} <= set(syms)
+    out = subprocess.run(["nm", "-D", "--defined-only", sfm.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sfm_[a-z0-9_]+)\b", out))
+    missing = [s for s in syms if s not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for s in syms:
+        assert hasattr(lib, s)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.sfm_status_string(0) == b"ok"
+    assert b"null" in lib.sfm_status_string(1)
+    assert sfm.sfm_version() >= 100
+
+
+P = 0x10000  # fake, never dereferenced: every call below fails validation first
+
+
+def scan(lib, **kw):
+    a = dict(u=P, delta=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P, Dskip=None, dbias=None, sp=1, cw=None, cb=None,
+             k=4, pad=1, act=0, y=6 * P, B1=2, B2=2, D=4, N=4, L=10, io=0, stream=None)
+    a.update(kw)
+    return lib.sfm_selective_scan_fwd(a["u"], a["delta"], a["A"], a["Bm"], a["Cm"], a["Dskip"], a["dbias"], a["sp"],
+                                      a["cw"], a["cb"], a["k"], a["pad"], a["act"], a["y"], a["B1"], a["B2"],
+                                      a["D"], a["N"], a["L"], a["io"], a["stream"])
+
+
+def test_scan_validation(lib):
+    assert scan(lib, u=None) == NULL
+    assert scan(lib, y=None) == NULL
+    assert scan(lib, io=7) == DTYPE
+    assert scan(lib, N=0) == SHAPE
+    assert scan(lib, N=17) == SHAPE
+    assert scan(lib, L=0) == SHAPE
+    assert scan(lib, B1=0) == SHAPE
+    assert scan(lib, B2=0) == SHAPE
+    assert scan(lib, D=0) == SHAPE
+    assert scan(lib, sp=2) == SHAPE
+    assert scan(lib, cw=7 * P, k=0) == SHAPE
+    assert scan(lib, cw=7 * P, k=9) == SHAPE
+    assert scan(lib, cw=7 * P, k=4, pad=4) == SHAPE
+    assert scan(lib, cw=7 * P, k=4, pad=-1) == SHAPE
+    assert scan(lib, cw=7 * P, act=3) == SHAPE
+    assert scan(lib, u=P + 2) == ALIGN
+    assert scan(lib, y=P) == ALIAS            # y on top of u
+    assert scan(lib, y=5 * P + 16) == ALIAS   # y inside Cm
+    assert b"overlaps" in lib.sfm_last_error()
+
+
+def test_conv_validation(lib):
+    f = lib.sfm_dwconv1d_fold
+    assert f(None, P, None, 2 * P, 1, 1, 4, 10, 4, 1, 0, 0, None) == NULL
+    assert f(P, P, None, 2 * P, 1, 1, 4, 10, 0, 0, 0, 0, None) == SHAPE
+    assert f(P, P, None, 2 * P, 1, 1, 4, 10, 4, 4, 0, 0, None) == SHAPE
+    assert f(P, P, None, 2 * P, 1, 1, 4, 10, 4, 1, 2, 0, None) == SHAPE
+    assert f(P, P, None, 2 * P, 1, 1, 4, 10, 4, 1, 0, 5, None) == DTYPE
+    assert f(P, P, None, P + 16, 1, 1, 4, 10, 4, 1, 0, 0, None) == ALIAS
+    assert f(P + 4, P, None, 2 * P, 1, 1, 4, 10, 4, 1, 0, 0, None) == ALIGN
+
+
+def test_aux_validation(lib):
+    f = lib.sfm_aux_pad_swap
+    assert f(None, P, 2, 3, 4, 0, 0, None) == NULL
+    assert f(P, 2 * P, 2, 3, 0, 0, 0, None) == SHAPE      # PAD needs T >= 1
+    assert f(P, 2 * P, 2, 3, 4, 2, 0, None) == SHAPE      # bad mode
+    assert f(P, 2 * P, 2, 3, 4, 0, 3, None) == DTYPE
+    assert f(P, P + 16, 2, 3, 4, 0, 0, None) == ALIAS     # PAD out overlaps in
+    assert f(P, P + 8, 2, 3, 4, 0, 0, None) == ALIGN
+    assert f(P, P + 16, 2, 3, 4, 1, 0, None) == ALIAS     # SWAP partial overlap
+
+
+def test_pick_b1_returns_divisor(lib):
+    for B, L, D, N in [(256, 51, 640, 8), (256, 198, 320, 8), (512, 198, 512, 16), (16, 4002, 320, 16),
+                       (7, 51, 640, 8), (1, 10, 16, 4), (96, 100, 256, 8)]:
+        b1 = sfm.sfm_pick_b1(B, L, D, N)
+        assert 1 <= b1 <= B and B % b1 == 0
+    with pytest.raises(sfm.SFMError):
+        sfm.sfm_pick_b1(0, 51, 640, 8)
+    assert lib.sfm_pick_b1(4, 10, 16, 4, None) == NULL
+
+
+def test_pick_b1_env_table_overrides(lib, tmp_path, monkeypatch):
+    t = tmp_path / "table.txt"
+    t.write_text("# B L D N B2\n256 51 640 8 8\n")
+    monkeypatch.setenv("SFM_B1_TABLE", str(t))
+    assert sfm.sfm_pick_b1(256, 51, 640, 8) == 32
+    # nearest key, then the largest divisor of B not above the table's B2
+    assert sfm.sfm_pick_b1(12, 51, 640, 8) == 2
