@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Throughput of the folded, segmented selective-scan hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic stage-shaped input:
+  adaptive-B1 pick (host table) -> aux pad (stage entry, T -> T+2)
+  -> fused boundary-masked depthwise conv + folded segmented selective scan
+  -> aux head/tail swap (in place, ready for the next layer).
+Inputs are resident in HBM before the timed region; the steps cycle through
+enough independent input sets (>= 2 GiB) that no set is still in the 256 MB
+Infinity Cache when it comes round again.
+
+Prints ONE JSON line.  `value` is token*channels per second (token*channels =
+B * D * (T + 2), aux tokens included).  The `roofline` object is for the scan
+kernel, timed live with HIP events around each of its launches on the stream
+it runs on; the `hbm` object gives the same kernel's algorithmic bytes against
+the HBM peak; `cpu_baseline` times the CPU oracle on the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload stage4] [--b2 B2]
+    python bench.py --mode copy    # plain 1 GiB copy, used to calibrate HBM counters
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 32 lanes/clock x 2.4 GHz
+VALU_PEAK_TSLOT = 256 * 4 * 32 * 2.4e9 / 1e12
+TRANS_SLOTS = 4  # v_exp_f32 / v_log_f32 issue at a quarter of the fp32 rate
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs, called directly."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the same libamdhip64 torch uses)
+        self.lib = None
+        for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+            try:
+                self.lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if self.lib is None:
+            raise RuntimeError("libamdhip64 not found")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e
+
+    def record(self, e, stream):
+        self.lib.hipEventRecord(e, stream)
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        self.lib.hipEventSynchronize(b)
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+
+def scan_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("scan.hip", "sfm_device.h", "sfm_internal.h"):
+        with open(os.path.join(ROOT, "selective_scan_segmented_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, b2: int):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current scan source and the same launch."""
+    path = os.path.join(ROOT, "profiles", f"scan_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = {k: re.search(rf"^{k}:\s*(\S+)", text, re.M) for k in ("source_hash", "b2", "bytes_per_launch")}
+    if not all(m.values()):
+        return None
+    if m["source_hash"].group(1) != scan_source_hash() or int(m["b2"].group(1)) != b2:
+        return None
+    return float(m["bytes_per_launch"].group(1))
+
+
+def alg_scan_bytes(w, io_bytes: int) -> int:
+    """Algorithmic HBM bytes of one fused conv+scan launch: the conv input, delta
+    and y once each, B and C once per sample, and the per-channel parameters."""
+    tc = w.B * w.D * w.L
+    return tc * 3 * io_bytes + 2 * w.B * w.N * w.L * io_bytes + w.D * (w.N + 3 + w.K) * 4
+
+
+def alg_scan_slots(w) -> int:
+    """Algorithmic VALU work of the fused conv+scan, in fp32 issue slots:
+    per (token, channel) N exp (quarter rate) and 4N mul/fma for the N states,
+    softplus (exp + log, 6 fp32 ops), K conv FMAs, bias add, Delta*u, D*u."""
+    per_tc = w.N * (TRANS_SLOTS + 4) + 2 * TRANS_SLOTS + 6 + w.K + 3
+    return w.B * w.D * w.L * per_tc
+
+
+def cpu_baseline(w, li, seconds: float):
+    import numpy as np
+
+    import oracle
+    threads = oracle.threads(max(1, min(16, os.cpu_count() or 1)))
+    x = li.as_f64("x")
+    args = [li.as_f64(k) for k in ("delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "conv_w")]
+    # bounded sample: whole samples taken from the front of the batch, sized so
+    # one pass of the oracle chain takes on the order of a second or two
+    nb = max(1, min(w.B, int(round(w.B * 0.25))))
+    xs = x[:nb]
+    d, A, Bm, Cm, Dk, bias, cw = args
+    d, Bm, Cm = d[:nb], Bm[:nb], Cm[:nb]
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        xp = oracle.aux_pad(xs, w.io)
+        y = oracle.layer(xp, d, A, Bm, Cm, Dk, bias, cw, pad_left=1, nthreads=threads)
+        oracle.aux_swap(oracle.round_io(y, w.io))
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 1000:
+            break
+    tcs = passes * nb * w.D * w.L / el
+    del np
+    return {"value": tcs, "unit": "token*channels/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nb} of {w.B} samples (all {w.D} channels, L={w.L}) x {passes} passes of the fp64 oracle "
+                      f"chain pad->conv->scan->swap, {el:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="stage4")
+    ap.add_argument("--b2", type=int, default=0, help="fold ratio; 0 = adaptive-B1 table")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets; 0 = enough for 2 GiB")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["step", "copy", "scan"], default="step",
+                    help="step: the whole hot path (default); scan: the scan launch alone; "
+                         "copy: a plain 1 GiB copy (counter calibration)")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the hot path shards by sample "
+                                   "(no collectives), so N GPUs would run N independent copies of this "
+                                   "bench -- run it with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import selective_scan_segmented_amd as sfm
+    from selective_scan_segmented_amd import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    if a.mode == "copy":
+        n = 1 << 29  # 1 GiB of bf16
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sp)
+        reps = 10
+        for _ in range(reps):
+            dst.copy_(src)
+        hip.record(e1, sp)
+        ms = hip.elapsed_ms(e0, e1) / reps
+        print(json.dumps({"mode": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "ms": ms,
+                          "GBps": 4 * n / ms / 1e6}))
+        return
+
+    w = synth.WORKLOADS[a.workload]
+    io_bytes = 4 if w.io == "f32" else 2
+    B1 = sfm.sfm_pick_b1(w.B, w.L, w.D, w.N)
+    b2 = a.b2 if a.b2 > 0 else w.B // B1
+    if w.B % b2:
+        raise SystemExit(f"B2={b2} must divide B={w.B}")
+    li = synth.make_layer(w, seed=synth.WORKLOAD_ORDER.index(a.workload))
+
+    def dev_io(arr):
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+    base = {"x": dev_io(li.x), "delta": dev_io(li.delta), "Bm": dev_io(li.Bm), "Cm": dev_io(li.Cm)}
+    prm = {k: torch.from_numpy(getattr(li, k)).to(dev) for k in ("A", "Dskip", "delta_bias", "conv_w")}
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + 2 * w.B * w.D * w.L * io_bytes
+    nsets = a.sets if a.sets > 0 else max(2, math.ceil((2 << 30) / set_bytes))
+    sets = []
+    for _ in range(nsets):
+        s = {k: v.clone() for k, v in base.items()}
+        s["xp"] = torch.empty((w.B, w.D, w.L), dtype=base["x"].dtype, device=dev)
+        s["y"] = torch.empty_like(s["xp"])
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    lib = sfm.load_library()
+    io = 0 if w.io == "f32" else 1
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    calls = []
+    for s in sets:
+        pad_args = (vp(s["x"]), vp(s["xp"]), w.B, w.D, w.T, 0, io, sp)
+        scan_args = (vp(s["xp"]), vp(s["delta"]), vp(prm["A"]), vp(s["Bm"]), vp(s["Cm"]), vp(prm["Dskip"]),
+                     vp(prm["delta_bias"]), 1, vp(prm["conv_w"]), None, w.K, 1, 0, vp(s["y"]),
+                     w.B // b2, b2, w.D, w.N, w.L, io, sp)
+        swap_args = (vp(s["y"]), vp(s["y"]), w.B, w.D, w.L - 2, 1, io, sp)
+        calls.append((pad_args, scan_args, swap_args))
+    b1_out = ctypes.c_int64()
+
+    def step(i, ev=None):
+        pad_args, scan_args, swap_args = calls[i % nsets]
+        if a.mode == "step":
+            lib.sfm_pick_b1(w.B, w.L, w.D, w.N, ctypes.byref(b1_out))
+            rc = lib.sfm_aux_pad_swap(*pad_args)
+            if rc:
+                raise RuntimeError(f"pad failed: {lib.sfm_last_error().decode()}")
+        if ev is not None:
+            hip.record(ev[0], sp)
+        rc = lib.sfm_selective_scan_fwd(*scan_args)
+        if ev is not None:
+            hip.record(ev[1], sp)
+        if rc:
+            raise RuntimeError(f"scan failed: {lib.sfm_last_error().decode()}")
+        if a.mode == "step":
+            rc = lib.sfm_aux_pad_swap(*swap_args)
+            if rc:
+                raise RuntimeError(f"swap failed: {lib.sfm_last_error().decode()}")
+
+    if a.mode == "scan":  # inputs of the scan must exist
+        for s in sets:
+            sfm.sfm_aux_pad_swap(s["x"], out=s["xp"], mode="pad")
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = a.steps
+    kev = [(hip.event(), hip.event()) for _ in range(K)]
+    t_start, t_end = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(t_start, sp)
+    h0 = time.perf_counter()
+    for i in range(K):
+        step(a.warmup + i, kev[i])
+    host_s = time.perf_counter() - h0
+    hip.record(t_end, sp)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed_ms(t_start, t_end)
+    scan_ms = sorted(hip.elapsed_ms(e0, e1) for e0, e1 in kev)
+    scan_avg = sum(scan_ms) / K
+    scan_med = scan_ms[K // 2]
+
+    tc = w.B * w.D * w.L
+    ms_per_step = total_ms / K
+    value = tc / (ms_per_step * 1e-3)
+    sbytes = alg_scan_bytes(w, io_bytes)
+    slots = alg_scan_slots(w)
+    hbm_gbps = sbytes / (scan_avg * 1e-3) / 1e9
+    alu = slots / (scan_avg * 1e-3) / 1e12
+    hbm_frac = hbm_gbps / HBM_PEAK_GBPS
+    alu_frac = alu / VALU_PEAK_TSLOT
+    traffic = read_traffic(a.workload, b2)
+    if alu_frac >= hbm_frac:
+        roof = {"bound": "alu", "achieved": round(alu, 3), "peak": round(VALU_PEAK_TSLOT, 3),
+                "unit": "T VALU-slot/s", "frac": round(alu_frac, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(hbm_frac, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = "sfm scan_kernel (fused conv + folded segmented scan)"
+    roof["kernel_ms_avg"] = round(scan_avg, 5)
+    roof["kernel_ms_median"] = round(scan_med, 5)
+    roof["alg_bytes_per_launch"] = sbytes
+    roof["alg_valu_slots_per_launch"] = slots
+    out = {
+        "metric": "folded selective-scan token*channels/s (T+2 aux tokens counted), % HBM peak",
+        "value": value,
+        "unit": "token*channels/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.io,
+        "data": "synthetic (seeded SplitMix64 + Box-Muller, stage-shaped)",
+        "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}",
+                   "B2": b2, "B1": w.B // b2, "mode": a.mode, "input_sets": nsets,
+                   "step": "pick_b1 + pad + fused conv/scan + swap" if a.mode == "step" else "scan only"},
+        "roofline": roof,
+        "hbm": {"scan_alg_GBps": round(hbm_gbps, 1), "frac_of_8TBps": round(hbm_frac, 4)},
+        "token_channels_T_only_per_s": w.B * w.D * w.T / (ms_per_step * 1e-3),
+        "host_ms_per_step": host_s * 1e3 / K,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, li, a.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

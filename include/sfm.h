@@ -145,6 +145,16 @@ sfm_status sfm_aux_pad_swap(const void* in, void* out, int64_t B, int64_t D, int
  */
 sfm_status sfm_pick_b1(int64_t B, int64_t L, int64_t D, int64_t N, int64_t* B1_out);
 
+/*
+ * sfm_scan_plan_string -- host-only diagnostic: writes (NUL-terminated,
+ * truncated to `cap` bytes) the launch plan sfm_selective_scan_fwd would use
+ * for these sizes -- staging mode, chunk length, pieces per folded row, channel
+ * tiles per workgroup, LDS bytes, grid.  conv_k = 0 means no fused conv.
+ * Returns SFM_ERR_SHAPE / SFM_ERR_UNSUPPORTED like the scan would.
+ */
+sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int conv_k,
+                                int io_dtype, char* buf, int64_t cap);
+
 /* Static text for a status code. */
 const char* sfm_status_string(sfm_status s);
 

@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["sfm_selective_scan_fwd", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1",
+__all__ = ["sfm_selective_scan_fwd", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1", "sfm_scan_plan_string",
            "sfm_version", "library_path", "load_library", "SFMError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,7 +50,9 @@ def load_library():
     lib.sfm_dwconv1d_fold.argtypes = [vp, fp, fp, vp, i64, i64, i64, i64, ci, ci, ci, ci, vp]
     lib.sfm_aux_pad_swap.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
     lib.sfm_pick_b1.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
-    for f in ("sfm_selective_scan_fwd", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1", "sfm_version"):
+    lib.sfm_scan_plan_string.argtypes = [i64, i64, i64, i64, i64, ci, ci, ctypes.c_char_p, i64]
+    for f in ("sfm_selective_scan_fwd", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1", "sfm_version",
+              "sfm_scan_plan_string"):
         getattr(lib, f).restype = ctypes.c_int
     lib.sfm_status_string.argtypes = [ctypes.c_int]
     lib.sfm_status_string.restype = ctypes.c_char_p
@@ -192,6 +194,14 @@ def sfm_aux_pad_swap(inp, out=None, mode="pad", stream=None):
     rc = load_library().sfm_aux_pad_swap(_ptr(inp), _ptr(out), B, D, T, code, io, _stream(stream))
     _check(rc, "sfm_aux_pad_swap")
     return out
+
+
+def sfm_scan_plan_string(B1: int, B2: int, D: int, N: int, L: int, conv_k: int = 4, io: str = "bf16") -> str:
+    """The launch plan sfm_selective_scan_fwd would use for these sizes (host only)."""
+    buf = ctypes.create_string_buffer(256)
+    _check(load_library().sfm_scan_plan_string(B1, B2, D, N, L, conv_k, SFM_BF16 if io == "bf16" else SFM_F32,
+                                               buf, 256), "sfm_scan_plan_string")
+    return buf.value.decode()
 
 
 def sfm_pick_b1(B: int, L: int, D: int, N: int) -> int:

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kWave * kPadWaves) void pad_kernel(const IO* __rest
     constexpr int kPadChunk = pad_chunk<IO>();
     __shared__ IO stage[kPadWaves][kWave * kPadChunk];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const long long r0 = ((long long)blockIdx.x * kPadWaves + wave) * kWave;
     if (r0 >= rows) return;  // whole wave leaves together; no block barrier is used
     const int nr = (int)((rows - r0) < kWave ? (rows - r0) : kWave);

@@ -9,12 +9,12 @@
 //  * A workgroup owns one folded row b1 and one tile of 64 channels.  The 64
 //    lanes of a wave are 64 channels, so every lane walks the same (sample, t)
 //    at the same time: B[b,:,t] and C[b,:,t] are wave-uniform and are staged
-//    once per wave in LDS as float32, read back as broadcasts.
+//    once per wave in LDS as float32, read back as 16-byte broadcasts.
 //  * The folded row (B2*L positions) is cut into `waves` contiguous pieces, one
 //    per wave.  Each lane scans its piece sequentially with the N-state float32
 //    recurrence in registers -- no cross-lane scan is needed, because the
-//    channel dimension already fills the wave; this is what removes the
-//    short-sequence under-fill the pages attribute to per-sequence warp scans.
+//    channel dimension already fills the wave; this removes the short-sequence
+//    under-fill the pages attribute to per-sequence warp scans.
 //  * The reset is a re-initialisation (h <- Bbar x) at every sample start, so
 //    non-finite values never cross a sample boundary.
 //  * When a piece starts inside a sample, the wave needs the state carried in
@@ -27,11 +27,22 @@
 //    carry, writing y.  Phase 1 is skipped when all cuts fall on sample starts.
 //  * Folding is index arithmetic only: position s of row b1 is sample
 //    b = b1*B2 + s/L at t = s mod L; nothing is copied.
-//  * Inputs are staged per chunk through LDS with coalesced loads; y is written
-//    back into the same LDS slots as delta and stored coalesced.
-//  * The optional depthwise conv is fused: the conv input is staged with its
-//    halo and the conv taps that fall outside the sample read zero (the
-//    boundary masking of the techloop walkthrough's conv-boundary part).
+//  * Staging (per chunk of positions, through LDS):
+//      mode 0 -- whole sample rows: the [64 x L] conv-input and delta slabs are
+//                contiguous, so they go straight into LDS by 16-byte direct
+//                global->LDS transfers, all in flight at once;
+//      mode 1 -- tiles of even-length rows: 4-byte direct transfers into LDS
+//                rows padded to an odd number of words (no bank conflicts when
+//                the 64 lanes read one column);
+//      mode 2 -- element loads (any shape), 16 per lane in flight.
+//    B and C become float32 [t][n] in LDS; y overwrites delta in LDS and is
+//    stored with wide coalesced stores.
+//  * The position loop is software-pipelined: the LDS reads of position t+1
+//    are issued before position t computes, so the wave does not wait on LDS
+//    latency each step, and at most two positions' inputs are live.
+//  * The optional depthwise conv is fused: a register window slides over the
+//    staged conv input and taps outside the sample read zero (the boundary
+//    masking of the techloop walkthrough's conv-boundary part).
 #include "sfm_device.h"
 #include "sfm_internal.h"
 
@@ -39,7 +50,7 @@ namespace sfm {
 
 namespace {
 
-constexpr int kMaxWaves = 16;
+constexpr int kMaxWaves = 8;
 
 template <typename IO, int NS, int KW, bool CONV>
 struct ScanWave {
@@ -51,16 +62,19 @@ struct ScanWave {
     // per-lane parameters
     float A[NS];
     float Dk, dbias, cw[KW], cb;
-    // LDS
+    // LDS stages
     IO* xs;
     IO* ds;
     float* bs;
     float* cs;
-    // chunk geometry
+    // geometry of the staged chunk: value at position q of this lane's row is
+    // xs[lane*xrs + q - xoff], ds[lane*drs + q - doff]; B/C at bs[(q-boff)*NS + n]
     int xrs, xoff, drs, doff, boff;
 
-    __device__ ScanWave(const ScanParams& p_, int lane_, int d0_, int b1_, char* lds)
-        : p(p_), lane(lane_), d0(d0_), nrows(min(kWave, p_.D - d0_)), b1(b1_) {
+    const int wc;  // index of this wave among the cw waves sharing the B/C stage
+
+    __device__ ScanWave(const ScanParams& p_, int lane_, int d0_, int b1_, char* own, float* bshared, int wc_)
+        : p(p_), lane(lane_), d0(d0_), nrows(max(0, min(kWave, p_.D - d0_))), b1(b1_), wc(wc_) {
         const int d = d0 + lane;
         const bool valid = d < p.D;
 #pragma unroll
@@ -70,70 +84,196 @@ struct ScanWave {
 #pragma unroll
         for (int j = 0; j < KW; ++j) cw[j] = (CONV && valid && j < p.K) ? p.conv_w[(size_t)d * p.K + j] : 0.0f;
         cb = (CONV && valid && p.conv_b) ? p.conv_b[d] : 0.0f;
-        char* q = lds;
-        xs = reinterpret_cast<IO*>(q);
-        q += p.xs_bytes;
-        ds = reinterpret_cast<IO*>(q);
-        q += p.ds_bytes;
-        bs = reinterpret_cast<float*>(q);
-        q += p.ch * NS * sizeof(float);
-        cs = reinterpret_cast<float*>(q);
-        // states n >= N stay zero in B and C for the whole kernel
-        for (int e = lane; e < p.ch * NS; e += kWave) {
-            bs[e] = 0.0f;
-            cs[e] = 0.0f;
+        xs = reinterpret_cast<IO*>(own);
+        ds = reinterpret_cast<IO*>(own + p.xs_bytes);
+        bs = bshared;
+        cs = bshared + p.ch * NS;
+        // states n >= N stay zero in B and C for the whole kernel (the first
+        // stage's barrier publishes this to the other waves of the group)
+        if (wc == 0) {
+            for (int e = lane; e < p.ch * NS; e += kWave) {
+                bs[e] = 0.0f;
+                cs[e] = 0.0f;
+            }
         }
         wave_lds_sync();
     }
 
+    // ------------------------------------------------------------ staging
+    // B/C of sample b, positions [lo, lo + cnt) -> float32 [q - boff][n].
+    // wide: 16-byte loads of the whole [N x L] block (lo == 0, cnt == L, aligned)
+    __device__ void stage_bc(const IO* bg, const IO* cg, int lo, int cnt, bool wide) {
+        const int L = p.L, N = p.N;
+        if (wide) {
+            constexpr int per = 16 / (int)sizeof(IO);
+            const int total = N * L;
+            const int units = total / per;
+            const float invL = 1.0f / (float)L;
+            for (int u0 = 0; u0 < units; u0 += 4 * kWave) {
+                uint4 vb[4], vc[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int u = u0 + k * kWave + lane;
+                    if (u < units) {
+                        vb[k] = reinterpret_cast<const uint4*>(bg)[u];
+                        vc[k] = reinterpret_cast<const uint4*>(cg)[u];
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int u = u0 + k * kWave + lane;
+                    if (u < units) {
+                        int n = div_small(u * per, invL);
+                        int t = u * per - n * L;
+#pragma unroll
+                        for (int j = 0; j < per; ++j) {
+                            bs[t * NS + n] = unpack<IO>(vb[k], j);
+                            cs[t * NS + n] = unpack<IO>(vc[k], j);
+                            if (++t == L) {
+                                t = 0;
+                                ++n;
+                            }
+                        }
+                    }
+                }
+            }
+            for (int e = units * per + lane; e < total; e += kWave) {
+                const int n = div_small(e, invL);
+                const int t = e - n * L;
+                bs[t * NS + n] = to_f32(bg[e]);
+                cs[t * NS + n] = to_f32(cg[e]);
+            }
+        } else {
+            const int total = N * cnt;
+            const float inv = 1.0f / (float)cnt;
+            for (int e0 = 0; e0 < total; e0 += 8 * kWave) {
+                IO vb[8], vc[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int e = e0 + k * kWave + lane;
+                    if (e < total) {
+                        const int n = div_small(e, inv);
+                        const int i = e - n * cnt;
+                        vb[k] = bg[(size_t)n * L + lo + i];
+                        vc[k] = cg[(size_t)n * L + lo + i];
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int e = e0 + k * kWave + lane;
+                    if (e < total) {
+                        const int n = div_small(e, inv);
+                        const int i = e - n * cnt;
+                        bs[(lo + i - boff) * NS + n] = to_f32(vb[k]);
+                        cs[(lo + i - boff) * NS + n] = to_f32(vc[k]);
+                    }
+                }
+            }
+        }
+    }
+
+    // mode 1: rows x positions [lo, hi) (lo, hi multiples of the elements per
+    // 4-byte word) by 4-byte direct transfers into LDS rows of `rs` elements.
+    // Lane-contiguous LDS words, per-lane global addresses; words outside the
+    // valid rows are not transferred (never read).
+    __device__ void dma_tile(const IO* g, IO* l, int rs, int lo, int hi) {
+        constexpr int ew = 4 / (int)sizeof(IO);
+        const int rsw = rs / ew;        // words per LDS row (odd)
+        const int nw = (hi - lo) / ew;  // words to move per row
+        const float inv = 1.0f / (float)rsw;
+        char* lb = reinterpret_cast<char*>(l);
+        const int L = p.L;
+        for (int k = 0; k < rsw; ++k) {  // 64 words per instruction, rsw instructions per tile
+            const int e = k * kWave + lane;
+            const int r = div_small(e, inv);
+            const int w = e - r * rsw;
+            if (r < nrows && w < nw)
+                __builtin_amdgcn_global_load_lds(g + (size_t)r * L + lo + w * ew, (lds_void_ptr)(lb + k * 256), 4, 0,
+                                                 0);
+        }
+    }
+
+    // rows x [lo, lo + cnt) of a [rows, L] slab -> LDS rows of stride `rs`;
+    // positions outside [0, L) become zero.  16 element loads per lane in flight.
+    __device__ void stage_rows(const IO* g, IO* l, int rs, int lo, int cnt) {
+        const int L = p.L;
+        const int total = nrows * cnt;
+        const float inv = 1.0f / (float)cnt;
+        for (int e0 = 0; e0 < total; e0 += 16 * kWave) {
+            IO v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int e = e0 + k * kWave + lane;
+                v[k] = Io<IO>::zero();
+                if (e < total) {
+                    const int c = div_small(e, inv);
+                    const int t = lo + e - c * cnt;
+                    if (t >= 0 && t < L) v[k] = g[(size_t)c * L + t];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int e = e0 + k * kWave + lane;
+                if (e < total) {
+                    const int c = div_small(e, inv);
+                    l[c * rs + e - c * cnt] = v[k];
+                }
+            }
+        }
+    }
+
     // Stage the inputs of sample b for positions [t0, t0 + len) into LDS.
-    __device__ void stage(int b, int t0, int len) {
+    // With cw > 1 the waves of a group share one B/C stage, written by wave 0
+    // between two workgroup barriers (every wave stages the same chunks).
+    __device__ void stage(int b, int t0, int len, bool first) {
         const int L = p.L, D = p.D, N = p.N;
+        const bool shared = p.cw > 1;
+        if (shared && !first) __syncthreads();  // the previous chunk's B/C has been consumed
+        const bool own_bc = !shared || wc == 0;
         const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * L;
         const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
         const IO* bg = static_cast<const IO*>(p.Bm) + (size_t)b * N * L;
         const IO* cg = static_cast<const IO*>(p.Cm) + (size_t)b * N * L;
-        if (p.flat) {
-            // whole sample rows: the [64 x L] slabs are contiguous in memory
+        if (p.mode == 0) {
+            // whole sample rows: the [64 x L] slabs are contiguous and 16-byte
+            // aligned; copy them straight into LDS, all transfers in flight at once
             xrs = L; xoff = 0; drs = L; doff = 0; boff = 0;
             const int n = nrows * L;
-            for (int e = lane; e < n; e += kWave) {
-                xs[e] = xg[e];
-                ds[e] = dg[e];
+            const int bytes = n * (int)sizeof(IO);
+            dma_to_lds(xg, xs, bytes, lane);
+            dma_to_lds(dg, ds, bytes, lane);
+            const int done = (bytes & ~15) / (int)sizeof(IO);
+            if (lane < n - done) {
+                xs[done + lane] = xg[done + lane];
+                ds[done + lane] = dg[done + lane];
             }
-            const float invL = 1.0f / (float)L;
-            for (int e = lane; e < N * L; e += kWave) {
-                const int nn = div_small(e, invL);
-                const int t = e - nn * L;
-                bs[t * NS + nn] = to_f32(bg[e]);
-                cs[t * NS + nn] = to_f32(cg[e]);
-            }
+            if (own_bc) stage_bc(bg, cg, 0, L, p.bc_wide != 0);
+            wait_vmem();
+        } else if (p.mode == 1) {
+            constexpr int ew = 4 / (int)sizeof(IO);
+            xrs = p.xrs; drs = p.drs;
+            int qa = CONV ? t0 - p.P : t0;
+            int qb = CONV ? t0 + len + KW - 1 - p.P : t0 + len;
+            qa = max(qa, 0) / ew * ew;
+            qb = (min(qb, L) + ew - 1) / ew * ew;
+            xoff = qa;
+            const int da = t0 / ew * ew;
+            const int db = (t0 + len + ew - 1) / ew * ew;
+            doff = da;
+            boff = t0;  // B/C rows hold exactly [t0, t0 + len): ch rows are allocated
+            dma_tile(xg, xs, xrs, qa, qb);
+            dma_tile(dg, ds, drs, da, db);
+            if (own_bc) stage_bc(bg, cg, t0, len, false);
+            wait_vmem();
         } else {
-            // partial rows with the conv halo; zeros outside the sample
-            const int xlen = CONV ? len + KW - 1 : len;
             xrs = p.xrs; drs = p.drs;
             xoff = CONV ? t0 - p.P : t0;
             doff = t0; boff = t0;
-            const float invx = 1.0f / (float)xlen;
-            for (int e = lane; e < nrows * xlen; e += kWave) {
-                const int c = div_small(e, invx);
-                const int i = e - c * xlen;
-                const int t = xoff + i;
-                xs[c * xrs + i] = (t >= 0 && t < L) ? xg[(size_t)c * L + t] : Io<IO>::zero();
-            }
-            const float invd = 1.0f / (float)len;
-            for (int e = lane; e < nrows * len; e += kWave) {
-                const int c = div_small(e, invd);
-                const int i = e - c * len;
-                ds[c * drs + i] = dg[(size_t)c * L + t0 + i];
-            }
-            for (int e = lane; e < N * len; e += kWave) {
-                const int nn = div_small(e, invd);
-                const int i = e - nn * len;
-                bs[i * NS + nn] = to_f32(bg[(size_t)nn * L + t0 + i]);
-                cs[i * NS + nn] = to_f32(cg[(size_t)nn * L + t0 + i]);
-            }
+            stage_rows(xg, xs, xrs, xoff, CONV ? len + KW - 1 : len);
+            stage_rows(dg, ds, drs, t0, len);
+            if (own_bc) stage_bc(bg, cg, t0, len, false);
         }
+        if (shared) __syncthreads();  // B/C of this chunk visible to the whole group
         wave_lds_sync();
     }
 
@@ -141,9 +281,33 @@ struct ScanWave {
     __device__ void store(int b, int t0, int len) {
         const int L = p.L;
         IO* yg = static_cast<IO*>(p.y) + ((size_t)b * p.D + d0) * L;
-        if (p.flat && len == L) {
+        if (p.mode == 0 && len == L) {
             const int n = nrows * L;
-            for (int e = lane; e < n; e += kWave) yg[e] = ds[e];
+            const int units = n * (int)sizeof(IO) / 16;
+            for (int u = lane; u < units; u += kWave)
+                reinterpret_cast<uint4*>(yg)[u] = reinterpret_cast<const uint4*>(ds)[u];
+            const int done = units * 16 / (int)sizeof(IO);
+            if (lane < n - done) yg[done + lane] = ds[done + lane];
+        } else if (p.mode == 1) {
+            // whole 4-byte words inside [t0, t0 + len), single elements at the edges
+            constexpr int ew = 4 / (int)sizeof(IO);
+            const int ta = (t0 + ew - 1) / ew * ew;
+            const int tb = (t0 + len) / ew * ew;
+            if (tb > ta) {
+                const int nw = (tb - ta) / ew;
+                const int total = nrows * nw;
+                const float inv = 1.0f / (float)nw;
+                for (int e = lane; e < total; e += kWave) {
+                    const int r = div_small(e, inv);
+                    const int w = e - r * nw;
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(&ds[r * drs + ta - doff + w * ew]);
+                    *reinterpret_cast<uint32_t*>(&yg[(size_t)r * L + ta + w * ew]) = v;
+                }
+            }
+            if (lane < nrows) {
+                for (int t = t0; t < min(ta, t0 + len); ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
+                for (int t = max(tb, ta); t < t0 + len; ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
+            }
         } else {
             const float inv = 1.0f / (float)len;
             for (int e = lane; e < nrows * len; e += kWave) {
@@ -155,50 +319,41 @@ struct ScanWave {
         wave_lds_sync();
     }
 
-    __device__ __forceinline__ float xs_at(int t) const { return to_f32(xs[lane * xrs + t - xoff]); }
-
-    // Scan positions [t0, t0 + len) of the staged sample.  OUT: write y into ds.
-    // AGG: accumulate sum of Delta*log2e in sd2 (no output).
-    template <bool OUT>
-    __device__ void scan_chunk(int t0, int len, float (&h)[NS], float& sd2) {
-        const int L = p.L;
-        float win[KW];
-        if constexpr (CONV) {
+    // ------------------------------------------------------------ compute
+    // B[t, :] and C[t, :] of one position from LDS (16-byte broadcast reads)
+    __device__ __forceinline__ void load_bc(const float* br, const float* cr, int t, float4 (&bq)[NS / 4],
+                                            float4 (&cq)[NS / 4]) {
+        const float4* b4 = reinterpret_cast<const float4*>(br + t * NS);
+        const float4* c4 = reinterpret_cast<const float4*>(cr + t * NS);
 #pragma unroll
-            for (int j = 0; j < KW - 1; ++j) {
-                const int q = t0 - p.P + j;
-                win[j + 1] = (q >= 0 && q < L) ? xs_at(q) : 0.0f;
-            }
+        for (int q = 0; q < NS / 4; ++q) {
+            bq[q] = b4[q];
+            cq[q] = c4[q];
         }
-        int t = t0;
-        const int tend = t0 + len;
-        if (t == 0) {
-            step<OUT, true>(t, h, sd2, win);
-            ++t;
-        }
-#pragma unroll 2
-        for (; t < tend; ++t) step<OUT, false>(t, h, sd2, win);
     }
 
-    template <bool OUT, bool FIRST>
-    __device__ __forceinline__ void step(int t, float (&h)[NS], float& sd2, float (&win)[KW]) {
+    // One position: conv tap in, Delta, N-state update, readout.
+    template <bool OUT, bool SP, bool SILU, bool FIRST>
+    __device__ __forceinline__ float core(float xnew, float dl, float (&h)[NS], float (&win)[KW], float& sd2,
+                                          const float4 (&bq)[NS / 4], const float4 (&cq)[NS / 4]) {
+        // Opaque to the compiler: pins this position's work after the previous
+        // position's, so the exp work of later positions is not hoisted (it
+        // would cost ~N registers per position and spill).
+        asm volatile("" : "+v"(xnew), "+v"(dl));
         float u;
         if constexpr (CONV) {
 #pragma unroll
             for (int j = 0; j < KW - 1; ++j) win[j] = win[j + 1];
-            const int q = t - p.P + KW - 1;
-            win[KW - 1] = (q < p.L) ? xs_at(q) : 0.0f;
+            win[KW - 1] = xnew;
             float acc = cb;
 #pragma unroll
             for (int j = 0; j < KW; ++j) acc = __builtin_fmaf(cw[j], win[j], acc);
-            u = (p.act == 1) ? silu(acc) : acc;
+            u = SILU ? silu(acc) : acc;
         } else {
-            u = to_f32(xs[lane * xrs + t - xoff]);
+            u = xnew;
         }
-        IO* dslot = &ds[lane * drs + t - doff];
-        const float dl = to_f32(*dslot) + dbias;
         float d2, dt;  // Delta * log2(e) and Delta
-        if (p.softplus) {
+        if constexpr (SP) {
             d2 = softplus_log2e(dl);
             dt = d2 * kLn2;
         } else {
@@ -208,20 +363,92 @@ struct ScanWave {
         const float du = dt * u;
         if constexpr (!OUT) sd2 += d2;
         float yv = Dk * u;
-        const float* bt = &bs[(t - boff) * NS];
-        const float* ct = &cs[(t - boff) * NS];
 #pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            const float bx = du * bt[n];
-            if constexpr (FIRST) {
-                h[n] = bx;  // reset: state re-initialised at the sample start
-            } else {
-                const float a = exp2_fast(d2 * A[n]);
-                h[n] = __builtin_fmaf(a, h[n], bx);
+        for (int q = 0; q < NS / 4; ++q) {
+            const float bv[4] = {bq[q].x, bq[q].y, bq[q].z, bq[q].w};
+            const float cv[4] = {cq[q].x, cq[q].y, cq[q].z, cq[q].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int n = q * 4 + k;
+                const float bx = du * bv[k];
+                if constexpr (FIRST) {
+                    h[n] = bx;  // reset: state re-initialised at the sample start
+                } else {
+                    const float a = exp2_fast(d2 * A[n]);
+                    h[n] = __builtin_fmaf(a, h[n], bx);
+                }
+                if constexpr (OUT) yv = __builtin_fmaf(cv[k], h[n], yv);
             }
-            if constexpr (OUT) yv = __builtin_fmaf(ct[n], h[n], yv);
         }
-        if constexpr (OUT) *dslot = from_f32<IO>(yv);
+        return yv;
+    }
+
+    // Scan positions [t0, t0 + len) of the staged sample.  OUT: write y into ds.
+    // AGG (OUT = false): accumulate the sum of Delta*log2e in sd2, no output.
+    template <bool OUT, bool SP, bool SILU>
+    __device__ void chunk_t(int t0, int len, float (&h)[NS], float& sd2) {
+        const int L = p.L;
+        const int P = CONV ? p.P : 0;
+        const IO* xr = xs + lane * xrs - xoff;
+        IO* dr = ds + lane * drs - doff;
+        const float* br = bs - boff * NS;
+        const float* cr = cs - boff * NS;
+        float win[KW];
+#pragma unroll
+        for (int j = 0; j < KW; ++j) win[j] = 0.0f;
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = 0; j < KW - 1; ++j) {
+                const int q = t0 - P + j;
+                win[j + 1] = (q >= 0 && q < L) ? to_f32(xr[q]) : 0.0f;
+            }
+        }
+        const int lag = CONV ? KW - 1 - P : 0;  // newest conv tap is x[t + lag]
+        int t = t0;
+        const int tend = t0 + len;
+        // inputs of one position, read from LDS one position ahead of use
+        float xc, dc;
+        float4 bq[NS / 4], cq[NS / 4];
+        auto fetch = [&](int tt, float& xv, float& dv, float4 (&bb)[NS / 4], float4 (&cc)[NS / 4]) {
+            const int q = tt + lag;
+            xv = (q < L) ? to_f32(xr[q]) : 0.0f;
+            dv = to_f32(dr[tt]);
+            load_bc(br, cr, tt, bb, cc);
+        };
+        if (t == 0) {
+            fetch(0, xc, dc, bq, cq);
+            const float y0 = core<OUT, SP, SILU, true>(xc, dc + dbias, h, win, sd2, bq, cq);
+            if constexpr (OUT) dr[0] = from_f32<IO>(y0);
+            ++t;
+        }
+        // two register sets used alternately: position t computes from one set
+        // while position t+1's reads land in the other, so nothing is copied
+        float x1, d1;
+        float4 bq1[NS / 4], cq1[NS / 4];
+        if (t < tend) fetch(t, xc, dc, bq, cq);
+        for (; t + 2 <= tend; t += 2) {
+            fetch(t + 1, x1, d1, bq1, cq1);
+            const float ya = core<OUT, SP, SILU, false>(xc, dc + dbias, h, win, sd2, bq, cq);
+            if constexpr (OUT) dr[t] = from_f32<IO>(ya);
+            fetch(min(t + 2, tend - 1), xc, dc, bq, cq);  // the last fetch repeats a valid position
+            const float yb = core<OUT, SP, SILU, false>(x1, d1 + dbias, h, win, sd2, bq1, cq1);
+            if constexpr (OUT) dr[t + 1] = from_f32<IO>(yb);
+        }
+        if (t < tend) {
+            const float ya = core<OUT, SP, SILU, false>(xc, dc + dbias, h, win, sd2, bq, cq);
+            if constexpr (OUT) dr[t] = from_f32<IO>(ya);
+        }
+    }
+
+    template <bool OUT>
+    __device__ void chunk(int t0, int len, float (&h)[NS], float& sd2) {
+        if (p.softplus) {
+            if (CONV && p.act == 1) chunk_t<OUT, true, true>(t0, len, h, sd2);
+            else chunk_t<OUT, true, false>(t0, len, h, sd2);
+        } else {
+            if (CONV && p.act == 1) chunk_t<OUT, false, true>(t0, len, h, sd2);
+            else chunk_t<OUT, false, false>(t0, len, h, sd2);
+        }
     }
 
     // Run folded positions [sa, sb) of row b1, state carried in h.
@@ -229,13 +456,15 @@ struct ScanWave {
     __device__ void run(int sa, int sb, float (&h)[NS], float& sd2) {
         const int L = p.L;
         int s = sa;
+        bool first = true;
         while (s < sb) {
             const int j = s / L;
             const int t0 = s - j * L;
             const int len = min(min(p.ch, L - t0), sb - s);
             const int b = b1 * p.B2 + j;
-            stage(b, t0, len);
-            scan_chunk<OUT>(t0, len, h, sd2);
+            stage(b, t0, len, first);
+            first = false;
+            chunk<OUT>(t0, len, h, sd2);
             wave_lds_sync();
             if (OUT) store(b, t0, len);
             s += len;
@@ -244,22 +473,30 @@ struct ScanWave {
 };
 
 template <typename IO, int NS, int KW, bool CONV>
-__global__ __launch_bounds__(kWave * kMaxWaves) void scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(NS <= 8 ? 3 : 2)))
+void scan_kernel(ScanParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // the wave index is the same for all 64 lanes; saying so keeps every
+    // position/piece index derived from it in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
     // giving each XCD a contiguous run of (row, tile) items keeps the B/C of a
     // folded row in one XCD's L2.
-    const int G = p.tiles * p.B1;
+    const int G = p.tgroups * p.B1;
     int g = blockIdx.x;
     if ((G & 7) == 0) g = (g & 7) * (G >> 3) + (g >> 3);
-    const int b1 = g / p.tiles;
-    const int tile = g - b1 * p.tiles;
-    ScanWave<IO, NS, KW, CONV> w(p, lane, tile * kWave, b1, smem + (size_t)wave * p.stage_bytes);
+    const int b1 = g / p.tgroups;
+    const int tg = g - b1 * p.tgroups;
+    const int wp = wave / p.cw;         // piece of the folded row
+    const int wc = wave - wp * p.cw;    // channel tile within the group
+    char* grp = smem + (size_t)wp * p.group_bytes;
+    ScanWave<IO, NS, KW, CONV> w(p, lane, (tg * p.cw + wc) * kWave, b1,
+                                 grp + p.bc_bytes + (size_t)wc * (p.xs_bytes + p.ds_bytes),
+                                 reinterpret_cast<float*>(grp), wc);
 
     const int S = p.B2 * p.L;
-    const int p0 = min(wave * p.piece, S);
+    const int p0 = min(wp * p.piece, S);
     const int p1 = min(p0 + p.piece, S);
     float h[NS];
 #pragma unroll
@@ -277,7 +514,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void scan_kernel(ScanParams p) {
             }
             w.template run<false>(q, p1, h, sd2);
         }
-        char* agg = smem + (size_t)p.waves * p.stage_bytes;
+        char* agg = smem + (size_t)p.waves * p.group_bytes;  // cw == 1 here: wave == piece
         int* aflag = reinterpret_cast<int*>(agg);
         float* asum = reinterpret_cast<float*>(agg + kMaxWaves * sizeof(int));
         float* ah = asum + (size_t)p.waves * kWave;
@@ -315,7 +552,7 @@ hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
             (void)hipGetLastError();  // do not leave a stale error for the launch check
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(p.tiles * p.B1)), dim3((unsigned)(kWave * p.waves)),
+    hipLaunchKernelGGL(kern, dim3((unsigned)(p.tgroups * p.B1)), dim3((unsigned)(kWave * p.cw * p.waves)),
                        (size_t)p.lds_bytes, stream, p);
     return hipGetLastError();
 }
@@ -334,11 +571,11 @@ hipError_t launch_io(const ScanParams& p, hipStream_t s) {
     return launch_ns<IO, 16>(p, s);
 }
 
-// LDS row stride (elements) whose length in 4-byte words is odd, so that the
-// 64 lanes reading one column hit distinct banks.
+// smallest row stride >= elems whose length in 4-byte words is odd (and whole),
+// so that the 64 lanes reading one column hit distinct banks
 int odd_word_stride(int elems, int elem_bytes) {
     int s = elems;
-    while (((s * elem_bytes + 3) / 4) % 2 == 0 || (s * elem_bytes) % 4 != 0) ++s;
+    while ((s * elem_bytes) % 4 != 0 || ((s * elem_bytes) / 4) % 2 == 0) ++s;
     return s;
 }
 
@@ -349,42 +586,52 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint) {
     p.ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
     const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 0;
     p.tiles = (p.D + kWave - 1) / kWave;
-    const int lds_cap = 160 * 1024;
+    p.bc_wide = ((long long)p.N * L * io_bytes) % 16 == 0 ? 1 : 0;
+    constexpr int kLdsCap = 160 * 1024;
+    constexpr int kLdsUnit = 1280;  // LDS is handed out to workgroups in units of this size
     const int agg_fixed = kMaxWaves * (int)sizeof(int);
-    auto stage_bytes = [&](int ch, bool flat, int& xsb, int& dsb, int& xrs, int& drs) {
-        if (flat) {
+    const int ew = 4 / io_bytes;
+    // per-wave x / delta stages
+    auto xd_bytes = [&](int ch, int mode, int& xsb, int& dsb, int& xrs, int& drs) {
+        if (mode == 0) {
             xrs = L;
             drs = L;
             xsb = kWave * L * io_bytes;
             dsb = xsb;
         } else {
-            xrs = odd_word_stride(ch + (kw ? kw - 1 : 0), io_bytes);
-            drs = odd_word_stride(ch, io_bytes);
+            // mode 1 rows hold the chunk plus word alignment at both ends
+            const int extra = mode == 1 ? 2 * (ew - 1) : 0;
+            xrs = odd_word_stride(ch + (kw ? kw - 1 : 0) + extra, io_bytes);
+            drs = odd_word_stride(ch + extra, io_bytes);
             xsb = kWave * xrs * io_bytes;
             dsb = kWave * drs * io_bytes;
         }
         xsb = (xsb + 15) & ~15;
         dsb = (dsb + 15) & ~15;
-        return xsb + dsb + 2 * ch * p.ns * (int)sizeof(float);
+        return xsb + dsb;
     };
-    // chunk length: whole samples when they fit comfortably, else fixed chunks
+    auto bc_bytes = [&](int ch) { return 2 * ch * p.ns * (int)sizeof(float); };
     int xsb = 0, dsb = 0, xrs = 0, drs = 0;
-    bool flat = L <= 256;
-    int ch = flat ? L : (ch_hint > 0 ? ch_hint : 32);
-    int sb = stage_bytes(ch, flat, xsb, dsb, xrs, drs);
-    if (flat && sb > 48 * 1024) {
-        flat = false;
-        ch = ch_hint > 0 ? ch_hint : 32;
-        sb = stage_bytes(ch, flat, xsb, dsb, xrs, drs);
+    // mode 0 (whole rows) when the [64 x L] slabs are 16-byte aligned and small
+    int mode = 2;
+    int ch = ch_hint > 0 ? ch_hint : 32;
+    if (L <= 256 && ((long long)p.D * L * io_bytes) % 16 == 0 && ch_hint <= 0 &&
+        xd_bytes(L, 0, xsb, dsb, xrs, drs) + bc_bytes(L) <= 20 * 1024) {
+        mode = 0;
+        ch = L;
     }
-    // waves per row
+    if (mode != 0) {
+        mode = ((long long)L * io_bytes) % 4 == 0 ? 1 : 2;
+        if (ch > L) ch = L;
+    }
+    // pieces per folded row
     int W;
     if (waves_hint > 0) {
         W = waves_hint;
     } else if (S <= 256 || p.B2 > 1) {
         // short rows: one or more whole samples per wave, cuts on sample starts
         W = 1;
-        for (int c = 1; c <= 8; ++c)
+        for (int c = 1; c <= kMaxWaves; ++c)
             if (p.B2 % c == 0) W = c;
     } else {
         // long rows: enough waves to fill 256 CUs x 4 SIMDs a few times over
@@ -394,41 +641,62 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint) {
     }
     if (W > kMaxWaves) W = kMaxWaves;
     if (W > S) W = S;
-    auto total_lds = [&](int w, int stage) {
-        const int piece = (S + w - 1) / w;
-        bool carry = false;
-        for (int i = 1; i < w; ++i) {
-            const int s0 = i * piece;
-            if (s0 < S && s0 % L) carry = true;
-        }
-        int agg = carry ? agg_fixed + w * kWave * (int)sizeof(float) * (1 + p.ns) : 0;
-        return w * stage + agg;
-    };
-    while (total_lds(W, sb) > lds_cap) {
-        if (!flat && ch > 8) {
-            ch /= 2;
-            sb = stage_bytes(ch, flat, xsb, dsb, xrs, drs);
-        } else if (W > 1) {
-            --W;
-        } else {
-            return false;
-        }
-    }
-    p.waves = W;
-    p.piece = (S + W - 1) / W;
-    p.need_carry = 0;
+    const int piece = (S + W - 1) / W;
+    int carry = 0;
     for (int i = 1; i < W; ++i) {
-        const int s0 = i * p.piece;
-        if (s0 < S && s0 % L) p.need_carry = 1;
+        const int s0 = i * piece;
+        if (s0 < S && s0 % L) carry = 1;
     }
+    auto lds_total = [&](int cw, int chv, int& grp) {
+        grp = bc_bytes(chv) + cw * xd_bytes(chv, mode, xsb, dsb, xrs, drs);
+        const int agg = carry ? agg_fixed + W * kWave * (int)sizeof(float) * (1 + p.ns) : 0;
+        return W * grp + agg;
+    };
+    // shrink the chunk until one workgroup of cw = 1 fits
+    int grp = 0;
+    while (lds_total(1, ch, grp) > kLdsCap) {
+        if (mode != 0 && ch > 8) ch /= 2;
+        else return false;
+    }
+    // channel tiles per workgroup sharing one B/C stage: the choice that needs
+    // the fewest rounds of resident waves (all pieces must then stage the same
+    // chunk sequence, so only without carries and with equal pieces)
+    const int vgpr_waves_per_cu = p.ns <= 8 ? 12 : 8;
+    int best_cw = 1;
+    long long best_rounds = -1;
+    for (int cw = 1; cw <= 4; cw *= 2) {
+        if (cw > 1 && (carry || S % W || cw * W > kMaxWaves || p.tiles < cw)) break;
+        const int tot = lds_total(cw, ch, grp);
+        if (tot > kLdsCap) break;
+        const int alloc = (tot + kLdsUnit - 1) / kLdsUnit * kLdsUnit;
+        int per_cu = kLdsCap / alloc * cw * W;
+        const int lim = vgpr_waves_per_cu / (cw * W) * (cw * W);
+        if (per_cu > lim) per_cu = lim;
+        if (per_cu < cw * W) per_cu = cw * W;
+        const long long tgroups = (p.tiles + cw - 1) / cw;
+        const long long waves = tgroups * p.B1 * cw * W;
+        const long long slots = 256LL * per_cu;
+        const long long rounds = (waves + slots - 1) / slots;
+        if (best_rounds < 0 || rounds < best_rounds) {
+            best_rounds = rounds;
+            best_cw = cw;
+        }
+    }
+    p.cw = best_cw;
+    p.tgroups = (p.tiles + p.cw - 1) / p.cw;
+    p.waves = W;
+    p.piece = piece;
+    p.need_carry = carry;
     p.ch = ch;
-    p.flat = flat ? 1 : 0;
+    p.mode = mode;
+    p.lds_bytes = lds_total(p.cw, ch, grp);
+    p.group_bytes = grp;
+    p.bc_bytes = bc_bytes(ch);
+    xd_bytes(ch, mode, xsb, dsb, xrs, drs);
     p.xrs = xrs;
     p.drs = drs;
     p.xs_bytes = xsb;
     p.ds_bytes = dsb;
-    p.stage_bytes = sb;
-    p.lds_bytes = total_lds(W, sb);
     return true;
 }
 

@@ -149,6 +149,34 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
     return hip_status(sfm::launch_scan(p, io_dtype, static_cast<hipStream_t>(stream)), "sfm_selective_scan_fwd");
 }
 
+sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int conv_k, int io_dtype,
+                                char* buf, int64_t cap) {
+    if (!buf || cap < 1) return fail(SFM_ERR_NULL, "sfm_scan_plan_string: buf is required");
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "sfm_scan_plan_string: io_dtype");
+    if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24) || N < 1 ||
+        N > SFM_MAX_N || conv_k < 0 || conv_k > SFM_MAX_K)
+        return fail(SFM_ERR_SHAPE, "sfm_scan_plan_string: sizes out of range");
+    sfm::ScanParams p{};
+    static const float dummy = 0.0f;
+    p.conv_w = conv_k ? &dummy : nullptr;
+    p.B1 = (int)B1;
+    p.B2 = (int)B2;
+    p.D = (int)D;
+    p.N = (int)N;
+    p.L = (int)L;
+    p.K = conv_k ? conv_k : 1;
+    int waves_hint = 0, ch_hint = 0;
+    if (const char* e = std::getenv("SFM_SCAN_WAVES")) waves_hint = std::atoi(e);
+    if (const char* e = std::getenv("SFM_SCAN_CHUNK")) ch_hint = std::atoi(e);
+    if (!sfm::plan_scan(p, io_bytes(io_dtype), waves_hint, ch_hint))
+        return fail(SFM_ERR_UNSUPPORTED, "sfm_scan_plan_string: no launch plan fits LDS");
+    snprintf(buf, (size_t)cap,
+             "mode=%d ch=%d pieces=%d piece=%d carry=%d cw=%d ns=%d lds=%d grid=%lld block=%d",
+             p.mode, p.ch, p.waves, p.piece, p.need_carry, p.cw, p.ns, p.lds_bytes,
+             (long long)p.tgroups * p.B1, 64 * p.cw * p.waves);
+    return ok();
+}
+
 sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, void* out, int64_t B1, int64_t B2,
                              int64_t D, int64_t L, int K, int pad_left, int act, int io_dtype, void* stream) {
     if (!x || !w || !out) return fail(SFM_ERR_NULL, "sfm_dwconv1d_fold: x, w and out are required");

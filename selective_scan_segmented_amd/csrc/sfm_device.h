@@ -44,6 +44,18 @@ template <> struct Io<__bf16> {
 };
 
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return Io<T>::to_f32(v); }
+
+// element j of a 16-byte packet of io elements, as float32
+template <typename T> __device__ __forceinline__ float unpack(const uint4& v, int j);
+template <> __device__ __forceinline__ float unpack<float>(const uint4& v, int j) {
+    const uint32_t w = j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+    return __uint_as_float(w);
+}
+template <> __device__ __forceinline__ float unpack<__bf16>(const uint4& v, int j) {
+    const int q = j >> 1;
+    const uint32_t w = q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+    return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+}
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return Io<T>::from_f32(v); }
 
 // ---------------------------------------------------------------- math
@@ -73,6 +85,26 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- memory movement
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Wait until every vector-memory operation of this wave, including direct
+// global->LDS transfers, has completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue direct global->LDS copies of the first (bytes & ~15) bytes of a region:
+// 64 lanes x 16 bytes per instruction, no registers involved, nothing waited
+// for.  `g` and `l` must be 16-byte aligned; `l` and `bytes` wave-uniform.
+__device__ __forceinline__ void dma_to_lds(const void* g, void* l, int bytes, int lane) {
+    const int units = bytes >> 4;
+    const char* gb = static_cast<const char*>(g);
+    char* lb = static_cast<char*>(l);
+    for (int u0 = 0; u0 < units; u0 += 64) {
+        if (u0 + lane < units)
+            __builtin_amdgcn_global_load_lds(gb + (size_t)(u0 + lane) * 16, (lds_void_ptr)(lb + u0 * 16), 16, 0, 0);
+    }
 }
 
 // floor(e / len) for 0 <= e < 2^22 and len >= 1, via a float reciprocal: the

@@ -24,13 +24,16 @@ struct ScanParams {
     // plan (filled by plan_scan)
     int ns;          // compiled state count (4, 8 or 16) >= N
     int tiles;       // ceil(D / 64)
-    int waves;       // waves per workgroup = pieces per folded row
+    int cw;          // channel tiles per workgroup sharing one B/C stage (waves per piece)
+    int tgroups;     // ceil(tiles / cw)
+    int waves;       // pieces per folded row (the workgroup has cw * waves waves)
     int piece;       // folded positions per wave
     int need_carry;  // 1 when some piece starts inside a sample
     int ch;          // positions per LDS chunk
-    int flat;        // 1: a chunk holds whole sample rows (contiguous slabs)
+    int mode;        // staging: 0 whole rows (16-byte DMA), 1 tiles (4-byte DMA), 2 element loads
     int xrs, drs;    // LDS row strides (elements) of the x and delta/y stages
-    int xs_bytes, ds_bytes, stage_bytes, lds_bytes;
+    int bc_wide;     // B/C blocks of whole samples are 16-byte aligned
+    int xs_bytes, ds_bytes, bc_bytes, group_bytes, lds_bytes;
 };
 
 // Fills the plan fields; waves_hint / ch_hint <= 0 select automatically.
