@@ -102,11 +102,13 @@ def read_traffic(workload: str, b2: int):
     return float(m["bytes_per_launch"].group(1))
 
 
-def alg_scan_bytes(w, io_bytes: int) -> int:
-    """Algorithmic HBM bytes of one fused conv+scan launch: the conv input, delta
-    and y once each, B and C once per sample, and the per-channel parameters."""
-    tc = w.B * w.D * w.L
-    return tc * 3 * io_bytes + 2 * w.B * w.N * w.L * io_bytes + w.D * (w.N + 3 + w.K) * 4
+def alg_scan_bytes(w, io_bytes: int, fused_pad: bool) -> int:
+    """Algorithmic HBM bytes of one scan launch: the conv input (T tokens per row
+    when the aux pad is fused, else L), delta and y once each, B and C once per
+    sample, and the per-channel parameters."""
+    xrow = w.T if fused_pad else w.L
+    return (w.B * w.D * (xrow + 2 * w.L) * io_bytes + 2 * w.B * w.N * w.L * io_bytes
+            + w.D * (w.N + 3 + w.K) * 4)
 
 
 def alg_scan_slots(w) -> int:
@@ -160,6 +162,8 @@ def main():
     ap.add_argument("--mode", choices=["step", "copy", "scan"], default="step",
                     help="step: the whole hot path (default); scan: the scan launch alone; "
                          "copy: a plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as three launches (pad, conv+scan, swap) instead of one")
     a = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -227,12 +231,15 @@ def main():
     lib = sfm.load_library()
     io = 0 if w.io == "f32" else 1
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    # fused (default): one launch does pad + conv + scan + swap from the unpadded x
+    fused = a.mode == "step" and not a.unfused
     calls = []
     for s in sets:
         pad_args = (vp(s["x"]), vp(s["xp"]), w.B, w.D, w.T, 0, io, sp)
-        scan_args = (vp(s["xp"]), vp(s["delta"]), vp(prm["A"]), vp(s["Bm"]), vp(s["Cm"]), vp(prm["Dskip"]),
+        scan_in = s["x"] if fused else s["xp"]
+        scan_args = (vp(scan_in), vp(s["delta"]), vp(prm["A"]), vp(s["Bm"]), vp(s["Cm"]), vp(prm["Dskip"]),
                      vp(prm["delta_bias"]), 1, vp(prm["conv_w"]), None, w.K, 1, 0, vp(s["y"]),
-                     w.B // b2, b2, w.D, w.N, w.L, io, sp)
+                     w.B // b2, b2, w.D, w.N, w.L, io, 3 if fused else 0, sp)
         swap_args = (vp(s["y"]), vp(s["y"]), w.B, w.D, w.L - 2, 1, io, sp)
         calls.append((pad_args, scan_args, swap_args))
     b1_out = ctypes.c_int64()
@@ -241,17 +248,18 @@ def main():
         pad_args, scan_args, swap_args = calls[i % nsets]
         if a.mode == "step":
             lib.sfm_pick_b1(w.B, w.L, w.D, w.N, ctypes.byref(b1_out))
+        if a.mode == "step" and not fused:
             rc = lib.sfm_aux_pad_swap(*pad_args)
             if rc:
                 raise RuntimeError(f"pad failed: {lib.sfm_last_error().decode()}")
         if ev is not None:
             hip.record(ev[0], sp)
-        rc = lib.sfm_selective_scan_fwd(*scan_args)
+        rc = lib.sfm_selective_scan_fwd_ex(*scan_args)
         if ev is not None:
             hip.record(ev[1], sp)
         if rc:
             raise RuntimeError(f"scan failed: {lib.sfm_last_error().decode()}")
-        if a.mode == "step":
+        if a.mode == "step" and not fused:
             rc = lib.sfm_aux_pad_swap(*swap_args)
             if rc:
                 raise RuntimeError(f"swap failed: {lib.sfm_last_error().decode()}")
@@ -282,7 +290,7 @@ def main():
     tc = w.B * w.D * w.L
     ms_per_step = total_ms / K
     value = tc / (ms_per_step * 1e-3)
-    sbytes = alg_scan_bytes(w, io_bytes)
+    sbytes = alg_scan_bytes(w, io_bytes, fused)
     slots = alg_scan_slots(w)
     hbm_gbps = sbytes / (scan_avg * 1e-3) / 1e9
     alu = slots / (scan_avg * 1e-3) / 1e12
@@ -296,7 +304,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(hbm_frac, 4)}
     roof["traffic"] = traffic
-    roof["kernel"] = "sfm scan_kernel (fused conv + folded segmented scan)"
+    roof["kernel"] = ("sfm scan_kernel (aux pad + boundary-masked conv + folded segmented scan + aux swap, "
+                      "one launch)" if fused else "sfm scan_kernel (conv + folded segmented scan)")
+    roof["plan"] = sfm.sfm_scan_plan_string(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, 3 if fused else 0)
     roof["kernel_ms_avg"] = round(scan_avg, 5)
     roof["kernel_ms_median"] = round(scan_med, 5)
     roof["alg_bytes_per_launch"] = sbytes
@@ -316,7 +326,8 @@ def main():
         "data": "synthetic (seeded SplitMix64 + Box-Muller, stage-shaped)",
         "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}",
                    "B2": b2, "B1": w.B // b2, "mode": a.mode, "input_sets": nsets,
-                   "step": "pick_b1 + pad + fused conv/scan + swap" if a.mode == "step" else "scan only"},
+                   "step": ("pick_b1 + one launch of pad/conv/scan/swap" if fused else
+                            "pick_b1 + pad + conv/scan + swap (3 launches)") if a.mode == "step" else "scan only"},
         "roofline": roof,
         "hbm": {"scan_alg_GBps": round(hbm_gbps, 1), "frac_of_8TBps": round(hbm_frac, 4)},
         "token_channels_T_only_per_s": w.B * w.D * w.T / (ms_per_step * 1e-3),

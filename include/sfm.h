@@ -104,6 +104,31 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
                                   int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype, void* stream);
 
 /*
+ * sfm_selective_scan_fwd_ex -- sfm_selective_scan_fwd with the stage's aux-token
+ * steps fused into the same launch ("Seeing Both Ways, Running One Way" 3.2;
+ * techloop walkthrough "第一个模块"):
+ *   flags & SFM_FUSE_PAD:  `u` is the UNPADDED [B1*B2, D, L-2] input of a stage's
+ *       first Mamba layer; each row is extended in the kernel to
+ *       [mean, x_1 .. x_T, mean] exactly as sfm_aux_pad_swap(PAD) would
+ *       (float64 index-order mean, one rounding to the io type) before the conv
+ *       and the scan read it.  L >= 3.
+ *   flags & SFM_FUSE_SWAP: y is written with positions 0 and L-1 exchanged, as
+ *       sfm_aux_pad_swap(SWAP) would leave it for the next layer.
+ * Results are bit-identical to the unfused sequence pad -> scan -> swap.  With
+ * either flag the launch keeps every sample inside one wave (no carried state),
+ * so very long single-sample rows run with less parallelism.
+ * Other arguments as sfm_selective_scan_fwd; flags = 0 is that function.
+ */
+#define SFM_FUSE_PAD 1
+#define SFM_FUSE_SWAP 2
+sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* Bm,
+                                     const void* Cm, const float* Dskip, const float* delta_bias,
+                                     int delta_softplus, const float* conv_w, const float* conv_b,
+                                     int conv_k, int conv_pad_left, int conv_act, void* y, int64_t B1,
+                                     int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype, int flags,
+                                     void* stream);
+
+/*
  * sfm_dwconv1d_fold -- boundary-masked depthwise conv1d over folded rows
  * ([TL] "第二个模块", conv-boundary part; [SBW] 8.1 item 5):
  *   out[b,d,t] = act(bias[d] + sum_{j<K} w[d,j] * x[b,d,t+j-pad_left]),
@@ -149,11 +174,12 @@ sfm_status sfm_pick_b1(int64_t B, int64_t L, int64_t D, int64_t N, int64_t* B1_o
  * sfm_scan_plan_string -- host-only diagnostic: writes (NUL-terminated,
  * truncated to `cap` bytes) the launch plan sfm_selective_scan_fwd would use
  * for these sizes -- staging mode, chunk length, pieces per folded row, channel
- * tiles per workgroup, LDS bytes, grid.  conv_k = 0 means no fused conv.
+ * tiles per workgroup, LDS bytes, grid.  conv_k = 0 means no fused conv;
+ * flags as for sfm_selective_scan_fwd_ex.
  * Returns SFM_ERR_SHAPE / SFM_ERR_UNSUPPORTED like the scan would.
  */
 sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int conv_k,
-                                int io_dtype, char* buf, int64_t cap);
+                                int io_dtype, int flags, char* buf, int64_t cap);
 
 /* Static text for a status code. */
 const char* sfm_status_string(sfm_status s);

@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["sfm_selective_scan_fwd", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1", "sfm_scan_plan_string",
+__all__ = ["sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1", "sfm_scan_plan_string",
            "sfm_version", "library_path", "load_library", "SFMError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,12 +47,14 @@ def load_library():
     vp, i64, ci, fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.sfm_selective_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
                                            i64, i64, i64, i64, i64, ci, vp]
+    lib.sfm_selective_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
+                                              i64, i64, i64, i64, i64, ci, ci, vp]
     lib.sfm_dwconv1d_fold.argtypes = [vp, fp, fp, vp, i64, i64, i64, i64, ci, ci, ci, ci, vp]
     lib.sfm_aux_pad_swap.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
     lib.sfm_pick_b1.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
-    lib.sfm_scan_plan_string.argtypes = [i64, i64, i64, i64, i64, ci, ci, ctypes.c_char_p, i64]
-    for f in ("sfm_selective_scan_fwd", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1", "sfm_version",
-              "sfm_scan_plan_string"):
+    lib.sfm_scan_plan_string.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci, ctypes.c_char_p, i64]
+    for f in ("sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_dwconv1d_fold", "sfm_aux_pad_swap",
+              "sfm_pick_b1", "sfm_version", "sfm_scan_plan_string"):
         getattr(lib, f).restype = ctypes.c_int
     lib.sfm_status_string.argtypes = [ctypes.c_int]
     lib.sfm_status_string.restype = ctypes.c_char_p
@@ -111,6 +113,9 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+SFM_FUSE_PAD, SFM_FUSE_SWAP = 1, 2
+
+
 def sfm_selective_scan_fwd(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, delta_softplus=True,
                            conv_w=None, conv_b=None, conv_pad_left=1, conv_act=None, y=None, B2=1,
                            stream=None):
@@ -120,9 +125,19 @@ def sfm_selective_scan_fwd(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, del
     With conv_w ([D, K] float32) ``u`` is the conv input and the boundary-masked conv is fused.
     B2 samples form one folded row (B1 = B / B2).  Returns y [B, D, L] (allocated if None).
     """
+    return sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b,
+                                     conv_pad_left, conv_act, y, B2, 0, stream)
+
+
+def sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, delta_softplus=True,
+                              conv_w=None, conv_b=None, conv_pad_left=1, conv_act=None, y=None, B2=1,
+                              flags=0, stream=None):
+    """sfm_selective_scan_fwd with the aux pad (flags & SFM_FUSE_PAD: u is the unpadded
+    [B, D, L-2] stage input) and/or the aux swap of y (flags & SFM_FUSE_SWAP) fused in."""
     torch = _torch()
     io = _io_code(u)
-    B, D, L = u.shape
+    B, D, XL = u.shape
+    L = XL + 2 if flags & SFM_FUSE_PAD else XL
     N = A.shape[1]
     if B % B2:
         raise ValueError(f"B2={B2} must divide B={B}")
@@ -141,12 +156,12 @@ def sfm_selective_scan_fwd(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, del
         K = conv_w.shape[1]
         _dev(conv_b, "conv_b", torch.float32, (D,))
     if y is None:
-        y = torch.empty_like(u)
+        y = torch.empty((B, D, L), dtype=u.dtype, device=u.device)
     _dev(y, "y", u.dtype, (B, D, L))
-    rc = load_library().sfm_selective_scan_fwd(
+    rc = load_library().sfm_selective_scan_fwd_ex(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(delta_bias), int(bool(delta_softplus)),
         _ptr(conv_w), _ptr(conv_b), K, int(conv_pad_left), _ACT[conv_act], _ptr(y),
-        B // B2, B2, D, N, L, io, _stream(stream))
+        B // B2, B2, D, N, L, io, int(flags), _stream(stream))
     _check(rc, "sfm_selective_scan_fwd")
     return y
 
@@ -196,11 +211,12 @@ def sfm_aux_pad_swap(inp, out=None, mode="pad", stream=None):
     return out
 
 
-def sfm_scan_plan_string(B1: int, B2: int, D: int, N: int, L: int, conv_k: int = 4, io: str = "bf16") -> str:
-    """The launch plan sfm_selective_scan_fwd would use for these sizes (host only)."""
+def sfm_scan_plan_string(B1: int, B2: int, D: int, N: int, L: int, conv_k: int = 4, io: str = "bf16",
+                         flags: int = 0) -> str:
+    """The launch plan sfm_selective_scan_fwd(_ex) would use for these sizes (host only)."""
     buf = ctypes.create_string_buffer(256)
     _check(load_library().sfm_scan_plan_string(B1, B2, D, N, L, conv_k, SFM_BF16 if io == "bf16" else SFM_F32,
-                                               buf, 256), "sfm_scan_plan_string")
+                                               flags, buf, 256), "sfm_scan_plan_string")
     return buf.value.decode()
 
 

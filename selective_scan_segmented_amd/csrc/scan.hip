@@ -70,11 +70,13 @@ struct ScanWave {
     // geometry of the staged chunk: value at position q of this lane's row is
     // xs[lane*xrs + q - xoff], ds[lane*drs + q - doff]; B/C at bs[(q-boff)*NS + n]
     int xrs, xoff, drs, doff, boff;
-
     const int wc;  // index of this wave among the cw waves sharing the B/C stage
+    float mean;    // fused aux pad: this row's head/tail token value (io-rounded)
+    IO y0;         // fused swap: y at t = 0 of the current sample, written last
 
     __device__ ScanWave(const ScanParams& p_, int lane_, int d0_, int b1_, char* own, float* bshared, int wc_)
-        : p(p_), lane(lane_), d0(d0_), nrows(max(0, min(kWave, p_.D - d0_))), b1(b1_), wc(wc_) {
+        : p(p_), lane(lane_), d0(d0_), nrows(max(0, min(kWave, p_.D - d0_))), b1(b1_), wc(wc_), mean(0.0f),
+          y0(Io<IO>::zero()) {
         const int d = d0 + lane;
         const bool valid = d < p.D;
 #pragma unroll
@@ -176,13 +178,12 @@ struct ScanWave {
     // 4-byte word) by 4-byte direct transfers into LDS rows of `rs` elements.
     // Lane-contiguous LDS words, per-lane global addresses; words outside the
     // valid rows are not transferred (never read).
-    __device__ void dma_tile(const IO* g, IO* l, int rs, int lo, int hi) {
+    __device__ void dma_tile(const IO* g, IO* l, int rs, int lo, int hi, int L) {
         constexpr int ew = 4 / (int)sizeof(IO);
         const int rsw = rs / ew;        // words per LDS row (odd)
         const int nw = (hi - lo) / ew;  // words to move per row
         const float inv = 1.0f / (float)rsw;
         char* lb = reinterpret_cast<char*>(l);
-        const int L = p.L;
         for (int k = 0; k < rsw; ++k) {  // 64 words per instruction, rsw instructions per tile
             const int e = k * kWave + lane;
             const int r = div_small(e, inv);
@@ -195,8 +196,7 @@ struct ScanWave {
 
     // rows x [lo, lo + cnt) of a [rows, L] slab -> LDS rows of stride `rs`;
     // positions outside [0, L) become zero.  16 element loads per lane in flight.
-    __device__ void stage_rows(const IO* g, IO* l, int rs, int lo, int cnt) {
-        const int L = p.L;
+    __device__ void stage_rows(const IO* g, IO* l, int rs, int lo, int cnt, int L) {
         const int total = nrows * cnt;
         const float inv = 1.0f / (float)cnt;
         for (int e0 = 0; e0 < total; e0 += 16 * kWave) {
@@ -227,72 +227,123 @@ struct ScanWave {
     // between two workgroup barriers (every wave stages the same chunks).
     __device__ void stage(int b, int t0, int len, bool first) {
         const int L = p.L, D = p.D, N = p.N;
+        const int XL = p.xrow;             // row length of the u tensor
+        const int sh = p.pad_in ? 1 : 0;   // padded position q reads u row index q - sh
         const bool shared = p.cw > 1;
         if (shared && !first) __syncthreads();  // the previous chunk's B/C has been consumed
         const bool own_bc = !shared || wc == 0;
-        const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * L;
+        const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * XL;
         const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
         const IO* bg = static_cast<const IO*>(p.Bm) + (size_t)b * N * L;
         const IO* cg = static_cast<const IO*>(p.Cm) + (size_t)b * N * L;
+        if (p.pad_in && p.mode != 0 && t0 == 0) row_mean(xg);
         if (p.mode == 0) {
-            // whole sample rows: the [64 x L] slabs are contiguous and 16-byte
-            // aligned; copy them straight into LDS, all transfers in flight at once
-            xrs = L; xoff = 0; drs = L; doff = 0; boff = 0;
-            const int n = nrows * L;
-            const int bytes = n * (int)sizeof(IO);
-            dma_to_lds(xg, xs, bytes, lane);
-            dma_to_lds(dg, ds, bytes, lane);
-            const int done = (bytes & ~15) / (int)sizeof(IO);
-            if (lane < n - done) {
-                xs[done + lane] = xg[done + lane];
-                ds[done + lane] = dg[done + lane];
-            }
+            // whole sample rows: the [64 x XL] and [64 x L] slabs are contiguous
+            // and 16-byte aligned; copy them straight into LDS, all in flight
+            xrs = XL; xoff = sh; drs = L; doff = 0; boff = 0;
+            const int nx = nrows * XL, nd = nrows * L;
+            dma_to_lds(xg, xs, nx * (int)sizeof(IO), lane);
+            dma_to_lds(dg, ds, nd * (int)sizeof(IO), lane);
+            const int donex = (nx * (int)sizeof(IO) & ~15) / (int)sizeof(IO);
+            const int doned = (nd * (int)sizeof(IO) & ~15) / (int)sizeof(IO);
+            if (lane < nx - donex) xs[donex + lane] = xg[donex + lane];
+            if (lane < nd - doned) ds[doned + lane] = dg[doned + lane];
             if (own_bc) stage_bc(bg, cg, 0, L, p.bc_wide != 0);
             wait_vmem();
+            if (p.pad_in) {
+                wave_lds_sync();
+                double acc = 0.0;  // float64, index order: bit-identical to the aux pad
+                if (lane < nrows)
+                    for (int i = 0; i < XL; ++i) acc += (double)to_f32(xs[lane * XL + i]);
+                mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+            }
         } else if (p.mode == 1) {
             constexpr int ew = 4 / (int)sizeof(IO);
             xrs = p.xrs; drs = p.drs;
-            int qa = CONV ? t0 - p.P : t0;
-            int qb = CONV ? t0 + len + KW - 1 - p.P : t0 + len;
+            // padded positions [qa, qb) needed, i.e. u row indices [qa - sh, qb - sh)
+            int qa = (CONV ? t0 - p.P : t0) - sh;
+            int qb = (CONV ? t0 + len + KW - 1 - p.P : t0 + len) - sh;
             qa = max(qa, 0) / ew * ew;
-            qb = (min(qb, L) + ew - 1) / ew * ew;
-            xoff = qa;
+            qb = (min(qb, XL) + ew - 1) / ew * ew;
+            xoff = qa + sh;
             const int da = t0 / ew * ew;
             const int db = (t0 + len + ew - 1) / ew * ew;
             doff = da;
             boff = t0;  // B/C rows hold exactly [t0, t0 + len): ch rows are allocated
-            dma_tile(xg, xs, xrs, qa, qb);
-            dma_tile(dg, ds, drs, da, db);
+            if (qb > qa) dma_tile(xg, xs, xrs, qa, qb, XL);
+            dma_tile(dg, ds, drs, da, db, L);
             if (own_bc) stage_bc(bg, cg, t0, len, false);
             wait_vmem();
         } else {
             xrs = p.xrs; drs = p.drs;
-            xoff = CONV ? t0 - p.P : t0;
+            const int lo = (CONV ? t0 - p.P : t0) - sh;  // u row index of LDS column 0
+            xoff = lo + sh;
             doff = t0; boff = t0;
-            stage_rows(xg, xs, xrs, xoff, CONV ? len + KW - 1 : len);
-            stage_rows(dg, ds, drs, t0, len);
+            stage_rows(xg, xs, xrs, lo, CONV ? len + KW - 1 : len, XL);
+            stage_rows(dg, ds, drs, t0, len, L);
             if (own_bc) stage_bc(bg, cg, t0, len, false);
         }
         if (shared) __syncthreads();  // B/C of this chunk visible to the whole group
         wave_lds_sync();
     }
 
-    // Store y for positions [t0, t0 + len) of sample b (y sits in ds).
+    // Fused aux pad, chunked rows: float64 index-order sum of this lane's whole
+    // unpadded row, streamed through the x stage before the sample's first chunk.
+    __device__ void row_mean(const IO* xg) {
+        constexpr int ew = 4 / (int)sizeof(IO);
+        const int XL = p.xrow;
+        const int step = p.ch;
+        double acc = 0.0;
+        for (int c0 = 0; c0 < XL; c0 += step) {
+            const int cl = min(step, XL - c0);
+            int lo = c0;
+            if (p.mode == 1) {
+                lo = c0 / ew * ew;
+                const int hi = (c0 + cl + ew - 1) / ew * ew;
+                dma_tile(xg, xs, p.xrs, lo, min(hi, XL), XL);
+                wait_vmem();
+            } else {
+                stage_rows(xg, xs, p.xrs, c0, cl, XL);
+            }
+            wave_lds_sync();
+            if (lane < nrows)
+                for (int i = c0; i < c0 + cl; ++i) acc += (double)to_f32(xs[lane * p.xrs + i - lo]);
+            wave_lds_sync();
+        }
+        mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+    }
+
+    // Store y for positions [t0, t0 + len) of sample b (y sits in ds).  With
+    // the fused swap, position 0 is written at column L-1 and vice versa.
     __device__ void store(int b, int t0, int len) {
         const int L = p.L;
         IO* yg = static_cast<IO*>(p.y) + ((size_t)b * p.D + d0) * L;
+        const bool sw = p.swap_out && L > 1;
         if (p.mode == 0 && len == L) {
+            if (sw && lane < nrows) {  // exchange the two end tokens of this lane's row in LDS
+                const IO a = ds[lane * L];
+                ds[lane * L] = ds[lane * L + L - 1];
+                ds[lane * L + L - 1] = a;
+            }
+            wave_lds_sync();
             const int n = nrows * L;
             const int units = n * (int)sizeof(IO) / 16;
             for (int u = lane; u < units; u += kWave)
                 reinterpret_cast<uint4*>(yg)[u] = reinterpret_cast<const uint4*>(ds)[u];
             const int done = units * 16 / (int)sizeof(IO);
             if (lane < n - done) yg[done + lane] = ds[done + lane];
-        } else if (p.mode == 1) {
-            // whole 4-byte words inside [t0, t0 + len), single elements at the edges
+            wave_lds_sync();
+            return;
+        }
+        // positions written here; the ends go out last when swapping
+        const int lo = (sw && t0 == 0) ? 1 : t0;
+        const int hi = (sw && t0 + len == L) ? L - 1 : t0 + len;
+        if (sw && t0 == 0 && lane < nrows) y0 = ds[lane * drs + 0 - doff];
+        if (p.mode == 1) {
+            // whole 4-byte words inside [lo, hi), single elements at the edges
             constexpr int ew = 4 / (int)sizeof(IO);
-            const int ta = (t0 + ew - 1) / ew * ew;
-            const int tb = (t0 + len) / ew * ew;
+            const int ta = (lo + ew - 1) / ew * ew;
+            const int tb = max(ta, hi / ew * ew);
             if (tb > ta) {
                 const int nw = (tb - ta) / ew;
                 const int total = nrows * nw;
@@ -305,21 +356,37 @@ struct ScanWave {
                 }
             }
             if (lane < nrows) {
-                for (int t = t0; t < min(ta, t0 + len); ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
-                for (int t = max(tb, ta); t < t0 + len; ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
+                for (int t = lo; t < min(ta, hi); ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
+                for (int t = tb; t < hi; ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
             }
-        } else {
-            const float inv = 1.0f / (float)len;
-            for (int e = lane; e < nrows * len; e += kWave) {
+        } else if (hi > lo) {
+            const int cnt = hi - lo;
+            const float inv = 1.0f / (float)cnt;
+            for (int e = lane; e < nrows * cnt; e += kWave) {
                 const int c = div_small(e, inv);
-                const int i = e - c * len;
-                yg[(size_t)c * L + t0 + i] = ds[c * drs + (t0 - doff) + i];
+                const int i = e - c * cnt;
+                yg[(size_t)c * L + lo + i] = ds[c * drs + (lo - doff) + i];
             }
+        }
+        if (sw && t0 + len == L && lane < nrows) {
+            yg[(size_t)lane * L] = ds[lane * drs + (L - 1) - doff];
+            yg[(size_t)lane * L + L - 1] = y0;
         }
         wave_lds_sync();
     }
 
     // ------------------------------------------------------------ compute
+    // Conv/scan input at padded position q (wave-uniform): zero outside the
+    // sample, the aux-token value at both ends when the pad is fused, else the
+    // staged value.  Branch-free: the LDS read always hits a valid column.
+    __device__ __forceinline__ float xat(const IO* xr, int q, int L, bool pad) const {
+        const int lo = pad ? 1 : 0;
+        const int qc = min(max(q, lo), L - 1 - lo);
+        float v = to_f32(xr[qc]);
+        v = (pad && (q == 0 || q == L - 1)) ? mean : v;
+        return (q < 0 || q >= L) ? 0.0f : v;
+    }
+
     // B[t, :] and C[t, :] of one position from LDS (16-byte broadcast reads)
     __device__ __forceinline__ void load_bc(const float* br, const float* cr, int t, float4 (&bq)[NS / 4],
                                             float4 (&cq)[NS / 4]) {
@@ -393,15 +460,13 @@ struct ScanWave {
         IO* dr = ds + lane * drs - doff;
         const float* br = bs - boff * NS;
         const float* cr = cs - boff * NS;
+        const bool pad = p.pad_in != 0;
         float win[KW];
 #pragma unroll
         for (int j = 0; j < KW; ++j) win[j] = 0.0f;
         if constexpr (CONV) {
 #pragma unroll
-            for (int j = 0; j < KW - 1; ++j) {
-                const int q = t0 - P + j;
-                win[j + 1] = (q >= 0 && q < L) ? to_f32(xr[q]) : 0.0f;
-            }
+            for (int j = 0; j < KW - 1; ++j) win[j + 1] = xat(xr, t0 - P + j, L, pad);
         }
         const int lag = CONV ? KW - 1 - P : 0;  // newest conv tap is x[t + lag]
         int t = t0;
@@ -410,8 +475,7 @@ struct ScanWave {
         float xc, dc;
         float4 bq[NS / 4], cq[NS / 4];
         auto fetch = [&](int tt, float& xv, float& dv, float4 (&bb)[NS / 4], float4 (&cc)[NS / 4]) {
-            const int q = tt + lag;
-            xv = (q < L) ? to_f32(xr[q]) : 0.0f;
+            xv = xat(xr, tt + lag, L, pad);
             dv = to_f32(dr[tt]);
             load_bc(br, cr, tt, bb, cc);
         };
@@ -583,6 +647,9 @@ int odd_word_stride(int elems, int elem_bytes) {
 
 bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint) {
     const int L = p.L, S = p.B2 * p.L;
+    if (p.xrow <= 0) p.xrow = p.pad_in ? L - 2 : L;
+    const int XL = p.xrow;
+    const bool fused = p.pad_in || p.swap_out;  // these keep each sample inside one wave
     p.ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
     const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 0;
     p.tiles = (p.D + kWave - 1) / kWave;
@@ -594,10 +661,10 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint) {
     // per-wave x / delta stages
     auto xd_bytes = [&](int ch, int mode, int& xsb, int& dsb, int& xrs, int& drs) {
         if (mode == 0) {
-            xrs = L;
+            xrs = XL;
             drs = L;
-            xsb = kWave * L * io_bytes;
-            dsb = xsb;
+            xsb = kWave * XL * io_bytes;
+            dsb = kWave * L * io_bytes;
         } else {
             // mode 1 rows hold the chunk plus word alignment at both ends
             const int extra = mode == 1 ? 2 * (ew - 1) : 0;
@@ -615,20 +682,20 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint) {
     // mode 0 (whole rows) when the [64 x L] slabs are 16-byte aligned and small
     int mode = 2;
     int ch = ch_hint > 0 ? ch_hint : 32;
-    if (L <= 256 && ((long long)p.D * L * io_bytes) % 16 == 0 && ch_hint <= 0 &&
-        xd_bytes(L, 0, xsb, dsb, xrs, drs) + bc_bytes(L) <= 20 * 1024) {
+    if (L <= 256 && ((long long)p.D * L * io_bytes) % 16 == 0 && ((long long)p.D * XL * io_bytes) % 16 == 0 &&
+        ch_hint <= 0 && xd_bytes(L, 0, xsb, dsb, xrs, drs) + bc_bytes(L) <= 20 * 1024) {
         mode = 0;
         ch = L;
     }
     if (mode != 0) {
-        mode = ((long long)L * io_bytes) % 4 == 0 ? 1 : 2;
+        mode = ((long long)L * io_bytes) % 4 == 0 && ((long long)XL * io_bytes) % 4 == 0 ? 1 : 2;
         if (ch > L) ch = L;
     }
     // pieces per folded row
     int W;
-    if (waves_hint > 0) {
+    if (waves_hint > 0 && !fused) {
         W = waves_hint;
-    } else if (S <= 256 || p.B2 > 1) {
+    } else if (S <= 256 || p.B2 > 1 || fused) {
         // short rows: one or more whole samples per wave, cuts on sample starts
         W = 1;
         for (int c = 1; c <= kMaxWaves; ++c)

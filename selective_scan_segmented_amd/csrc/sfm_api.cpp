@@ -86,8 +86,22 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
                                   int delta_softplus, const float* conv_w, const float* conv_b, int conv_k,
                                   int conv_pad_left, int conv_act, void* y, int64_t B1, int64_t B2, int64_t D,
                                   int64_t N, int64_t L, int io_dtype, void* stream) {
+    return sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b, conv_k,
+                                     conv_pad_left, conv_act, y, B1, B2, D, N, L, io_dtype, 0, stream);
+}
+
+sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* Bm,
+                                     const void* Cm, const float* Dskip, const float* delta_bias,
+                                     int delta_softplus, const float* conv_w, const float* conv_b, int conv_k,
+                                     int conv_pad_left, int conv_act, void* y, int64_t B1, int64_t B2, int64_t D,
+                                     int64_t N, int64_t L, int io_dtype, int flags, void* stream) {
     if (!u || !delta || !A || !Bm || !Cm || !y)
         return fail(SFM_ERR_NULL, "sfm_selective_scan_fwd: u, delta, A, Bm, Cm and y are required");
+    if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP))
+        return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd_ex: unknown flags 0x%x", flags);
+    const bool pad_in = (flags & SFM_FUSE_PAD) != 0;
+    if (pad_in && L < 3)
+        return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd_ex: SFM_FUSE_PAD needs L >= 3, got %lld", (long long)L);
     if (io_dtype != SFM_F32 && io_dtype != SFM_BF16)
         return fail(SFM_ERR_DTYPE, "sfm_selective_scan_fwd: io_dtype %d", io_dtype);
     if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24))
@@ -115,7 +129,8 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
     const int64_t B = B1 * B2;
     const int eb = io_bytes(io_dtype);
     const Range ry = rng("y", y, B * D * L * eb);
-    const Range ins[] = {rng("u", u, B * D * L * eb), rng("delta", delta, B * D * L * eb),
+    const int64_t XL = pad_in ? L - 2 : L;
+    const Range ins[] = {rng("u", u, B * D * XL * eb), rng("delta", delta, B * D * L * eb),
                          rng("Bm", Bm, B * N * L * eb), rng("Cm", Cm, B * N * L * eb),
                          rng("A", A, D * N * 4)};
     for (const Range& r : ins)
@@ -141,6 +156,9 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
     p.P = conv_w ? conv_pad_left : 0;
     p.act = conv_w ? conv_act : 0;
     p.softplus = delta_softplus;
+    p.pad_in = pad_in ? 1 : 0;
+    p.swap_out = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+    p.xrow = (int)XL;
     int waves_hint = 0, ch_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_WAVES")) waves_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_CHUNK")) ch_hint = std::atoi(e);
@@ -150,7 +168,7 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
 }
 
 sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int conv_k, int io_dtype,
-                                char* buf, int64_t cap) {
+                                int flags, char* buf, int64_t cap) {
     if (!buf || cap < 1) return fail(SFM_ERR_NULL, "sfm_scan_plan_string: buf is required");
     if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "sfm_scan_plan_string: io_dtype");
     if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24) || N < 1 ||
@@ -165,6 +183,11 @@ sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, in
     p.N = (int)N;
     p.L = (int)L;
     p.K = conv_k ? conv_k : 1;
+    if ((flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP)) || ((flags & SFM_FUSE_PAD) && L < 3))
+        return fail(SFM_ERR_SHAPE, "sfm_scan_plan_string: bad flags for these sizes");
+    p.pad_in = (flags & SFM_FUSE_PAD) ? 1 : 0;
+    p.swap_out = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+    p.xrow = p.pad_in ? (int)L - 2 : (int)L;
     int waves_hint = 0, ch_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_WAVES")) waves_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_CHUNK")) ch_hint = std::atoi(e);

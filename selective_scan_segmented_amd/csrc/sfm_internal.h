@@ -21,6 +21,9 @@ struct ScanParams {
     void* y;
     int B1, B2, D, N, L;
     int K, P, act, softplus;
+    int pad_in;      // u holds unpadded rows of L-2 tokens; the aux pad is fused
+    int swap_out;    // y is written with positions 0 and L-1 exchanged
+    int xrow;        // row length of the u tensor (L, or L-2 with pad_in)
     // plan (filled by plan_scan)
     int ns;          // compiled state count (4, 8 or 16) >= N
     int tiles;       // ceil(D / 64)

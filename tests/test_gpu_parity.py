@@ -376,3 +376,108 @@ def test_L1_scan():
     sync()
     want = oracle.selective_scan(arrs[0], arrs[1], A, arrs[2], arrs[3])
     assert_close(from_dev(y), want, "f32", "L=1")
+
+
+# ------------------------------------------------- fused aux pad / aux swap
+
+FUSE_CASES = [
+    # name, B2   (tiny: f32 whole rows; stage4: whole rows; stage3/base/long: chunked rows)
+    ("tiny", 1), ("tiny", 2), ("stage4", 1), ("stage4", 4), ("stage3", 1), ("stage3", 8),
+]
+
+
+@pytest.mark.parametrize("name,B2", FUSE_CASES)
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_fused_pad_swap_matches_unfused_chain(name, B2, flags):
+    """sfm_selective_scan_fwd_ex(flags) is bit-identical to pad -> scan -> swap."""
+    say(f"fused {name} B2={B2} flags={flags}")
+    li = layer_inputs(name)
+    prm = dev_params(li)
+    x = to_dev(li.x)
+    d, Bm, Cm = to_dev(li.delta), to_dev(li.Bm), to_dev(li.Cm)
+    xp = sfm.sfm_aux_pad_swap(x, mode="pad")
+    ref = sfm.sfm_selective_scan_fwd(xp, d, prm["A"], Bm, Cm, prm["Dskip"], prm["delta_bias"],
+                                     conv_w=prm["conv_w"], conv_pad_left=1, B2=B2)
+    if flags & 2:
+        sfm.sfm_aux_pad_swap(ref, out=ref, mode="swap")
+    u_in = x if flags & 1 else xp
+    got = sfm.sfm_selective_scan_fwd_ex(u_in, d, prm["A"], Bm, Cm, prm["Dskip"], prm["delta_bias"],
+                                        conv_w=prm["conv_w"], conv_pad_left=1, B2=B2, flags=flags)
+    sync()
+    assert np.array_equal(from_dev(got), from_dev(ref))
+
+
+def test_fused_stage4_against_oracle():
+    li = layer_inputs("stage4")
+    prm = dev_params(li)
+    got = sfm.sfm_selective_scan_fwd_ex(to_dev(li.x), to_dev(li.delta), prm["A"], to_dev(li.Bm), to_dev(li.Cm),
+                                        prm["Dskip"], prm["delta_bias"], conv_w=prm["conv_w"], conv_pad_left=1,
+                                        B2=1, flags=3)
+    sync()
+    key = ("oracle", "stage4")
+    if key not in _cache:
+        _cache[key] = oracle_layer(li)
+    assert_close(from_dev(got), oracle.aux_swap(_cache[key]), "bf16", "fused stage4")
+
+
+@pytest.mark.parametrize("name", ["base_stage3", "long"])
+def test_fused_sampled_against_oracle(name):
+    say(f"fused sampled {name}")
+    li = layer_inputs(name)
+    prm = dev_params(li)
+    w = synth.WORKLOADS[name]
+    B2 = w.B // sfm.sfm_pick_b1(w.B, w.L, w.D, w.N)
+    got = sfm.sfm_selective_scan_fwd_ex(to_dev(li.x), to_dev(li.delta), prm["A"], to_dev(li.Bm), to_dev(li.Cm),
+                                        prm["Dskip"], prm["delta_bias"], conv_w=prm["conv_w"], conv_pad_left=1,
+                                        B2=B2, flags=3)
+    sync()
+    samples = np.array([0, w.B // 2, w.B - 1])
+    want = oracle.aux_swap(oracle_layer(li, samples))
+    assert_close(from_dev(got)[samples], want, "bf16", f"fused {name}")
+
+
+@pytest.mark.parametrize("B,D,N,T,B2,K,P,io", [
+    (3, 70, 5, 49, 3, 4, 1, "bf16"),    # ragged tile, odd L, whole rows
+    (2, 40, 8, 299, 1, 4, 2, "bf16"),   # odd L > 256: element staging, chunked mean
+    (2, 72, 16, 300, 2, 3, 0, "f32"),   # chunked tiles in f32
+    (4, 8, 4, 1, 2, 2, 1, "f32"),       # T = 1: mean of a single token
+])
+def test_fused_edge_shapes(B, D, N, T, B2, K, P, io):
+    import torch
+    r = np.random.default_rng(T * 7 + D)
+    L = T + 2
+    f = lambda *s: r.standard_normal(s).astype(np.float32)
+    x, delta, Bm, Cm = f(B, D, T), f(B, D, L), f(B, N, L), f(B, N, L)
+    if io == "bf16":
+        cast = lambda a: synth.f32_to_bf16_bits(a)
+    else:
+        cast = lambda a: a
+    x, delta, Bm, Cm = map(cast, (x, delta, Bm, Cm))
+    A = (-r.uniform(0.5, 4.0, (D, N))).astype(np.float32)
+    Dk, db = f(D), r.uniform(-4, -1, D).astype(np.float32)
+    cw = r.uniform(-0.5, 0.5, (D, K)).astype(np.float32)
+    T_ = lambda a: torch.from_numpy(a).cuda()
+    xd, dd, Bd, Cd = map(to_dev, (x, delta, Bm, Cm))
+    xp = sfm.sfm_aux_pad_swap(xd, mode="pad")
+    ref = sfm.sfm_selective_scan_fwd(xp, dd, T_(A), Bd, Cd, T_(Dk), T_(db), conv_w=T_(cw), conv_pad_left=P, B2=B2)
+    sfm.sfm_aux_pad_swap(ref, out=ref, mode="swap")
+    got = sfm.sfm_selective_scan_fwd_ex(xd, dd, T_(A), Bd, Cd, T_(Dk), T_(db), conv_w=T_(cw), conv_pad_left=P,
+                                        B2=B2, flags=3)
+    sync()
+    assert np.array_equal(from_dev(got), from_dev(ref))
+    up = lambda a: synth.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+    want = oracle.aux_swap(oracle.layer(oracle.aux_pad(up(x), io), up(delta), A, up(Bm), up(Cm), Dk, db, cw,
+                                        pad_left=P))
+    assert_close(from_dev(got), want, io, "fused edge")
+
+
+def test_fused_pad_rejects_short_rows():
+    import torch
+    u = torch.zeros((2, 4, 1), device="cuda")  # L - 2 = 1 -> L = 3 is fine; L = 2 is not expressible here
+    A = torch.zeros((4, 2), device="cuda")
+    BC = torch.zeros((2, 2, 3), device="cuda")
+    sfm.sfm_selective_scan_fwd_ex(u, torch.zeros((2, 4, 3), device="cuda"), A, BC, BC, flags=1)
+    lib = sfm.load_library()
+    rc = lib.sfm_selective_scan_fwd_ex(u.data_ptr(), u.data_ptr(), A.data_ptr(), BC.data_ptr(), BC.data_ptr(),
+                                       None, None, 1, None, None, 0, 0, 0, A.data_ptr(), 2, 1, 4, 2, 2, 0, 1, None)
+    assert rc == 2  # SFM_ERR_SHAPE: SFM_FUSE_PAD needs L >= 3
