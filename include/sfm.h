@@ -96,6 +96,13 @@ typedef enum { SFM_AUX_PAD = 0, SFM_AUX_SWAP = 1 } sfm_aux_mode;
  *   io_dtype   sfm_dtype of u, delta, Bm, Cm and y
  *   stream     hipStream_t or NULL
  * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN (nothing launched) or HIP.
+ *
+ * Launch-plan overrides (environment, read on every call; for tuning and
+ * tests, results do not depend on them beyond float32 summation order):
+ *   SFM_SCAN_WAVES=w    pieces per folded row (carried state between pieces)
+ *   SFM_SCAN_CHUNK=c    positions per LDS chunk (tiled staging)
+ *   SFM_SCAN_STAGGER=t  delay per dispatch round in 10 ns ticks (0 = off) for
+ *                       grids that are resident all at once
  */
 sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
                                   const void* Cm, const float* Dskip, const float* delta_bias,

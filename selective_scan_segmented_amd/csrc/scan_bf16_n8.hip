@@ -1,0 +1,4 @@
+// scan_bf16_n8.hip -- selective-scan kernels for bf16 io and up to 8 states.
+#include "scan_kernel.h"
+
+SFM_SCAN_INSTANCE(__bf16, bf16, 8)

@@ -1,0 +1,795 @@
+// scan_kernel.h -- the selective-scan kernel template (included by the
+// per-type instantiation units scan_<io>_n<N>.hip and by scan.hip).
+//
+// Method ("Seeing Both Ways, Running One Way", sections 3.1 and 3.3; techloop
+// walkthrough "第二个模块：Batch Folding with Periodic State Reset"):
+//   h_s = Abar_s * h_{s-1} + Bbar_s x_s,  y_s = C_s h_s (+ D x_s)
+// over folded rows of B2 samples, Abar_s = 0 where s mod L == 0.
+//
+// Work mapping (MI355X-first, not the pages' CUDA one):
+//  * A workgroup owns one folded row b1 and one tile of 64 channels.  The 64
+//    lanes of a wave are 64 channels, so every lane walks the same (sample, t)
+//    at the same time: B[b,:,t] and C[b,:,t] are wave-uniform and are staged
+//    once per wave in LDS as float32, read back as 16-byte broadcasts.
+//  * The folded row (B2*L positions) is cut into `waves` contiguous pieces, one
+//    per wave.  Each lane scans its piece sequentially with the N-state float32
+//    recurrence in registers -- no cross-lane scan is needed, because the
+//    channel dimension already fills the wave; this removes the short-sequence
+//    under-fill the pages attribute to per-sequence warp scans.
+//  * The reset is a re-initialisation (h <- Bbar x) at every sample start, so
+//    non-finite values never cross a sample boundary.
+//  * When a piece starts inside a sample, the wave needs the state carried in
+//    from the piece before it.  Phase 1: every wave computes the aggregate of
+//    its piece's tail segment (from its last sample start, or the whole piece if
+//    it holds none): flag "contains a reset", sum of Delta*log2e (so the decay
+//    product is exp2(A * sum)) and the end state from zero.  The aggregates meet
+//    in LDS; each wave folds its predecessors' aggregates with the segmented
+//    operator (a reset cuts the carry) and phase 2 rescans its piece from that
+//    carry, writing y.  Phase 1 is skipped when all cuts fall on sample starts.
+//  * Folding is index arithmetic only: position s of row b1 is sample
+//    b = b1*B2 + s/L at t = s mod L; nothing is copied.
+//  * Staging (per chunk of positions, through LDS):
+//      mode 0 -- whole sample rows: the [64 x L] conv-input and delta slabs are
+//                contiguous, so they go straight into LDS by 16-byte direct
+//                global->LDS transfers, all in flight at once;
+//      mode 1 -- tiles of even-length rows: 4-byte direct transfers into LDS
+//                rows padded to an odd number of words (no bank conflicts when
+//                the 64 lanes read one column);
+//      mode 2 -- element loads (any shape), 16 per lane in flight.
+//    B and C become float32 [t][n] in LDS; y overwrites delta in LDS and is
+//    stored with wide coalesced stores.
+//  * The position loop is software-pipelined: the LDS reads of position t+1
+//    are issued before position t computes, so the wave does not wait on LDS
+//    latency each step, and at most two positions' inputs are live.
+//  * The optional depthwise conv is fused: a register window slides over the
+//    staged conv input and taps outside the sample read zero (the boundary
+//    masking of the techloop walkthrough's conv-boundary part).
+#pragma once
+
+#include "sfm_device.h"
+#include "sfm_internal.h"
+
+namespace sfm {
+namespace scan_detail {
+
+constexpr int kMaxWaves = 8;
+
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+struct ScanWave {
+    const ScanParams& p;
+    const int lane;
+    const int d0;
+    const int nrows;  // valid channel rows of this tile (<= 64)
+    const int b1;
+    // per-lane parameters
+    float A[NS];
+    float Dk, dbias, cw[KW], cb;
+    // LDS stages
+    IO* xs;
+    IO* ds;
+    float* bs;
+    float* cs;
+    IO* braw;  // mode 0 with bc_dma: raw B then C of one sample, [N][L] each
+    // geometry of the staged chunk: value at position q of this lane's row is
+    // xs[lane*xrs + q - xoff], ds[lane*drs + q - doff]; B/C at bs[(q-boff)*NS + n]
+    int xrs, xoff, drs, doff, boff;
+    const int wc;  // index of this wave among the cw waves sharing the B/C stage
+    float mean;    // fused aux pad: this row's head/tail token value (io-rounded)
+    IO y0;         // fused swap: y at t = 0 of the current sample, written last
+
+    __device__ __forceinline__ ScanWave(const ScanParams& p_, int lane_, int d0_, int b1_, char* own, float* bshared, int wc_)
+        : p(p_), lane(lane_), d0(d0_), nrows(max(0, min(kWave, p_.D - d0_))), b1(b1_), wc(wc_), mean(0.0f),
+          y0(Io<IO>::zero()) {
+        xs = reinterpret_cast<IO*>(own);
+        ds = reinterpret_cast<IO*>(own + p.xs_bytes);
+        bs = bshared;
+        cs = bshared + p.ch * NS;
+        braw = reinterpret_cast<IO*>(reinterpret_cast<char*>(bshared) + p.bcr_off);
+    }
+
+    // States n >= N stay zero in B and C for the whole kernel (the first
+    // stage's barrier publishes this to the other waves of the group).
+    __device__ __forceinline__ void zero_unused_states() {
+        if (wc == 0 && p.N < NS) {
+            for (int e = lane; e < p.ch * NS; e += kWave) {
+                if (e % NS >= p.N) {
+                    bs[e] = 0.0f;
+                    cs[e] = 0.0f;
+                }
+            }
+        }
+        wave_lds_sync();
+    }
+
+    // Per-channel parameters into registers.  Called once, after the first
+    // stage's loads are in flight, so that they do not delay those.
+    bool params_loaded = false;
+    __device__ __forceinline__ void load_params() {
+        const int d = d0 + lane;
+        const bool valid = d < p.D;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) A[n] = (valid && n < p.N) ? p.A[(size_t)d * p.N + n] : 0.0f;
+        Dk = (valid && p.Dskip) ? p.Dskip[d] : 0.0f;
+        dbias = (valid && p.dbias) ? p.dbias[d] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) cw[j] = (CONV && valid && j < p.K) ? p.conv_w[(size_t)d * p.K + j] : 0.0f;
+        cb = (CONV && valid && p.conv_b) ? p.conv_b[d] : 0.0f;
+        params_loaded = true;
+    }
+
+    // ------------------------------------------------------------ staging
+    // Raw B/C of a whole sample (already in LDS) -> float32 [t][n].
+    __device__ __forceinline__ void widen_bc() {
+        const int L = p.L, tot = p.N * L;
+        const float invL = 1.0f / (float)L;
+        for (int e = lane; e < tot; e += kWave) {
+            const int n = div_small(e, invL);
+            const int t = e - n * L;
+            bs[t * NS + n] = to_f32(braw[e]);
+            cs[t * NS + n] = to_f32(braw[tot + e]);
+        }
+    }
+
+    // B/C of sample b, positions [lo, lo + cnt) -> float32 [q - boff][n].
+    // wide: 16-byte loads of the whole [N x L] block (lo == 0, cnt == L, aligned)
+    __device__ __forceinline__ void stage_bc(const IO* bg, const IO* cg, int lo, int cnt, bool wide) {
+        const int L = p.L, N = p.N;
+        if (wide) {
+            constexpr int per = 16 / (int)sizeof(IO);
+            const int total = N * L;
+            const int units = total / per;
+            const float invL = 1.0f / (float)L;
+            for (int u0 = 0; u0 < units; u0 += 4 * kWave) {
+                uint4 vb[4], vc[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int u = u0 + k * kWave + lane;
+                    if (u < units) {
+                        vb[k] = reinterpret_cast<const uint4*>(bg)[u];
+                        vc[k] = reinterpret_cast<const uint4*>(cg)[u];
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int u = u0 + k * kWave + lane;
+                    if (u < units) {
+                        int n = div_small(u * per, invL);
+                        int t = u * per - n * L;
+#pragma unroll
+                        for (int j = 0; j < per; ++j) {
+                            bs[t * NS + n] = unpack<IO>(vb[k], j);
+                            cs[t * NS + n] = unpack<IO>(vc[k], j);
+                            if (++t == L) {
+                                t = 0;
+                                ++n;
+                            }
+                        }
+                    }
+                }
+            }
+            for (int e = units * per + lane; e < total; e += kWave) {
+                const int n = div_small(e, invL);
+                const int t = e - n * L;
+                bs[t * NS + n] = to_f32(bg[e]);
+                cs[t * NS + n] = to_f32(cg[e]);
+            }
+        } else {
+            const int total = N * cnt;
+            const float inv = 1.0f / (float)cnt;
+            for (int e0 = 0; e0 < total; e0 += 8 * kWave) {
+                IO vb[8], vc[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int e = e0 + k * kWave + lane;
+                    if (e < total) {
+                        const int n = div_small(e, inv);
+                        const int i = e - n * cnt;
+                        vb[k] = bg[(size_t)n * L + lo + i];
+                        vc[k] = cg[(size_t)n * L + lo + i];
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int e = e0 + k * kWave + lane;
+                    if (e < total) {
+                        const int n = div_small(e, inv);
+                        const int i = e - n * cnt;
+                        bs[(lo + i - boff) * NS + n] = to_f32(vb[k]);
+                        cs[(lo + i - boff) * NS + n] = to_f32(vc[k]);
+                    }
+                }
+            }
+        }
+    }
+
+    // mode 1: rows x positions [lo, hi) (lo, hi multiples of the elements per
+    // 4-byte word) by 4-byte direct transfers into LDS rows of `rs` elements.
+    // Lane-contiguous LDS words, per-lane global addresses; words outside the
+    // valid rows are not transferred (never read).
+    __device__ __forceinline__ void dma_tile(const IO* g, IO* l, int rs, int lo, int hi, int L) {
+        constexpr int ew = 4 / (int)sizeof(IO);
+        const int rsw = rs / ew;        // words per LDS row (odd)
+        const int nw = (hi - lo) / ew;  // words to move per row
+        const float inv = 1.0f / (float)rsw;
+        char* lb = reinterpret_cast<char*>(l);
+        // 64 words per instruction, rsw instructions per tile, sixteen per LDS base
+        for (int k0 = 0; k0 < rsw; k0 += 16) {
+            char* lk = lb + k0 * 256;
+            static_for<16>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if (k0 + k < rsw) {
+                    const int e = (k0 + k) * kWave + lane;
+                    const int r = div_small(e, inv);
+                    const int w = e - r * rsw;
+                    if (r < nrows && w < nw) dma_at<4, k * 256>(g + (size_t)r * L + lo + w * ew, lk);
+                }
+            });
+        }
+    }
+
+    // rows x [lo, lo + cnt) of a [rows, L] slab -> LDS rows of stride `rs`;
+    // positions outside [0, L) become zero.  16 element loads per lane in flight.
+    __device__ __forceinline__ void stage_rows(const IO* g, IO* l, int rs, int lo, int cnt, int L) {
+        const int total = nrows * cnt;
+        const float inv = 1.0f / (float)cnt;
+        for (int e0 = 0; e0 < total; e0 += 16 * kWave) {
+            IO v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int e = e0 + k * kWave + lane;
+                v[k] = Io<IO>::zero();
+                if (e < total) {
+                    const int c = div_small(e, inv);
+                    const int t = lo + e - c * cnt;
+                    if (t >= 0 && t < L) v[k] = g[(size_t)c * L + t];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int e = e0 + k * kWave + lane;
+                if (e < total) {
+                    const int c = div_small(e, inv);
+                    l[c * rs + e - c * cnt] = v[k];
+                }
+            }
+        }
+    }
+
+    // Mode 0: put the direct transfers of sample b's whole rows (and, with
+    // bc_dma, its raw B/C) in flight.  The [64 x XL] and [64 x L] slabs are
+    // contiguous and 16-byte aligned.
+    bool prefetched = false;
+    __device__ __forceinline__ void issue0(int b) {
+        const int L = p.L, D = p.D, XL = p.xrow;
+        const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * XL;
+        const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
+        const int nx = nrows * XL, nd = nrows * L;
+        if (ds == xs + nx && (nx * (int)sizeof(IO)) % 16 == 0) {
+            // the two stages are adjacent in LDS: one transfer list
+            dma2_to_lds(xg, nx * (int)sizeof(IO) / 16, dg, nd * (int)sizeof(IO) / 16, xs, lane);
+        } else {
+            dma_to_lds(xg, xs, nx * (int)sizeof(IO), lane);
+            dma_to_lds(dg, ds, nd * (int)sizeof(IO), lane);
+        }
+        if (p.bc_dma && (p.cw == 1 || wc == 0)) {
+            const int nbc = p.N * L * (int)sizeof(IO) / 16;
+            dma2_to_lds(static_cast<const IO*>(p.Bm) + (size_t)b * p.N * L, nbc,
+                        static_cast<const IO*>(p.Cm) + (size_t)b * p.N * L, nbc, braw, lane);
+        }
+    }
+
+    // Stage the inputs of sample b for positions [t0, t0 + len) into LDS.
+    // With cw > 1 the waves of a group share one B/C stage, written by wave 0
+    // between two workgroup barriers (every wave stages the same chunks).
+    __device__ __forceinline__ void stage(int b, int t0, int len, bool first) {
+        const int L = p.L, D = p.D, N = p.N;
+        const int XL = p.xrow;             // row length of the u tensor
+        const int sh = p.pad_in ? 1 : 0;   // padded position q reads u row index q - sh
+        const bool shared = p.cw > 1;
+        if (shared && !first) __syncthreads();  // the previous chunk's B/C has been consumed
+        const bool own_bc = !shared || wc == 0;
+        const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * XL;
+        const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
+        const IO* bg = static_cast<const IO*>(p.Bm) + (size_t)b * N * L;
+        const IO* cg = static_cast<const IO*>(p.Cm) + (size_t)b * N * L;
+        if (p.pad_in && p.mode != 0 && t0 == 0) row_mean(xg);
+        if (p.mode == 0) {
+            xrs = XL; xoff = sh; drs = L; doff = 0; boff = 0;
+            const int nx = nrows * XL, nd = nrows * L;
+            if (!prefetched) issue0(b);
+            prefetched = false;
+            if (!params_loaded) load_params();
+            if (!p.bc_dma && own_bc) stage_bc(bg, cg, 0, L, p.bc_wide != 0);
+            wait_vmem();
+            // elements past the last whole 16-byte unit (only when nrows < 64)
+            const int donex = (nx * (int)sizeof(IO) & ~15) / (int)sizeof(IO);
+            const int doned = (nd * (int)sizeof(IO) & ~15) / (int)sizeof(IO);
+            if (lane < nx - donex) xs[donex + lane] = xg[donex + lane];
+            if (lane < nd - doned) ds[doned + lane] = dg[doned + lane];
+            wave_lds_sync();
+            if (p.bc_dma && own_bc) widen_bc();
+            if (p.pad_in) {
+                // float64, index order: bit-identical to the aux pad
+                const double acc = lane < nrows ? sum_in_order(xs + lane * XL, XL, 0.0) : 0.0;
+                mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+            }
+        } else if (p.mode == 1) {
+            constexpr int ew = 4 / (int)sizeof(IO);
+            xrs = p.xrs; drs = p.drs;
+            // padded positions [qa, qb) needed, i.e. u row indices [qa - sh, qb - sh)
+            int qa = (CONV ? t0 - p.P : t0) - sh;
+            int qb = (CONV ? t0 + len + KW - 1 - p.P : t0 + len) - sh;
+            qa = max(qa, 0) / ew * ew;
+            qb = (min(qb, XL) + ew - 1) / ew * ew;
+            xoff = qa + sh;
+            const int da = t0 / ew * ew;
+            const int db = (t0 + len + ew - 1) / ew * ew;
+            doff = da;
+            boff = t0;  // B/C rows hold exactly [t0, t0 + len): ch rows are allocated
+            if (qb > qa) dma_tile(xg, xs, xrs, qa, qb, XL);
+            dma_tile(dg, ds, drs, da, db, L);
+            if (!params_loaded) load_params();
+            if (own_bc) stage_bc(bg, cg, t0, len, false);
+            wait_vmem();
+        } else {
+            xrs = p.xrs; drs = p.drs;
+            const int lo = (CONV ? t0 - p.P : t0) - sh;  // u row index of LDS column 0
+            xoff = lo + sh;
+            doff = t0; boff = t0;
+            if (!params_loaded) load_params();
+            stage_rows(xg, xs, xrs, lo, CONV ? len + KW - 1 : len, XL);
+            stage_rows(dg, ds, drs, t0, len, L);
+            if (own_bc) stage_bc(bg, cg, t0, len, false);
+        }
+        if (shared) __syncthreads();  // B/C of this chunk visible to the whole group
+        wave_lds_sync();
+    }
+
+    // acc + r[0] + r[1] + ... + r[n-1] in float64, one addition at a time in
+    // index order; the LDS reads are issued eight at a time
+    __device__ __forceinline__ double sum_in_order(const IO* r, int n, double acc) const {
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = to_f32(r[i + k]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc += (double)v[k];
+        }
+        for (; i < n; ++i) acc += (double)to_f32(r[i]);
+        return acc;
+    }
+
+    // Fused aux pad, chunked rows: float64 index-order sum of this lane's whole
+    // unpadded row, streamed through the x stage before the sample's first chunk.
+    __device__ __forceinline__ void row_mean(const IO* xg) {
+        constexpr int ew = 4 / (int)sizeof(IO);
+        const int XL = p.xrow;
+        const int step = p.ch;
+        double acc = 0.0;
+        for (int c0 = 0; c0 < XL; c0 += step) {
+            const int cl = min(step, XL - c0);
+            int lo = c0;
+            if (p.mode == 1) {
+                lo = c0 / ew * ew;
+                const int hi = (c0 + cl + ew - 1) / ew * ew;
+                dma_tile(xg, xs, p.xrs, lo, min(hi, XL), XL);
+                wait_vmem();
+            } else {
+                stage_rows(xg, xs, p.xrs, c0, cl, XL);
+            }
+            wave_lds_sync();
+            if (lane < nrows) acc = sum_in_order(xs + lane * p.xrs + c0 - lo, cl, acc);
+            wave_lds_sync();
+        }
+        mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+    }
+
+    // Store y for positions [t0, t0 + len) of sample b (y sits in ds).  With
+    // the fused swap, position 0 is written at column L-1 and vice versa.
+    __device__ __forceinline__ void store(int b, int t0, int len) {
+        const int L = p.L;
+        IO* yg = static_cast<IO*>(p.y) + ((size_t)b * p.D + d0) * L;
+        const bool sw = p.swap_out && L > 1;
+        if (p.mode == 0 && len == L) {
+            if (sw && lane < nrows) {  // exchange the two end tokens of this lane's row in LDS
+                const IO a = ds[lane * L];
+                ds[lane * L] = ds[lane * L + L - 1];
+                ds[lane * L + L - 1] = a;
+            }
+            wave_lds_sync();
+            const int n = nrows * L;
+            const int units = n * (int)sizeof(IO) / 16;
+            for (int u = lane; u < units; u += kWave)
+                reinterpret_cast<uint4*>(yg)[u] = reinterpret_cast<const uint4*>(ds)[u];
+            const int done = units * 16 / (int)sizeof(IO);
+            if (lane < n - done) yg[done + lane] = ds[done + lane];
+            wave_lds_sync();
+            return;
+        }
+        // positions written here; the ends go out last when swapping
+        const int lo = (sw && t0 == 0) ? 1 : t0;
+        const int hi = (sw && t0 + len == L) ? L - 1 : t0 + len;
+        if (sw && t0 == 0 && lane < nrows) y0 = ds[lane * drs + 0 - doff];
+        if (p.mode == 1) {
+            // whole 4-byte words inside [lo, hi), single elements at the edges
+            constexpr int ew = 4 / (int)sizeof(IO);
+            const int ta = (lo + ew - 1) / ew * ew;
+            const int tb = max(ta, hi / ew * ew);
+            if (tb > ta) {
+                const int nw = (tb - ta) / ew;
+                const int total = nrows * nw;
+                const float inv = 1.0f / (float)nw;
+                for (int e = lane; e < total; e += kWave) {
+                    const int r = div_small(e, inv);
+                    const int w = e - r * nw;
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(&ds[r * drs + ta - doff + w * ew]);
+                    *reinterpret_cast<uint32_t*>(&yg[(size_t)r * L + ta + w * ew]) = v;
+                }
+            }
+            if (lane < nrows) {
+                for (int t = lo; t < min(ta, hi); ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
+                for (int t = tb; t < hi; ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
+            }
+        } else if (hi > lo) {
+            const int cnt = hi - lo;
+            const float inv = 1.0f / (float)cnt;
+            for (int e = lane; e < nrows * cnt; e += kWave) {
+                const int c = div_small(e, inv);
+                const int i = e - c * cnt;
+                yg[(size_t)c * L + lo + i] = ds[c * drs + (lo - doff) + i];
+            }
+        }
+        if (sw && t0 + len == L && lane < nrows) {
+            yg[(size_t)lane * L] = ds[lane * drs + (L - 1) - doff];
+            yg[(size_t)lane * L + L - 1] = y0;
+        }
+        wave_lds_sync();
+    }
+
+    // ------------------------------------------------------------ compute
+    // Conv/scan input at padded position q (wave-uniform): zero outside the
+    // sample, the aux-token value at both ends when the pad is fused, else the
+    // staged value.  Branch-free: the LDS read always hits a valid column.
+    __device__ __forceinline__ float xat(const IO* xr, int q, int L, bool pad) const {
+        const int lo = pad ? 1 : 0;
+        const int qc = min(max(q, lo), L - 1 - lo);
+        float v = to_f32(xr[qc]);
+        v = (pad && (q == 0 || q == L - 1)) ? mean : v;
+        return (q < 0 || q >= L) ? 0.0f : v;
+    }
+
+    // B[t, :] and C[t, :] of one position from LDS (16-byte broadcast reads)
+    __device__ __forceinline__ void load_bc(const float* br, const float* cr, int t, float4 (&bq)[NS / 4],
+                                            float4 (&cq)[NS / 4]) {
+        const float4* b4 = reinterpret_cast<const float4*>(br + t * NS);
+        const float4* c4 = reinterpret_cast<const float4*>(cr + t * NS);
+#pragma unroll
+        for (int q = 0; q < NS / 4; ++q) {
+            bq[q] = b4[q];
+            cq[q] = c4[q];
+        }
+    }
+
+    // Makes all of one position's B/C values live at once, so the reads that
+    // produced them are waited for with a single counter wait.
+    __device__ __forceinline__ static void pin_bc(const float4 (&bq)[NS / 4], const float4 (&cq)[NS / 4]) {
+#pragma unroll
+        for (int q = 0; q < NS / 4; q += 2) {
+            if constexpr (NS >= 8) {
+                asm volatile("" ::"v"(bq[q].x), "v"(bq[q].y), "v"(bq[q].z), "v"(bq[q].w), "v"(bq[q + 1].x),
+                             "v"(bq[q + 1].y), "v"(bq[q + 1].z), "v"(bq[q + 1].w), "v"(cq[q].x), "v"(cq[q].y),
+                             "v"(cq[q].z), "v"(cq[q].w), "v"(cq[q + 1].x), "v"(cq[q + 1].y), "v"(cq[q + 1].z),
+                             "v"(cq[q + 1].w));
+            } else {
+                asm volatile("" ::"v"(bq[q].x), "v"(bq[q].y), "v"(bq[q].z), "v"(bq[q].w), "v"(cq[q].x),
+                             "v"(cq[q].y), "v"(cq[q].z), "v"(cq[q].w));
+            }
+        }
+    }
+
+    // One position: conv tap in, Delta, N-state update, readout.  The inputs
+    // arrive as raw LDS bits (xb as float32 bits when XF32, else io bits; db
+    // always io bits) and are widened here, after the pin, so that the reads
+    // issued for the next position stay in flight while this one computes.
+    template <bool OUT, bool FIRST, bool XF32>
+    __device__ __forceinline__ float core(uint32_t xb, uint32_t db, float (&h)[NS], float (&win)[KW], float& sd2,
+                                          const float4 (&bq)[NS / 4], const float4 (&cq)[NS / 4]) {
+        // Opaque to the compiler: pins this position's work after the previous
+        // position's, so the exp work of later positions is not hoisted (it
+        // would cost ~N registers per position and spill).
+        asm volatile("" : "+v"(xb), "+v"(db));
+        pin_bc(bq, cq);
+        const float xnew = XF32 ? __uint_as_float(xb) : Io<IO>::of_bits(xb);
+        const float dl = Io<IO>::of_bits(db) + dbias;
+        float u;
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = 0; j < KW - 1; ++j) win[j] = win[j + 1];
+            win[KW - 1] = xnew;
+            float acc = cb;
+#pragma unroll
+            for (int j = 0; j < KW; ++j) acc = __builtin_fmaf(cw[j], win[j], acc);
+            u = SILU ? silu(acc) : acc;
+        } else {
+            u = xnew;
+        }
+        float d2, dt;  // Delta * log2(e) and Delta
+        if constexpr (SP) {
+            d2 = softplus_log2e(dl);
+            dt = d2 * kLn2;
+        } else {
+            dt = dl;  // exact, so integer-valued steps stay exact
+            d2 = dl * kLog2e;
+        }
+        const float du = dt * u;
+        if constexpr (!OUT) sd2 += d2;
+        float yv = Dk * u;
+#pragma unroll
+        for (int q = 0; q < NS / 4; ++q) {
+            const float bv[4] = {bq[q].x, bq[q].y, bq[q].z, bq[q].w};
+            const float cv[4] = {cq[q].x, cq[q].y, cq[q].z, cq[q].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int n = q * 4 + k;
+                const float bx = du * bv[k];
+                if constexpr (FIRST) {
+                    h[n] = bx;  // reset: state re-initialised at the sample start
+                } else {
+                    const float a = exp2_fast(d2 * A[n]);
+                    h[n] = __builtin_fmaf(a, h[n], bx);
+                }
+                if constexpr (OUT) yv = __builtin_fmaf(cv[k], h[n], yv);
+            }
+        }
+        return yv;
+    }
+
+    // Positions [t, tend) (none of them a sample start), software-pipelined:
+    // two register sets are used alternately, position t computing from one
+    // while position t+1's LDS reads land in the other, so nothing is copied.
+    // CHECK: the newest conv tap may fall outside the sample or on a fused aux
+    // token, so it goes through xat; otherwise it is read from LDS directly.
+    template <bool OUT, bool CHECK>
+    __device__ __forceinline__ void steps(int t, int tend, const IO* xr, IO* dr, const float* br, const float* cr,
+                                          int lag, float (&h)[NS], float (&win)[KW], float& sd2) {
+        if (t >= tend) return;
+        const int L = p.L;
+        const bool pad = p.pad_in != 0;
+        auto fetch = [&](int tt, uint32_t& xv, uint32_t& dv, float4 (&bb)[NS / 4], float4 (&cc)[NS / 4])
+                         __attribute__((always_inline)) {
+            if constexpr (CHECK) xv = __float_as_uint(xat(xr, tt + lag, L, pad));
+            else xv = Io<IO>::bits(xr[tt + lag]);
+            dv = Io<IO>::bits(dr[tt]);
+            load_bc(br, cr, tt, bb, cc);
+        };
+        uint32_t x0, d0, x1, d1;
+        float4 bq0[NS / 4], cq0[NS / 4], bq1[NS / 4], cq1[NS / 4];
+        auto step = [&](int tt, uint32_t xv, uint32_t dv, const float4 (&bb)[NS / 4], const float4 (&cc)[NS / 4])
+                        __attribute__((always_inline)) {
+            const float yv = core<OUT, false, CHECK>(xv, dv, h, win, sd2, bb, cc);
+            if constexpr (OUT) dr[tt] = from_f32<IO>(yv);
+        };
+        fetch(t, x0, d0, bq0, cq0);
+        if constexpr (!CHECK) {
+            // four positions per trip (with a four-tap conv window the window
+            // registers return to their roles after one trip: nothing is copied)
+            for (; t + 4 < tend; t += 4) {
+                fetch(t + 1, x1, d1, bq1, cq1);
+                step(t, x0, d0, bq0, cq0);
+                fetch(t + 2, x0, d0, bq0, cq0);
+                step(t + 1, x1, d1, bq1, cq1);
+                fetch(t + 3, x1, d1, bq1, cq1);
+                step(t + 2, x0, d0, bq0, cq0);
+                fetch(t + 4, x0, d0, bq0, cq0);
+                step(t + 3, x1, d1, bq1, cq1);
+            }
+        } else {
+            for (; t + 2 < tend; t += 2) {
+                fetch(t + 1, x1, d1, bq1, cq1);
+                step(t, x0, d0, bq0, cq0);
+                fetch(t + 2, x0, d0, bq0, cq0);
+                step(t + 1, x1, d1, bq1, cq1);
+            }
+        }
+        // the last one to four positions; set 0 holds position t
+        const int r = tend - t;
+        if (r >= 2) fetch(t + 1, x1, d1, bq1, cq1);
+        step(t, x0, d0, bq0, cq0);
+        if (r >= 2) {
+            if (r >= 3) fetch(t + 2, x0, d0, bq0, cq0);
+            step(t + 1, x1, d1, bq1, cq1);
+            if (r >= 3) {
+                if (r >= 4) fetch(t + 3, x1, d1, bq1, cq1);
+                step(t + 2, x0, d0, bq0, cq0);
+                if (r >= 4) step(t + 3, x1, d1, bq1, cq1);
+            }
+        }
+    }
+
+    // Scan positions [t0, t0 + len) of the staged sample.  OUT: write y into ds.
+    // AGG (OUT = false): accumulate the sum of Delta*log2e in sd2, no output.
+    template <bool OUT>
+    __device__ __forceinline__ void chunk(int t0, int len, float (&h)[NS], float& sd2) {
+        const int L = p.L;
+        const int P = CONV ? p.P : 0;
+        const IO* xr = xs + lane * xrs - xoff;
+        IO* dr = ds + lane * drs - doff;
+        const float* br = bs - boff * NS;
+        const float* cr = cs - boff * NS;
+        const bool pad = p.pad_in != 0;
+        float win[KW];
+#pragma unroll
+        for (int j = 0; j < KW; ++j) win[j] = 0.0f;
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = 0; j < KW - 1; ++j) win[j + 1] = xat(xr, t0 - P + j, L, pad);
+        }
+        const int lag = CONV ? KW - 1 - P : 0;  // newest conv tap is x[t + lag]; P < K <= KW
+        int t = t0;
+        const int tend = t0 + len;
+        if (t == 0) {
+            float4 bq[NS / 4], cq[NS / 4];
+            load_bc(br, cr, 0, bq, cq);
+            const float y0 = core<OUT, true, true>(__float_as_uint(xat(xr, lag, L, pad)),
+                                                             Io<IO>::bits(dr[0]), h, win, sd2, bq, cq);
+            if constexpr (OUT) dr[0] = from_f32<IO>(y0);
+            ++t;
+        }
+        // From t >= 1 on the tap t + lag >= 1 is inside the sample and past a
+        // fused head token; it stays before the tail token while t < tf.
+        const int tf = max(t, min(tend, L - (pad ? 1 : 0) - lag));
+        steps<OUT, false>(t, tf, xr, dr, br, cr, lag, h, win, sd2);
+        steps<OUT, true>(tf, tend, xr, dr, br, cr, lag, h, win, sd2);
+    }
+
+    // Run folded positions [sa, sb) of row b1, state carried in h.
+    // out: write y (phase 2); else accumulate the aggregate (phase 1).  One
+    // call site, so the staging code is inlined once.
+    __device__ __forceinline__ void run(bool out, int sa, int sb, float (&h)[NS], float& sd2) {
+        const int L = p.L;
+        int s = sa;
+        bool first = true;
+        while (s < sb) {
+            const int j = s / L;
+            const int t0 = s - j * L;
+            const int len = min(min(p.ch, L - t0), sb - s);
+            const int b = b1 * p.B2 + j;
+            stage(b, t0, len, first);
+            first = false;
+            if (out) chunk<true>(t0, len, h, sd2);
+            else chunk<false>(t0, len, h, sd2);
+            wave_lds_sync();
+            if (out) store(b, t0, len);
+            s += len;
+        }
+    }
+};
+
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+__global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(NS <= 8 ? 3 : 2)))
+void scan_kernel(ScanParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    if (p.stagger_ticks) {
+        const unsigned long long r = blockIdx.x / p.stagger_period;
+        if (r) {
+            const unsigned long long until = __builtin_amdgcn_s_memrealtime() + r * p.stagger_ticks;
+            while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    // the wave index is the same for all 64 lanes; saying so keeps every
+    // position/piece index derived from it in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
+    // giving each XCD a contiguous run of (row, tile) items keeps the B/C of a
+    // folded row in one XCD's L2.
+    const int G = p.tgroups * p.B1;
+    int g = blockIdx.x;
+    if ((G & 7) == 0) g = (g & 7) * (G >> 3) + (g >> 3);
+    const int b1 = g / p.tgroups;
+    const int tg = g - b1 * p.tgroups;
+    const int wp = wave / p.cw;         // piece of the folded row
+    const int wc = wave - wp * p.cw;    // channel tile within the group
+    char* grp = smem + (size_t)wp * p.group_bytes;
+    ScanWave<IO, NS, KW, CONV, SP, SILU> w(p, lane, (tg * p.cw + wc) * kWave, b1,
+                                 grp + p.bc_bytes + (size_t)wc * (p.xs_bytes + p.ds_bytes),
+                                 reinterpret_cast<float*>(grp), wc);
+
+    const int S = p.B2 * p.L;
+    const int p0 = min(wp * p.piece, S);
+    const int p1 = min(p0 + p.piece, S);
+    // whole-row staging without carries: the first sample's transfers go out
+    // before anything else, so they overlap the rest of the set-up
+    if (p.mode == 0 && !p.need_carry && p0 < p1) {
+        w.issue0(b1 * p.B2 + p0 / p.L);
+        w.prefetched = true;
+    }
+    w.zero_unused_states();
+    float h[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+    float sd2 = 0.0f;
+
+    // phase 1 (only with carries): aggregate of the tail segment of this
+    // piece; phase 2: scan the piece from the carried state and write y
+    for (int phase = p.need_carry ? 1 : 2; phase <= 2; ++phase) {
+        int sa = p0, flag = 1;
+        if (phase == 1 && p0 < p1) {
+            sa = ((p1 - 1) / p.L) * p.L;  // last sample start in the piece
+            if (sa < p0) {
+                sa = p0;
+                flag = 0;
+            }
+        }
+        if (sa < p1) w.run(phase == 2, sa, p1, h, sd2);
+        if (phase == 2) break;
+        char* agg = smem + (size_t)p.waves * p.group_bytes;  // cw == 1 here: wave == piece
+        int* aflag = reinterpret_cast<int*>(agg);
+        float* asum = reinterpret_cast<float*>(agg + kMaxWaves * sizeof(int));
+        float* ah = asum + (size_t)p.waves * kWave;
+        if (lane == 0) aflag[wave] = flag;
+        asum[wave * kWave + lane] = sd2;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) ah[((size_t)wave * NS + n) * kWave + lane] = h[n];
+        __syncthreads();
+        // carry-in: fold predecessors with the segmented operator
+        if (!w.params_loaded) w.load_params();
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+        for (int v = 0; v < wave; ++v) {
+            const int f = aflag[v];
+            const float sv = asum[v * kWave + lane];
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+                const float hv = ah[((size_t)v * NS + n) * kWave + lane];
+                h[n] = f ? hv : __builtin_fmaf(exp2_fast(w.A[n] * sv), h[n], hv);
+            }
+        }
+        sd2 = 0.0f;
+    }
+}
+
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
+    auto kern = scan_kernel<IO, NS, KW, CONV, SP, SILU>;
+    static bool attr_set = false;
+    if (!attr_set && p.lds_bytes > 64 * 1024) {
+        // allow dynamic LDS beyond 64 KB (gfx950 has 160 KB per workgroup)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                160 * 1024) != hipSuccess)
+            (void)hipGetLastError();  // do not leave a stale error for the launch check
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(p.tgroups * p.B1)), dim3((unsigned)(kWave * p.cw * p.waves)),
+                       (size_t)p.lds_bytes, stream, p);
+    return hipGetLastError();
+}
+
+// softplus on/off and the conv activation select separate kernels, so each
+// kernel holds only the position loop it runs
+template <typename IO, int NS, int KW, bool CONV>
+hipError_t launch_sp(const ScanParams& p, hipStream_t s) {
+    const bool silu = CONV && p.act == 1;
+    if (p.softplus) return silu ? launch_t<IO, NS, KW, CONV, true, CONV>(p, s) : launch_t<IO, NS, KW, CONV, true, false>(p, s);
+    return silu ? launch_t<IO, NS, KW, CONV, false, CONV>(p, s) : launch_t<IO, NS, KW, CONV, false, false>(p, s);
+}
+
+template <typename IO, int NS>
+hipError_t launch_ns(const ScanParams& p, hipStream_t s) {
+    if (!p.conv_w) return launch_sp<IO, NS, 4, false>(p, s);
+    if (p.K <= 4) return launch_sp<IO, NS, 4, true>(p, s);
+    return launch_sp<IO, NS, 8, true>(p, s);
+}
+
+}  // namespace scan_detail
+}  // namespace sfm
+
+// One translation unit per (io type, state count) instantiates the kernels:
+// SFM_SCAN_INSTANCE(float, f32, 8) defines sfm::launch_scan_f32_n8.
+#define SFM_SCAN_INSTANCE(IOT, NAME, NSV)                                                     \
+    namespace sfm {                                                                          \
+    hipError_t launch_scan_##NAME##_n##NSV(const ScanParams& p, hipStream_t s) {             \
+        return scan_detail::launch_ns<IOT, NSV>(p, s);                                        \
+    }                                                                                         \
+    }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sfm {
 
 constexpr int kWave = 64;
@@ -20,6 +22,9 @@ template <> struct Io<float> {
     static __device__ __forceinline__ float from_f32(float v) { return v; }
     static __device__ __forceinline__ float from_f64(double v) { return (float)v; }  // RNE
     static __device__ __forceinline__ float zero() { return 0.0f; }
+    // raw element bits held in a 32-bit register, and their float32 value
+    static __device__ __forceinline__ uint32_t bits(float v) { return __float_as_uint(v); }
+    static __device__ __forceinline__ float of_bits(uint32_t b) { return __uint_as_float(b); }
 };
 template <> struct Io<__bf16> {
     static __device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
@@ -41,6 +46,8 @@ template <> struct Io<__bf16> {
         return (__bf16)f;
     }
     static __device__ __forceinline__ __bf16 zero() { return (__bf16)0.0f; }
+    static __device__ __forceinline__ uint32_t bits(__bf16 v) { return __builtin_bit_cast(unsigned short, v); }
+    static __device__ __forceinline__ float of_bits(uint32_t b) { return __uint_as_float(b << 16); }
 };
 
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return Io<T>::to_f32(v); }
@@ -94,16 +101,86 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // global->LDS transfers, has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// One 64-lane direct global->LDS transfer of SIZE bytes per lane: lane i's
+// bytes at global address g land at LDS address l + OFF + i * SIZE.  OFF is an
+// immediate of the instruction (it moves both addresses, so g is passed
+// pre-decremented).  Consecutive transfers that differ only in OFF share one
+// LDS base register; rewriting that register between transfers serialises
+// them (measured on gfx950: about twice the time to land a 13-transfer burst
+// with ten waves per CU).
+template <int SIZE, int OFF>
+__device__ __forceinline__ void dma_at(const void* g, void* l) {
+    static_assert((SIZE == 16 && OFF % 1024 == 0 && OFF < 4096) || (SIZE == 4 && OFF % 256 == 0 && OFF < 4096),
+                  "unsupported transfer size / offset");
+    const char* gp = static_cast<const char*>(g) - OFF;
+    const lds_void_ptr lp = (lds_void_ptr)l;
+    // the builtin takes its size and offset as literals
+#define SFM_DMA_AT(S, O) \
+    if constexpr (SIZE == S && OFF == O) __builtin_amdgcn_global_load_lds(gp, lp, S, O, 0);
+    SFM_DMA_AT(16, 0) SFM_DMA_AT(16, 1024) SFM_DMA_AT(16, 2048) SFM_DMA_AT(16, 3072)
+    SFM_DMA_AT(4, 0) SFM_DMA_AT(4, 256) SFM_DMA_AT(4, 512) SFM_DMA_AT(4, 768)
+    SFM_DMA_AT(4, 1024) SFM_DMA_AT(4, 1280) SFM_DMA_AT(4, 1536) SFM_DMA_AT(4, 1792)
+    SFM_DMA_AT(4, 2048) SFM_DMA_AT(4, 2304) SFM_DMA_AT(4, 2560) SFM_DMA_AT(4, 2816)
+    SFM_DMA_AT(4, 3072) SFM_DMA_AT(4, 3328) SFM_DMA_AT(4, 3584) SFM_DMA_AT(4, 3840)
+#undef SFM_DMA_AT
+}
+
+// Compile-time loop: f(std::integral_constant<int, k>) for k = 0 .. K-1.
+template <int K, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (K > 0) {
+        static_for<K - 1>(f);
+        f(std::integral_constant<int, K - 1>{});
+    }
+}
+
+// Direct global->LDS copy of two regions into one contiguous LDS range:
+// n0 16-byte units from g0, then n1 units from g1, landing at l.  Every
+// instruction moves 64 units; a lane's source lies in g0 or g1 by its unit
+// index, so an instruction may straddle the two.  Full instructions go four per
+// LDS base with no lane mask; only the tail is masked.  `l`, n0 and n1 are
+// wave-uniform; g0, g1 and l 16-byte aligned.  Nothing is waited for.
+__device__ __forceinline__ void dma2_to_lds(const void* g0, int n0, const void* g1, int n1, void* l, int lane) {
+    const int n = n0 + n1;
+    const int full = n >> 6;
+    const char* a = static_cast<const char*>(g0);
+    const char* b = static_cast<const char*>(g1) - (size_t)n0 * 16;
+    char* lb = static_cast<char*>(l);
+    auto src = [&](int u) __attribute__((always_inline)) { return (u < n0 ? a : b) + (size_t)u * 16; };
+    int k = 0;
+    for (; k + 4 <= full; k += 4) {
+        char* ll = lb + k * 1024;
+        const int u = k * 64 + lane;
+        dma_at<16, 0>(src(u), ll);
+        dma_at<16, 1024>(src(u + 64), ll);
+        dma_at<16, 2048>(src(u + 128), ll);
+        dma_at<16, 3072>(src(u + 192), ll);
+    }
+    char* ll = lb + k * 1024;
+    const int u = k * 64 + lane;
+    const int rem = n - u;  // this lane's units left from instruction k on
+    if (rem > 0) dma_at<16, 0>(src(u), ll);
+    if (rem > 64) dma_at<16, 1024>(src(u + 64), ll);
+    if (rem > 128) dma_at<16, 2048>(src(u + 128), ll);
+    if (rem > 192) dma_at<16, 3072>(src(u + 192), ll);
+}
+
 // Issue direct global->LDS copies of the first (bytes & ~15) bytes of a region:
-// 64 lanes x 16 bytes per instruction, no registers involved, nothing waited
-// for.  `g` and `l` must be 16-byte aligned; `l` and `bytes` wave-uniform.
+// 64 lanes x 16 bytes per instruction, four instructions per LDS base, no
+// registers involved, nothing waited for.  `g` and `l` must be 16-byte
+// aligned; `l` and `bytes` wave-uniform.
 __device__ __forceinline__ void dma_to_lds(const void* g, void* l, int bytes, int lane) {
     const int units = bytes >> 4;
-    const char* gb = static_cast<const char*>(g);
+    const char* gb = static_cast<const char*>(g) + lane * 16;
     char* lb = static_cast<char*>(l);
-    for (int u0 = 0; u0 < units; u0 += 64) {
-        if (u0 + lane < units)
-            __builtin_amdgcn_global_load_lds(gb + (size_t)(u0 + lane) * 16, (lds_void_ptr)(lb + u0 * 16), 16, 0, 0);
+    for (int u0 = 0; u0 < units; u0 += 4 * 64) {
+        const char* gg = gb + (size_t)u0 * 16;
+        char* ll = lb + u0 * 16;
+        const int rem = units - u0 - lane;  // this lane moves unit u0 + 64k + lane while 64k < rem
+        if (rem > 0) dma_at<16, 0>(gg, ll);
+        if (rem > 64) dma_at<16, 1024>(gg + 1024, ll);
+        if (rem > 128) dma_at<16, 2048>(gg + 2048, ll);
+        if (rem > 192) dma_at<16, 3072>(gg + 3072, ll);
     }
 }
 

@@ -36,12 +36,27 @@ struct ScanParams {
     int mode;        // staging: 0 whole rows (16-byte DMA), 1 tiles (4-byte DMA), 2 element loads
     int xrs, drs;    // LDS row strides (elements) of the x and delta/y stages
     int bc_wide;     // B/C blocks of whole samples are 16-byte aligned
+    int bc_dma;      // mode 0: B/C of a sample arrive by direct transfer into a raw area, then widen in LDS
+    int bcr_off;     // byte offset of that raw [2][N][L] io area inside the group's B/C region
     int xs_bytes, ds_bytes, bc_bytes, group_bytes, lds_bytes;
+    // Staggered start (0 = off): when the whole grid is resident at once, the
+    // workgroups of dispatch round r = blockIdx / stagger_period issue their
+    // loads r * stagger_ticks (10 ns ticks) after they start.
+    int stagger_period, stagger_ticks;
 };
 
-// Fills the plan fields; waves_hint / ch_hint <= 0 select automatically.
-bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint);
+// Fills the plan fields; waves_hint / ch_hint <= 0 select automatically,
+// stagger_hint < 0 selects automatically, 0 turns the staggered start off and
+// > 0 sets the delay per dispatch round in 10 ns ticks.
+bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint = -1);
 hipError_t launch_scan(const ScanParams& p, int io_dtype, hipStream_t stream);
+// per-(io type, state count) kernel sets, one translation unit each
+hipError_t launch_scan_f32_n4(const ScanParams& p, hipStream_t s);
+hipError_t launch_scan_f32_n8(const ScanParams& p, hipStream_t s);
+hipError_t launch_scan_f32_n16(const ScanParams& p, hipStream_t s);
+hipError_t launch_scan_bf16_n4(const ScanParams& p, hipStream_t s);
+hipError_t launch_scan_bf16_n8(const ScanParams& p, hipStream_t s);
+hipError_t launch_scan_bf16_n16(const ScanParams& p, hipStream_t s);
 
 hipError_t launch_dwconv1d(const void* x, const float* w, const float* bias, void* out, int64_t B1, int64_t B2,
                            int64_t D, int64_t L, int K, int pad_left, int act, int io_dtype, hipStream_t stream);
