@@ -81,7 +81,7 @@ class Hip:
 
 def scan_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("scan.hip", "sfm_device.h", "sfm_internal.h"):
+    for f in ("scan.hip", "scan_kernel.h", "sfm_device.h", "sfm_internal.h"):
         with open(os.path.join(ROOT, "selective_scan_segmented_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -69,18 +69,6 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
         return 2 * ch * p.ns * (int)sizeof(float) + (m == 0 && p.bc_wide ? bcr_bytes : 0);
     };
     int xsb = 0, dsb = 0, xrs = 0, drs = 0;
-    // mode 0 (whole rows) when the [64 x L] slabs are 16-byte aligned and small
-    int mode = 2;
-    int ch = ch_hint > 0 ? ch_hint : 32;
-    if (L <= 256 && ((long long)p.D * L * io_bytes) % 16 == 0 && ((long long)p.D * XL * io_bytes) % 16 == 0 &&
-        ch_hint <= 0 && xd_bytes(L, 0, xsb, dsb, xrs, drs) + bc_bytes(L, 0) <= 20 * 1024) {
-        mode = 0;
-        ch = L;
-    }
-    if (mode != 0) {
-        mode = ((long long)L * io_bytes) % 4 == 0 && ((long long)XL * io_bytes) % 4 == 0 ? 1 : 2;
-        if (ch > L) ch = L;
-    }
     // pieces per folded row
     int W;
     if (waves_hint > 0 && !fused) {
@@ -103,6 +91,22 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     for (int i = 1; i < W; ++i) {
         const int s0 = i * piece;
         if (s0 < S && s0 % L) carry = 1;
+    }
+    // mode 0 (whole rows) when the [64 x L] slabs are 16-byte aligned and
+    // small and no piece starts inside a sample (its kernels hold no carry path)
+    int mode = 2;
+    int ch = ch_hint > 0 ? ch_hint : 32;
+    const int part = p.D % kWave;  // rows of a partial last channel tile
+    if (!carry && L <= 256 && ((long long)p.D * L * io_bytes) % 16 == 0 &&
+        ((long long)p.D * XL * io_bytes) % 16 == 0 && (part * XL * io_bytes) % 16 == 0 &&
+        (part * L * io_bytes) % 16 == 0 && ch_hint <= 0 &&
+        xd_bytes(L, 0, xsb, dsb, xrs, drs) + bc_bytes(L, 0) <= 20 * 1024) {
+        mode = 0;
+        ch = L;
+    }
+    if (mode != 0) {
+        mode = ((long long)L * io_bytes) % 4 == 0 && ((long long)XL * io_bytes) % 4 == 0 ? 1 : 2;
+        if (ch > L) ch = L;
     }
     auto lds_total = [&](int cw, int chv, int& grp) {
         grp = bc_bytes(chv, mode) + cw * xd_bytes(chv, mode, xsb, dsb, xrs, drs);

@@ -54,7 +54,7 @@ namespace scan_detail {
 
 constexpr int kMaxWaves = 8;
 
-template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int MODE>
 struct ScanWave {
     const ScanParams& p;
     const int lane;
@@ -81,7 +81,9 @@ struct ScanWave {
         : p(p_), lane(lane_), d0(d0_), nrows(max(0, min(kWave, p_.D - d0_))), b1(b1_), wc(wc_), mean(0.0f),
           y0(Io<IO>::zero()) {
         xs = reinterpret_cast<IO*>(own);
-        ds = reinterpret_cast<IO*>(own + p.xs_bytes);
+        // whole-row staging packs the delta rows right after this tile's x rows
+        // (one contiguous transfer list; the planner keeps it 16-byte aligned)
+        ds = MODE == 0 ? xs + nrows * p.xrow : reinterpret_cast<IO*>(own + p.xs_bytes);
         bs = bshared;
         cs = bshared + p.ch * NS;
         braw = reinterpret_cast<IO*>(reinterpret_cast<char*>(bshared) + p.bcr_off);
@@ -264,13 +266,8 @@ struct ScanWave {
         const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * XL;
         const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
         const int nx = nrows * XL, nd = nrows * L;
-        if (ds == xs + nx && (nx * (int)sizeof(IO)) % 16 == 0) {
-            // the two stages are adjacent in LDS: one transfer list
-            dma2_to_lds(xg, nx * (int)sizeof(IO) / 16, dg, nd * (int)sizeof(IO) / 16, xs, lane);
-        } else {
-            dma_to_lds(xg, xs, nx * (int)sizeof(IO), lane);
-            dma_to_lds(dg, ds, nd * (int)sizeof(IO), lane);
-        }
+        // the x and delta rows are adjacent in LDS and whole 16-byte units
+        dma2_to_lds(xg, nx * (int)sizeof(IO) / 16, dg, nd * (int)sizeof(IO) / 16, xs, lane);
         if (p.bc_dma && (p.cw == 1 || wc == 0)) {
             const int nbc = p.N * L * (int)sizeof(IO) / 16;
             dma2_to_lds(static_cast<const IO*>(p.Bm) + (size_t)b * p.N * L, nbc,
@@ -292,20 +289,16 @@ struct ScanWave {
         const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
         const IO* bg = static_cast<const IO*>(p.Bm) + (size_t)b * N * L;
         const IO* cg = static_cast<const IO*>(p.Cm) + (size_t)b * N * L;
-        if (p.pad_in && p.mode != 0 && t0 == 0) row_mean(xg);
-        if (p.mode == 0) {
+        if constexpr (MODE != 0) {
+            if (p.pad_in && t0 == 0) row_mean(xg);
+        }
+        if constexpr (MODE == 0) {
             xrs = XL; xoff = sh; drs = L; doff = 0; boff = 0;
-            const int nx = nrows * XL, nd = nrows * L;
             if (!prefetched) issue0(b);
             prefetched = false;
             if (!params_loaded) load_params();
             if (!p.bc_dma && own_bc) stage_bc(bg, cg, 0, L, p.bc_wide != 0);
             wait_vmem();
-            // elements past the last whole 16-byte unit (only when nrows < 64)
-            const int donex = (nx * (int)sizeof(IO) & ~15) / (int)sizeof(IO);
-            const int doned = (nd * (int)sizeof(IO) & ~15) / (int)sizeof(IO);
-            if (lane < nx - donex) xs[donex + lane] = xg[donex + lane];
-            if (lane < nd - doned) ds[doned + lane] = dg[doned + lane];
             wave_lds_sync();
             if (p.bc_dma && own_bc) widen_bc();
             if (p.pad_in) {
@@ -313,7 +306,7 @@ struct ScanWave {
                 const double acc = lane < nrows ? sum_in_order(xs + lane * XL, XL, 0.0) : 0.0;
                 mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
             }
-        } else if (p.mode == 1) {
+        } else if constexpr (MODE == 1) {
             constexpr int ew = 4 / (int)sizeof(IO);
             xrs = p.xrs; drs = p.drs;
             // padded positions [qa, qb) needed, i.e. u row indices [qa - sh, qb - sh)
@@ -370,7 +363,7 @@ struct ScanWave {
         for (int c0 = 0; c0 < XL; c0 += step) {
             const int cl = min(step, XL - c0);
             int lo = c0;
-            if (p.mode == 1) {
+            if constexpr (MODE == 1) {
                 lo = c0 / ew * ew;
                 const int hi = (c0 + cl + ew - 1) / ew * ew;
                 dma_tile(xg, xs, p.xrs, lo, min(hi, XL), XL);
@@ -391,27 +384,23 @@ struct ScanWave {
         const int L = p.L;
         IO* yg = static_cast<IO*>(p.y) + ((size_t)b * p.D + d0) * L;
         const bool sw = p.swap_out && L > 1;
-        if (p.mode == 0 && len == L) {
+        if constexpr (MODE == 0) {  // whole rows: len == L
             if (sw && lane < nrows) {  // exchange the two end tokens of this lane's row in LDS
                 const IO a = ds[lane * L];
                 ds[lane * L] = ds[lane * L + L - 1];
                 ds[lane * L + L - 1] = a;
             }
             wave_lds_sync();
-            const int n = nrows * L;
-            const int units = n * (int)sizeof(IO) / 16;
+            const int units = nrows * L * (int)sizeof(IO) / 16;  // whole units (planner)
             for (int u = lane; u < units; u += kWave)
                 reinterpret_cast<uint4*>(yg)[u] = reinterpret_cast<const uint4*>(ds)[u];
-            const int done = units * 16 / (int)sizeof(IO);
-            if (lane < n - done) yg[done + lane] = ds[done + lane];
             wave_lds_sync();
-            return;
-        }
+        } else {
         // positions written here; the ends go out last when swapping
         const int lo = (sw && t0 == 0) ? 1 : t0;
         const int hi = (sw && t0 + len == L) ? L - 1 : t0 + len;
         if (sw && t0 == 0 && lane < nrows) y0 = ds[lane * drs + 0 - doff];
-        if (p.mode == 1) {
+        if constexpr (MODE == 1) {
             // whole 4-byte words inside [lo, hi), single elements at the edges
             constexpr int ew = 4 / (int)sizeof(IO);
             const int ta = (lo + ew - 1) / ew * ew;
@@ -445,6 +434,7 @@ struct ScanWave {
             yg[(size_t)lane * L + L - 1] = y0;
         }
         wave_lds_sync();
+        }
     }
 
     // ------------------------------------------------------------ compute
@@ -666,7 +656,7 @@ struct ScanWave {
     }
 };
 
-template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int MODE>
 __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(NS <= 8 ? 3 : 2)))
 void scan_kernel(ScanParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -692,7 +682,7 @@ void scan_kernel(ScanParams p) {
     const int wp = wave / p.cw;         // piece of the folded row
     const int wc = wave - wp * p.cw;    // channel tile within the group
     char* grp = smem + (size_t)wp * p.group_bytes;
-    ScanWave<IO, NS, KW, CONV, SP, SILU> w(p, lane, (tg * p.cw + wc) * kWave, b1,
+    ScanWave<IO, NS, KW, CONV, SP, SILU, MODE> w(p, lane, (tg * p.cw + wc) * kWave, b1,
                                  grp + p.bc_bytes + (size_t)wc * (p.xs_bytes + p.ds_bytes),
                                  reinterpret_cast<float*>(grp), wc);
 
@@ -701,7 +691,7 @@ void scan_kernel(ScanParams p) {
     const int p1 = min(p0 + p.piece, S);
     // whole-row staging without carries: the first sample's transfers go out
     // before anything else, so they overlap the rest of the set-up
-    if (p.mode == 0 && !p.need_carry && p0 < p1) {
+    if (MODE == 0 && !p.need_carry && p0 < p1) {
         w.issue0(b1 * p.B2 + p0 / p.L);
         w.prefetched = true;
     }
@@ -713,7 +703,10 @@ void scan_kernel(ScanParams p) {
 
     // phase 1 (only with carries): aggregate of the tail segment of this
     // piece; phase 2: scan the piece from the carried state and write y
-    for (int phase = p.need_carry ? 1 : 2; phase <= 2; ++phase) {
+    // (whole-row staging never has carries: the planner keeps mode 0 for
+    // pieces that start on sample boundaries)
+    const bool carry = MODE != 0 && p.need_carry;
+    for (int phase = carry ? 1 : 2; phase <= 2; ++phase) {
         int sa = p0, flag = 1;
         if (phase == 1 && p0 < p1) {
             sa = ((p1 - 1) / p.L) * p.L;  // last sample start in the piece
@@ -723,7 +716,7 @@ void scan_kernel(ScanParams p) {
             }
         }
         if (sa < p1) w.run(phase == 2, sa, p1, h, sd2);
-        if (phase == 2) break;
+        if (MODE == 0 || phase == 2) break;
         char* agg = smem + (size_t)p.waves * p.group_bytes;  // cw == 1 here: wave == piece
         int* aflag = reinterpret_cast<int*>(agg);
         float* asum = reinterpret_cast<float*>(agg + kMaxWaves * sizeof(int));
@@ -750,9 +743,9 @@ void scan_kernel(ScanParams p) {
     }
 }
 
-template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int MODE>
 hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
-    auto kern = scan_kernel<IO, NS, KW, CONV, SP, SILU>;
+    auto kern = scan_kernel<IO, NS, KW, CONV, SP, SILU, MODE>;
     static bool attr_set = false;
     if (!attr_set && p.lds_bytes > 64 * 1024) {
         // allow dynamic LDS beyond 64 KB (gfx950 has 160 KB per workgroup)
@@ -766,13 +759,22 @@ hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// softplus on/off and the conv activation select separate kernels, so each
-// kernel holds only the position loop it runs
+// The staging mode, softplus on/off and the conv activation select separate
+// kernels, so each kernel holds only the staging path and position loop it
+// runs (a runtime choice would let the compiler keep every path's set-up live).
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+hipError_t launch_mode(const ScanParams& p, hipStream_t s) {
+    if (p.mode == 0) return launch_t<IO, NS, KW, CONV, SP, SILU, 0>(p, s);
+    if (p.mode == 1) return launch_t<IO, NS, KW, CONV, SP, SILU, 1>(p, s);
+    return launch_t<IO, NS, KW, CONV, SP, SILU, 2>(p, s);
+}
+
 template <typename IO, int NS, int KW, bool CONV>
 hipError_t launch_sp(const ScanParams& p, hipStream_t s) {
     const bool silu = CONV && p.act == 1;
-    if (p.softplus) return silu ? launch_t<IO, NS, KW, CONV, true, CONV>(p, s) : launch_t<IO, NS, KW, CONV, true, false>(p, s);
-    return silu ? launch_t<IO, NS, KW, CONV, false, CONV>(p, s) : launch_t<IO, NS, KW, CONV, false, false>(p, s);
+    if (p.softplus)
+        return silu ? launch_mode<IO, NS, KW, CONV, true, CONV>(p, s) : launch_mode<IO, NS, KW, CONV, true, false>(p, s);
+    return silu ? launch_mode<IO, NS, KW, CONV, false, CONV>(p, s) : launch_mode<IO, NS, KW, CONV, false, false>(p, s);
 }
 
 template <typename IO, int NS>

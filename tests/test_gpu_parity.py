@@ -339,6 +339,7 @@ def test_deterministic_and_every_element_written():
     (4, 64, 5, 30, 2, 8, 3, None),    # N padded to 8, widest conv
     (2, 130, 12, 40, 2, 5, 4, "silu"),  # N padded to 16, right-only halo
     (6, 16, 16, 20, 6, 1, 0, None),   # B2 = B: a single folded row
+    (3, 72, 8, 49, 3, 4, 1, None),    # whole-row staging with a partial 8-row tile
     (2, 8, 7, 300, 1, 3, 2, None),    # L > 256: chunked rows, carry across waves
 ])
 def test_edge_shapes(B, D, N, T, B2, K, P, act):
@@ -438,6 +439,7 @@ def test_fused_sampled_against_oracle(name):
 
 @pytest.mark.parametrize("B,D,N,T,B2,K,P,io", [
     (3, 70, 5, 49, 3, 4, 1, "bf16"),    # ragged tile, odd L, whole rows
+    (3, 72, 8, 49, 1, 4, 1, "bf16"),    # whole-row staging with a partial 8-row tile
     (2, 40, 8, 299, 1, 4, 2, "bf16"),   # odd L > 256: element staging, chunked mean
     (2, 72, 16, 300, 2, 3, 0, "f32"),   # chunked tiles in f32
     (4, 8, 4, 1, 2, 2, 1, "f32"),       # T = 1: mean of a single token
