@@ -165,15 +165,15 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     // Staggered start.  Whole-row staging loads everything up front; when the
     // whole grid is resident at once, every wave would otherwise wait for the
     // entire input to arrive before its first step.  Delaying dispatch round r
-    // by r times the time HBM needs for one round's inputs (~4.7 TB/s
-    // measured for this access pattern) lets early rounds compute while later
-    // rounds load.
+    // by about the time HBM needs for one round's inputs (measured best near
+    // 6.5 TB/s worth of a round on MI355X) lets early rounds compute while
+    // later rounds load.
     p.stagger_period = 0;
     p.stagger_ticks = 0;
     const long long grid = (long long)p.tgroups * p.B1;
     if (mode == 0 && !carry && grid > cus && grid <= (long long)cus * best_per_cu && stagger_hint != 0) {
         const long long wg_bytes = (long long)p.cw * kWave * (XL + L) * io_bytes + 2LL * p.N * L * io_bytes;
-        long long ticks = stagger_hint > 0 ? stagger_hint : (long long)cus * wg_bytes / 47000;
+        long long ticks = stagger_hint > 0 ? stagger_hint : (long long)cus * wg_bytes / 65000;
         if (ticks > 500) ticks = 500;
         if (ticks > 0) {
             p.stagger_period = cus;

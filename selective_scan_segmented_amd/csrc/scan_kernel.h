@@ -266,14 +266,20 @@ struct ScanWave {
         const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * XL;
         const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
         const int nx = nrows * XL, nd = nrows * L;
-        // the x and delta rows are adjacent in LDS and whole 16-byte units
-        dma2_to_lds(xg, nx * (int)sizeof(IO) / 16, dg, nd * (int)sizeof(IO) / 16, xs, lane);
+        // order: parameters, B/C, x, delta -- everything but the delta rows can
+        // then be waited for (and used) while the delta rows are still landing
+        if (!params_loaded) load_params();
         if (p.bc_dma && (p.cw == 1 || wc == 0)) {
             const int nbc = p.N * L * (int)sizeof(IO) / 16;
             dma2_to_lds(static_cast<const IO*>(p.Bm) + (size_t)b * p.N * L, nbc,
                         static_cast<const IO*>(p.Cm) + (size_t)b * p.N * L, nbc, braw, lane);
         }
+        // the x and delta rows are adjacent in LDS and whole 16-byte units
+        const int n0 = nx * (int)sizeof(IO) / 16, n = n0 + nd * (int)sizeof(IO) / 16;
+        dma2_to_lds(xg, n0, dg, n - n0, xs, lane);
+        delta_only = (n + 63) / 64 - 1 - (n0 - 1) / 64;  // transfers after the last one holding x
     }
+    int delta_only = 0;
 
     // Stage the inputs of sample b for positions [t0, t0 + len) into LDS.
     // With cw > 1 the waves of a group share one B/C stage, written by wave 0
@@ -296,9 +302,9 @@ struct ScanWave {
             xrs = XL; xoff = sh; drs = L; doff = 0; boff = 0;
             if (!prefetched) issue0(b);
             prefetched = false;
-            if (!params_loaded) load_params();
             if (!p.bc_dma && own_bc) stage_bc(bg, cg, 0, L, p.bc_wide != 0);
-            wait_vmem();
+            // parameters, B/C and x have landed; delta may still be in flight
+            wait_vmem_at_most(delta_only);
             wave_lds_sync();
             if (p.bc_dma && own_bc) widen_bc();
             if (p.pad_in) {
@@ -306,6 +312,8 @@ struct ScanWave {
                 const double acc = lane < nrows ? sum_in_order(xs + lane * XL, XL, 0.0) : 0.0;
                 mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
             }
+            wait_vmem();
+            wave_lds_sync();
         } else if constexpr (MODE == 1) {
             constexpr int ew = 4 / (int)sizeof(IO);
             xrs = p.xrs; drs = p.drs;
