@@ -54,9 +54,15 @@ def _load():
         lib.oracle_selective_scan_folded.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
                                                      _dp, _i64, _i64, _i64, _i64, _i64, ctypes.c_int]
         lib.oracle_round_io.argtypes = [_dp, _dp, _i64, ctypes.c_int]
+        lib.oracle_selective_scan_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
+                                                  _dp, _dp, _i64, _i64, ctypes.c_int, _dp,
+                                                  _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                                  _i64, _i64, _i64, _i64, ctypes.c_int]
+        lib.oracle_aux_pad_bwd.argtypes = [_dp, _dp, _i64, _i64, _i64]
         lib.oracle_threads.argtypes = [ctypes.c_int]
         for f in ("oracle_aux_pad", "oracle_aux_swap", "oracle_dwconv1d", "oracle_selective_scan",
-                  "oracle_selective_scan_folded", "oracle_round_io", "oracle_threads"):
+                  "oracle_selective_scan_folded", "oracle_round_io", "oracle_threads",
+                  "oracle_selective_scan_bwd", "oracle_aux_pad_bwd"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -163,3 +169,62 @@ def layer(x_padded, delta, A, Bm, Cm, Dskip, delta_bias, conv_w, conv_b=None, pa
     if io != "f64":
         u = round_io(u, io)
     return selective_scan(u, delta, A, Bm, Cm, Dskip, delta_bias, softplus=softplus, nthreads=nthreads)
+
+
+def selective_scan_bwd(x, delta, A, Bm, Cm, Dskip, delta_bias, dy, conv_w=None, conv_b=None,
+                       pad_left: int = 1, act: int = 0, softplus: bool = True, nthreads: int = 1) -> dict:
+    """Gradients of the per-sample layer (optional conv, then scan) for upstream dy.
+
+    x is the conv input (or u without conv), [B, D, L].  Returns float64 arrays:
+    dx [B,D,L], ddelta [B,D,L], dA [D,N], dBm, dCm [B,N,L], dDskip [D],
+    ddelta_bias [D], and with conv dconv_w [D,K], dconv_b [D]."""
+    x, delta, A, Bm, Cm, dy = map(_f64, (x, delta, A, Bm, Cm, dy))
+    Dskip = None if Dskip is None else _f64(Dskip)
+    delta_bias = None if delta_bias is None else _f64(delta_bias)
+    B, D, L = x.shape
+    N = A.shape[1]
+    K = 0
+    if conv_w is not None:
+        conv_w = _f64(conv_w)
+        K = conv_w.shape[1]
+        conv_b = None if conv_b is None else _f64(conv_b)
+    out = dict(dx=np.empty_like(x), ddelta=np.empty_like(x), dA=np.empty_like(A), dBm=np.empty_like(Bm),
+               dCm=np.empty_like(Cm), dDskip=np.empty(D), ddelta_bias=np.empty(D))
+    if conv_w is not None:
+        out["dconv_w"] = np.empty_like(conv_w)
+        out["dconv_b"] = np.empty(D)
+    _check(_load().oracle_selective_scan_bwd(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(delta_bias), int(softplus),
+        _ptr(conv_w), _ptr(conv_b), K, pad_left, act, _ptr(dy),
+        _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dBm"]), _ptr(out["dCm"]),
+        _ptr(out["dDskip"]), _ptr(out["ddelta_bias"]), _ptr(out.get("dconv_w")), _ptr(out.get("dconv_b")),
+        B, D, N, L, nthreads), "selective_scan_bwd")
+    return out
+
+
+def aux_pad_bwd(dxp) -> np.ndarray:
+    """Gradient of the aux pad: [B, D, T+2] -> [B, D, T]."""
+    dxp = _f64(dxp)
+    B, D, L = dxp.shape
+    dx = np.empty((B, D, L - 2))
+    _check(_load().oracle_aux_pad_bwd(_ptr(dxp), _ptr(dx), B, D, L - 2), "aux_pad_bwd")
+    return dx
+
+
+def layer_bwd(x, delta, A, Bm, Cm, Dskip, delta_bias, dy, conv_w=None, conv_b=None, pad_left: int = 1,
+              act: int = 0, softplus: bool = True, fuse_pad: bool = False, fuse_swap: bool = False,
+              nthreads: int = 1) -> dict:
+    """Backward of pad (optional) -> conv -> scan -> swap (optional).
+
+    With fuse_pad, x is the unpadded [B, D, L-2] stage input (its padded form
+    is rebuilt exactly as the forward does, mean unrounded) and dx comes back
+    unpadded; with fuse_swap, dy is the gradient of the swapped output."""
+    x, dy = _f64(x), _f64(dy)
+    xp = aux_pad(x, "f64") if fuse_pad else x
+    if fuse_swap:
+        dy = aux_swap(dy)
+    g = selective_scan_bwd(xp, delta, A, Bm, Cm, Dskip, delta_bias, dy, conv_w, conv_b, pad_left, act,
+                           softplus, nthreads)
+    if fuse_pad:
+        g["dx"] = aux_pad_bwd(g["dx"])
+    return g

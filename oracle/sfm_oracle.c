@@ -39,6 +39,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -237,6 +238,194 @@ int oracle_selective_scan_folded(const double* u, const double* delta, const dou
             }
             y[ix] = acc + (Dskip ? Dskip[d] : 0.0) * ut;
         }
+    }
+    return 0;
+}
+
+/* ================================================================ backward
+ * Gradients of the per-sample forward above with respect to all of its inputs,
+ * for an upstream gradient dy = dLoss/dy.  The pages give the forward only (the
+ * method is trained end to end, [SBW] 3.3 / [TL] "第二个模块"); the backward
+ * here is the chain rule applied to exactly that definition, written out in
+ * reverse time for each (sample, channel):
+ *   z_t = cb + sum_j w_j x~_{t+j-P}, u_t = act(z_t)   (u_t = x_t without conv)
+ *   v_t = delta_t + bias, Delta_t = softplus(v_t)     (or v_t)
+ *   h_0 = Delta_0 B_0 u_0 (reset), h_t = a_t h_{t-1} + Delta_t B_t u_t, a_t = exp(Delta_t A)
+ *   y_t = sum_n C_t h_t + D u_t
+ * G_t = dLoss/dh_t collects dy_t C_t and, through h_{t+1} = a_{t+1} h_t + ..,
+ * a_{t+1} G_{t+1}; nothing flows across the reset into the previous sample.
+ * Softplus keeps PyTorch's threshold: its derivative is exactly 1 above 20.
+ * Per-channel gradients (dA, dD, dbias, dw, dcb) are summed over samples and
+ * positions, dB and dC over channels, each in increasing index order.
+ * Layouts as the forward; outputs are overwritten.  Pass conv_w = NULL for no
+ * conv (then dx is du); dconv_w / dconv_b are then not touched.
+ */
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_selective_scan_bwd(const double* x, const double* delta, const double* A,
+                              const double* Bm, const double* Cm, const double* Dskip,
+                              const double* delta_bias, int softplus_on,
+                              const double* conv_w, const double* conv_b, int64_t K, int64_t P, int act,
+                              const double* dy,
+                              double* dx, double* ddelta, double* dA, double* dBm, double* dCm,
+                              double* dDskip, double* ddelta_bias, double* dconv_w, double* dconv_b,
+                              int64_t B, int64_t D, int64_t N, int64_t L, int nthreads) {
+    if (N < 1 || N > 64 || L < 1) return 2;
+    if (conv_w && (K < 1 || P < 0 || P >= K)) return 2;
+    const int64_t KK = conv_w ? K : 0;
+    set_threads(nthreads);
+    /* per-(b, d) partial sums of the per-channel gradients, reduced afterwards in
+     * increasing b so the result does not depend on the thread count */
+    const int64_t pc = N + 2 + KK + (conv_w ? 1 : 0);
+    double* part = (double*)calloc((size_t)(B * D * pc), sizeof(double));
+    /* per-(b, d) contributions to dB, dC: [B, D, N, L] */
+    double* pbc = (double*)calloc((size_t)(2 * B * D * N * L), sizeof(double));
+    int fail = (part == NULL || pbc == NULL);
+    if (!fail) {
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < B * D; ++r) {
+            const int64_t b = r / D, d = r % D;
+            double* z = (double*)malloc((size_t)L * sizeof(double));
+            double* u = (double*)malloc((size_t)L * sizeof(double));
+            double* v = (double*)malloc((size_t)L * sizeof(double));
+            double* dt = (double*)malloc((size_t)L * sizeof(double));
+            double* h = (double*)malloc((size_t)(L * N) * sizeof(double));   /* h[t*N + n] */
+            double* a = (double*)malloc((size_t)(L * N) * sizeof(double));   /* a[t*N + n] */
+            double* du = (double*)malloc((size_t)L * sizeof(double));
+            double* dz = (double*)malloc((size_t)L * sizeof(double));
+            double G[64];
+            const double* xr = x + r * L;
+            /* forward, keeping every intermediate */
+            for (int64_t t = 0; t < L; ++t) {
+                if (conv_w) {
+                    double acc = conv_b ? conv_b[d] : 0.0;
+                    for (int64_t j = 0; j < K; ++j) {
+                        const int64_t s = t + j - P;
+                        acc += conv_w[d * K + j] * ((s >= 0 && s < L) ? xr[s] : 0.0);
+                    }
+                    z[t] = acc;
+                    u[t] = act == 1 ? acc * sigmoid(acc) : acc;
+                } else {
+                    z[t] = xr[t];
+                    u[t] = xr[t];
+                }
+                v[t] = delta[r * L + t] + (delta_bias ? delta_bias[d] : 0.0);
+                dt[t] = softplus_on ? softplus(v[t]) : v[t];
+                for (int64_t n = 0; n < N; ++n) {
+                    const double bx = dt[t] * Bm[(b * N + n) * L + t] * u[t];
+                    if (t == 0) {
+                        a[n] = 0.0;
+                        h[n] = bx;
+                    } else {
+                        a[t * N + n] = exp(dt[t] * A[d * N + n]);
+                        h[t * N + n] = a[t * N + n] * h[(t - 1) * N + n] + bx;
+                    }
+                }
+            }
+            /* reverse time */
+            double* pr = part + r * pc;   /* [dA (N), dD, dbias, dw (KK), dcb] */
+            for (int64_t n = 0; n < N; ++n) G[n] = 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const double g = dy[r * L + t];
+                double ddt = 0.0;
+                du[t] = (Dskip ? Dskip[d] : 0.0) * g;
+                pr[N] += g * u[t];
+                for (int64_t n = 0; n < N; ++n) {
+                    const double Bv = Bm[(b * N + n) * L + t], Cv = Cm[(b * N + n) * L + t];
+                    /* G_t = dy_t C_t + a_{t+1} G_{t+1}  (G holds a_{t+1} G_{t+1} here) */
+                    G[n] = g * Cv + G[n];
+                    pbc[((r * 2 + 1) * N + n) * L + t] = g * h[t * N + n];          /* dC */
+                    pbc[((r * 2 + 0) * N + n) * L + t] = G[n] * dt[t] * u[t];       /* dB */
+                    du[t] += G[n] * dt[t] * Bv;
+                    ddt += G[n] * Bv * u[t];
+                    if (t > 0) {
+                        const double dat = G[n] * h[(t - 1) * N + n];               /* dLoss/da_t */
+                        ddt += dat * a[t * N + n] * A[d * N + n];
+                        pr[n] += dat * a[t * N + n] * dt[t];
+                        G[n] = a[t * N + n] * G[n];                                 /* -> a_t G_t */
+                    } else {
+                        G[n] = 0.0;                                                 /* reset */
+                    }
+                }
+                const double dv = softplus_on ? (v[t] > 20.0 ? ddt : ddt * sigmoid(v[t])) : ddt;
+                ddelta[r * L + t] = dv;
+                pr[N + 1] += dv;
+                if (conv_w) {
+                    double dact = 1.0;
+                    if (act == 1) {
+                        const double s = sigmoid(z[t]);
+                        dact = s + z[t] * s * (1.0 - s);
+                    }
+                    dz[t] = du[t] * dact;
+                } else {
+                    dz[t] = du[t];
+                }
+            }
+            if (conv_w) {
+                for (int64_t s = 0; s < L; ++s) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < K; ++j) {
+                        const int64_t t = s + P - j;
+                        if (t >= 0 && t < L) acc += conv_w[d * K + j] * dz[t];
+                    }
+                    dx[r * L + s] = acc;
+                }
+                for (int64_t j = 0; j < K; ++j) {
+                    double acc = 0.0;
+                    for (int64_t t = 0; t < L; ++t) {
+                        const int64_t s = t + j - P;
+                        if (s >= 0 && s < L) acc += dz[t] * xr[s];
+                    }
+                    pr[N + 2 + j] = acc;
+                }
+                double acc = 0.0;
+                for (int64_t t = 0; t < L; ++t) acc += dz[t];
+                pr[N + 2 + K] = acc;
+            } else {
+                for (int64_t t = 0; t < L; ++t) dx[r * L + t] = dz[t];
+            }
+            free(z); free(u); free(v); free(dt); free(h); free(a); free(du); free(dz);
+        }
+        /* reductions in increasing index order */
+        for (int64_t d = 0; d < D; ++d) {
+            for (int64_t k = 0; k < pc; ++k) {
+                double acc = 0.0;
+                for (int64_t b = 0; b < B; ++b) acc += part[(b * D + d) * pc + k];
+                if (k < N) dA[d * N + k] = acc;
+                else if (k == N) { if (dDskip) dDskip[d] = acc; }
+                else if (k == N + 1) { if (ddelta_bias) ddelta_bias[d] = acc; }
+                else if (k < N + 2 + KK) dconv_w[d * K + (k - N - 2)] = acc;
+                else if (dconv_b) dconv_b[d] = acc;
+            }
+        }
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t t = 0; t < L; ++t) {
+                    double sb = 0.0, sc = 0.0;
+                    for (int64_t d = 0; d < D; ++d) {
+                        const int64_t r = b * D + d;
+                        sb += pbc[((r * 2 + 0) * N + n) * L + t];
+                        sc += pbc[((r * 2 + 1) * N + n) * L + t];
+                    }
+                    dBm[(b * N + n) * L + t] = sb;
+                    dCm[(b * N + n) * L + t] = sc;
+                }
+    }
+    free(part);
+    free(pbc);
+    return fail ? 3 : 0;
+}
+
+/* Backward of the aux pad: the mean feeds both end tokens, so each unpadded
+ * token receives its own padded gradient plus (g_0 + g_{L-1}) / T.  The io
+ * rounding of the mean is passed through as the identity. */
+int oracle_aux_pad_bwd(const double* dxp, double* dx, int64_t B, int64_t D, int64_t T) {
+    if (T < 1) return 2;
+    const int64_t L = T + 2;
+    for (int64_t r = 0; r < B * D; ++r) {
+        const double* g = dxp + r * L;
+        const double ends = (g[0] + g[L - 1]) / (double)T;
+        for (int64_t t = 0; t < T; ++t) dx[r * T + t] = g[1 + t] + ends;
     }
     return 0;
 }
