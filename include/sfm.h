@@ -149,6 +149,54 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
                              void* stream);
 
 /*
+ * sfm_selective_scan_bwd -- gradients of sfm_selective_scan_fwd_ex (same
+ * arguments and flags) for an upstream gradient dy of its output.  The pages
+ * give the forward only ([SBW] 3.3 and [TL] "第二个模块": the model is trained
+ * end to end); this is the chain rule of that forward in reverse time, with the
+ * reset cutting every gradient path between the samples of a folded row and
+ * PyTorch's softplus threshold (derivative 1 above 20).
+ *
+ * Inputs as the forward (u is the conv input; unpadded [B, D, L-2] with
+ * SFM_FUSE_PAD); dy [B1*B2, D, L] io is the gradient of the forward output y
+ * (of the swapped y with SFM_FUSE_SWAP).  Outputs (device, overwritten):
+ *   du          [B1*B2, D, L] io  gradient of the conv input in the PADDED layout
+ *               (positions 0 and L-1 are the aux tokens with SFM_FUSE_PAD; pass
+ *               it to sfm_aux_pad_bwd for the unpadded input's gradient)
+ *   ddelta      [B1*B2, D, L] io
+ *   dA          [D, N] f32;   dBm, dCm [B1*B2, N, L] f32 (summed over channels)
+ *   dDskip, ddelta_bias [D] f32 or NULL (not computed)
+ *   dconv_w     [D, conv_k] f32 (required with conv_w);  dconv_b [D] f32 or NULL
+ * workspace: device memory of at least sfm_selective_scan_bwd_workspace_size()
+ *   bytes, owned by the caller, not overlapping anything else; it holds float32
+ *   state checkpoints (every 8 positions, 4 with N > 8) for the duration of the
+ *   call.  The library allocates nothing.  The f32 sums are accumulated with
+ *   atomics, so their summation order (and last bits) may vary between runs.
+ * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN (nothing launched), HIP.
+ */
+sfm_status sfm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
+                                  const void* Cm, const float* Dskip, const float* delta_bias,
+                                  int delta_softplus, const float* conv_w, const float* conv_b,
+                                  int conv_k, int conv_pad_left, int conv_act, const void* dy,
+                                  void* du, void* ddelta, float* dA, float* dBm, float* dCm,
+                                  float* dDskip, float* ddelta_bias, float* dconv_w, float* dconv_b,
+                                  int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype,
+                                  int flags, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes sfm_selective_scan_bwd needs for these sizes (host only;
+ * conv_k = 0 for no conv).  Returns SFM_OK or SHAPE/DTYPE/UNSUPPORTED. */
+sfm_status sfm_selective_scan_bwd_workspace_size(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
+                                                 int conv_k, int io_dtype, int flags, int64_t* bytes);
+
+/*
+ * sfm_aux_pad_bwd -- gradient of the aux pad ([SBW] 3.2, [TL] "第一个模块"):
+ * both end tokens are the row mean, so gx[b,d,i] = gpad[b,d,1+i] +
+ * (gpad[b,d,0] + gpad[b,d,T+1]) / T.  gpad [B, D, T+2] io in, gx [B, D, T] io
+ * out (must not overlap); float32 arithmetic, one rounding to io.
+ */
+sfm_status sfm_aux_pad_bwd(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,
+                           void* stream);
+
+/*
  * sfm_aux_pad_swap -- the auxiliary head/tail tokens ([SBW] 3.2, [TL]
  * "第一个模块").
  *  mode SFM_AUX_PAD:  in [B, D, T] -> out [B, D, T+2]; out[..,0] = out[..,T+1] =

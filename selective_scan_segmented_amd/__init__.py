@@ -15,8 +15,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_pick_b1", "sfm_scan_plan_string",
-           "sfm_version", "library_path", "load_library", "SFMError"]
+__all__ = ["sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_selective_scan_bwd",
+           "sfm_selective_scan_bwd_workspace_size", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_aux_pad_bwd",
+           "sfm_pick_b1", "sfm_scan_plan_string", "sfm_version", "library_path", "load_library", "SFMError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "libsfm.so")
@@ -50,11 +51,18 @@ def load_library():
     lib.sfm_selective_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
                                               i64, i64, i64, i64, i64, ci, ci, vp]
     lib.sfm_dwconv1d_fold.argtypes = [vp, fp, fp, vp, i64, i64, i64, i64, ci, ci, ci, ci, vp]
+    lib.sfm_selective_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
+                                           vp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                           i64, i64, i64, i64, i64, ci, ci, vp, i64, vp]
+    lib.sfm_selective_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci,
+                                                          ctypes.POINTER(ctypes.c_int64)]
+    lib.sfm_aux_pad_bwd.argtypes = [vp, vp, i64, i64, i64, ci, vp]
     lib.sfm_aux_pad_swap.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
     lib.sfm_pick_b1.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.sfm_scan_plan_string.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci, ctypes.c_char_p, i64]
     for f in ("sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_dwconv1d_fold", "sfm_aux_pad_swap",
-              "sfm_pick_b1", "sfm_version", "sfm_scan_plan_string"):
+              "sfm_pick_b1", "sfm_version", "sfm_scan_plan_string", "sfm_selective_scan_bwd",
+              "sfm_selective_scan_bwd_workspace_size", "sfm_aux_pad_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.sfm_status_string.argtypes = [ctypes.c_int]
     lib.sfm_status_string.restype = ctypes.c_char_p
@@ -164,6 +172,91 @@ def sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, 
         B // B2, B2, D, N, L, io, int(flags), _stream(stream))
     _check(rc, "sfm_selective_scan_fwd")
     return y
+
+
+def sfm_selective_scan_bwd_workspace_size(B1: int, B2: int, D: int, N: int, L: int, conv_k: int = 4,
+                                          io: str = "bf16", flags: int = 0) -> int:
+    """Workspace bytes sfm_selective_scan_bwd needs (host only)."""
+    out = ctypes.c_int64(0)
+    _check(load_library().sfm_selective_scan_bwd_workspace_size(B1, B2, D, N, L, conv_k,
+                                                                SFM_BF16 if io == "bf16" else SFM_F32, flags,
+                                                                ctypes.byref(out)),
+           "sfm_selective_scan_bwd_workspace_size")
+    return int(out.value)
+
+
+def sfm_selective_scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, delta_bias=None, delta_softplus=True,
+                           conv_w=None, conv_b=None, conv_pad_left=1, conv_act=None, B2=1, flags=0,
+                           workspace=None, grads=None, stream=None):
+    """Gradients of sfm_selective_scan_fwd_ex for upstream dy (see include/sfm.h).
+
+    Returns a dict: du (padded layout [B, D, L], io), ddelta (io), dA, dBm, dCm,
+    dDskip, ddelta_bias, dconv_w, dconv_b (float32).  `grads` may hold
+    preallocated tensors under those names; `workspace` a uint8 GPU tensor of at
+    least sfm_selective_scan_bwd_workspace_size() bytes."""
+    torch = _torch()
+    io = _io_code(u)
+    B, D, XL = u.shape
+    L = XL + 2 if flags & SFM_FUSE_PAD else XL
+    N = A.shape[1]
+    if B % B2:
+        raise ValueError(f"B2={B2} must divide B={B}")
+    _dev(u, "u")
+    for t, name, shape in ((delta, "delta", (B, D, L)), (Bm, "Bm", (B, N, L)), (Cm, "Cm", (B, N, L)),
+                           (dy, "dy", (B, D, L))):
+        _dev(t, name, u.dtype, shape)
+    _dev(A, "A", torch.float32, (D, N))
+    _dev(Dskip, "Dskip", torch.float32, (D,))
+    _dev(delta_bias, "delta_bias", torch.float32, (D,))
+    K = 0
+    if conv_w is not None:
+        _dev(conv_w, "conv_w", torch.float32)
+        if conv_w.dim() != 2 or conv_w.shape[0] != D:
+            raise ValueError("conv_w must be [D, K]")
+        K = conv_w.shape[1]
+        _dev(conv_b, "conv_b", torch.float32, (D,))
+    g = dict(grads or {})
+    f32 = dict(dtype=torch.float32, device=u.device)
+    shapes = dict(du=((B, D, L), u.dtype), ddelta=((B, D, L), u.dtype), dA=((D, N), torch.float32),
+                  dBm=((B, N, L), torch.float32), dCm=((B, N, L), torch.float32))
+    if Dskip is not None:
+        shapes["dDskip"] = ((D,), torch.float32)
+    if delta_bias is not None:
+        shapes["ddelta_bias"] = ((D,), torch.float32)
+    if conv_w is not None:
+        shapes["dconv_w"] = ((D, K), torch.float32)
+        if conv_b is not None:
+            shapes["dconv_b"] = ((D,), torch.float32)
+    for k, (shape, dt) in shapes.items():
+        if g.get(k) is None:
+            g[k] = torch.empty(shape, dtype=dt, device=u.device)
+        _dev(g[k], k, dt, shape)
+    need = sfm_selective_scan_bwd_workspace_size(B // B2, B2, D, N, L, K, "bf16" if io == SFM_BF16 else "f32",
+                                                 flags)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=u.device)
+    _dev(workspace, "workspace")
+    rc = load_library().sfm_selective_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(delta_bias), int(bool(delta_softplus)),
+        _ptr(conv_w), _ptr(conv_b), K, int(conv_pad_left), _ACT[conv_act], _ptr(dy),
+        _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]), _ptr(g.get("dDskip")),
+        _ptr(g.get("ddelta_bias")), _ptr(g.get("dconv_w")), _ptr(g.get("dconv_b")),
+        B // B2, B2, D, N, L, io, int(flags), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(rc, "sfm_selective_scan_bwd")
+    return g
+
+
+def sfm_aux_pad_bwd(gpad, gx=None, stream=None):
+    """Gradient of the aux pad: gpad [B, D, T+2] -> gx [B, D, T]."""
+    io = _io_code(gpad)
+    B, D, L = gpad.shape
+    _dev(gpad, "gpad")
+    if gx is None:
+        gx = _torch().empty((B, D, L - 2), dtype=gpad.dtype, device=gpad.device)
+    _dev(gx, "gx", gpad.dtype, (B, D, L - 2))
+    _check(load_library().sfm_aux_pad_bwd(_ptr(gpad), _ptr(gx), B, D, L - 2, io, _stream(stream)), "sfm_aux_pad_bwd")
+    return gx
 
 
 def sfm_dwconv1d_fold(x, w, bias=None, pad_left=1, act=None, out=None, B2=1, stream=None):

@@ -97,6 +97,22 @@ __global__ __launch_bounds__(256) void swap_copy_kernel(const IO* __restrict__ i
     }
 }
 
+// Backward of PAD: the mean feeds both end tokens, so each unpadded token
+// receives its own padded gradient plus (g_0 + g_{L-1}) / T (float32, one
+// rounding to the io type).  One thread per output element.
+template <typename IO>
+__global__ void pad_bwd_kernel(const IO* __restrict__ gp, IO* __restrict__ gx, long long n, int T) {
+    const int L = T + 2;
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n;
+         e += (long long)gridDim.x * blockDim.x) {
+        const long long r = e / T;
+        const int i = (int)(e - r * T);
+        const IO* g = gp + r * L;
+        const float ends = (to_f32(g[0]) + to_f32(g[L - 1])) / (float)T;
+        gx[e] = from_f32<IO>(to_f32(g[1 + i]) + ends);
+    }
+}
+
 unsigned grid_for(long long work, int per_block) {
     long long b = (work + per_block - 1) / per_block;
     if (b > 65536) b = 65536;
@@ -127,7 +143,19 @@ hipError_t swap_t(const void* in, void* out, int64_t rows, int64_t L, hipStream_
     return hipGetLastError();
 }
 
+template <typename IO>
+hipError_t pad_bwd_t(const void* gp, void* gx, int64_t rows, int64_t T, hipStream_t s) {
+    const long long n = rows * T;
+    hipLaunchKernelGGL((pad_bwd_kernel<IO>), dim3(grid_for(n, 256)), dim3(256), 0, s, static_cast<const IO*>(gp),
+                       static_cast<IO*>(gx), n, (int)T);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_aux_pad_bwd(const void* gp, void* gx, int64_t rows, int64_t T, int io_dtype, hipStream_t stream) {
+    return io_dtype == 0 ? pad_bwd_t<float>(gp, gx, rows, T, stream) : pad_bwd_t<__bf16>(gp, gx, rows, T, stream);
+}
 
 hipError_t launch_aux_pad(const void* in, void* out, int64_t rows, int64_t T, int io_dtype, hipStream_t stream) {
     return io_dtype == 0 ? pad_t<float>(in, out, rows, T, stream) : pad_t<__bf16>(in, out, rows, T, stream);

@@ -1,0 +1,455 @@
+// bwd.hip -- backward of the boundary-masked depthwise conv + folded, segmented
+// selective scan, for gfx950 (wave64).
+//
+// The pages give the forward only (the method is trained end to end:
+// "Seeing Both Ways, Running One Way" 3.3; techloop walkthrough "第二个模块").
+// The gradients here are the chain rule of that forward, run in reverse time
+// for each (sample, channel):
+//   G_t   = dy_t C_t + a_{t+1} G_{t+1}           (gradient reaching the state h_t)
+//   dC_t  = dy_t h_t,  dB_t = G_t Delta_t u_t     (summed over channels)
+//   du_t  = D dy_t + sum_n G_t Delta_t B_t
+//   dDelta_t = sum_n G_t B_t u_t + [t > 0] sum_n G_t h_{t-1} a_t A
+//   dA   += [t > 0] G_t h_{t-1} a_t Delta_t,  dD += dy_t u_t
+// then softplus and the conv (with its zero taps outside the sample) backwards.
+// The reset at every sample start is a re-initialisation, so no gradient
+// crosses from a sample into the one before it in the folded row.
+//
+// Work mapping: one wave per (folded row b1, tile of 64 channels); lanes are
+// channels, the B2 samples of the row run one after the other.  Per sample:
+//  * sweep 1 runs the forward recurrence in chunks of Q positions and writes
+//    the state entering every chunk (fp32) to a caller-provided workspace;
+//  * sweep 2 visits the chunks in reverse: it re-runs the chunk forward from
+//    its checkpoint keeping the Q states in registers, then steps backwards.
+// Inputs of a chunk are staged through LDS with coalesced loads.  dB and dC
+// (sums over channels) go through an LDS transpose: each lane writes its terms
+// for R positions, then each lane sums one (position, state) row of 64 and adds
+// it to the output with a float32 atomic (one per channel tile).  Per-channel
+// sums (dA, dD, dbias, dconv) stay in registers over the wave's samples and are
+// added with atomics at the end.  All float32 outputs are zeroed first.
+#include "sfm_device.h"
+#include "sfm_internal.h"
+
+namespace sfm {
+
+namespace {
+
+constexpr int kRedStride = 68;  // floats per row of the transpose buffer (16-byte rows, no 16-lane bank clash)
+
+__device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + exp2_fast(-v * kLog2e)); }
+
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kernel(BwdParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    constexpr int XW = Q + KW - 1;  // x window columns of a chunk
+    constexpr int R = 32 / NS;      // positions per dB/dC transpose round (2*NS*R = 64 rows)
+    static_assert(Q % R == 0, "chunk must hold whole transpose rounds");
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    const int b1 = g / p.tiles;
+    const int tile = g - b1 * p.tiles;
+    const int d0 = tile * kWave;
+    const int nrows = min(kWave, p.D - d0);
+    const int d = d0 + lane;
+    const bool valid = lane < nrows;
+    const int L = p.L, XL = p.xrow, N = p.N;
+    const int P = CONV ? p.P : 0;
+    const int sh = p.pad_in ? 1 : 0;  // padded position q reads u row index q - sh
+
+    IO* xs = reinterpret_cast<IO*>(smem + p.xs_off);     // [64][XW]: column c = position t0 - P + c
+    IO* dls = reinterpret_cast<IO*>(smem + p.ds_off);    // [64][Q]   delta, then ddelta
+    IO* dys = reinterpret_cast<IO*>(smem + p.dys_off);   // [64][Q]   dy
+    float* bs = reinterpret_cast<float*>(smem + p.bc_off);  // [Q][NS]
+    float* cs = bs + Q * NS;                               // [Q][NS]
+    float* red = reinterpret_cast<float*>(smem + p.red_off);  // [64][kRedStride]
+    float* dxs = reinterpret_cast<float*>(smem + p.mean_off);  // [64][XW] fp32 dx of the chunk's window
+
+    // per-channel parameters
+    float A[NS], Dk, db, cw[KW], cb;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) A[n] = (valid && n < N) ? p.A[(size_t)d * N + n] : 0.0f;
+    Dk = (valid && p.Dskip) ? p.Dskip[d] : 0.0f;
+    db = (valid && p.dbias) ? p.dbias[d] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) cw[j] = (CONV && valid && j < p.K) ? p.conv_w[(size_t)d * p.K + j] : 0.0f;
+    cb = (CONV && valid && p.conv_b) ? p.conv_b[d] : 0.0f;
+    float gA[NS], gD = 0.0f, gb = 0.0f, gw[KW], gcb = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) gA[n] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) gw[j] = 0.0f;
+    // states n >= N stay zero in the B/C stage
+    for (int e = lane; e < Q * NS; e += kWave) {
+        bs[e] = 0.0f;
+        cs[e] = 0.0f;
+    }
+    float* ws = p.ws + (size_t)g * p.nchk * NS * kWave;
+
+    for (int j = 0; j < p.B2; ++j) {
+        const int b = b1 * p.B2 + j;
+        const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * p.D + d0) * XL;
+        const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * p.D + d0) * L;
+        const IO* yg = static_cast<const IO*>(p.dy) + ((size_t)b * p.D + d0) * L;
+        const IO* bgl = static_cast<const IO*>(p.Bm) + (size_t)b * N * L;
+        const IO* cgl = static_cast<const IO*>(p.Cm) + (size_t)b * N * L;
+        IO* dug = static_cast<IO*>(p.du) + ((size_t)b * p.D + d0) * L;
+        IO* ddg = static_cast<IO*>(p.ddelta) + ((size_t)b * p.D + d0) * L;
+
+        // --- staging helpers (coalesced: consecutive lanes take consecutive positions of a row)
+        // x window of the chunk at t0: padded positions [t0 - P, t0 - P + XW); zero outside the
+        // sample; the aux-token ends (pad_in) are filled in by xv() from `mean`.
+        auto stage_x = [&](int t0) __attribute__((always_inline)) {
+            for (int e = lane; e < kWave * XW; e += kWave) {
+                const int r = e / XW;
+                const int c = e - r * XW;
+                const int q = t0 - P + c;
+                IO v = Io<IO>::zero();
+                if (r < nrows && q - sh >= 0 && q - sh < XL) v = xg[(size_t)r * XL + q - sh];
+                xs[r * XW + c] = v;
+            }
+        };
+        // delta and dy of positions [t0, t0 + cnt); dy read with the ends exchanged when swap_dy
+        auto stage_d = [&](int t0, int cnt, bool with_dy) __attribute__((always_inline)) {
+            for (int e = lane; e < kWave * Q; e += kWave) {
+                const int r = e / Q;
+                const int c = e - r * Q;
+                const int t = t0 + c;
+                IO v = Io<IO>::zero(), w = Io<IO>::zero();
+                if (r < nrows && c < cnt) {
+                    v = dg[(size_t)r * L + t];
+                    if (with_dy) {
+                        const int ts = (p.swap_dy && L > 1) ? (t == 0 ? L - 1 : (t == L - 1 ? 0 : t)) : t;
+                        w = yg[(size_t)r * L + ts];
+                    }
+                }
+                dls[r * Q + c] = v;
+                if (with_dy) dys[r * Q + c] = w;
+            }
+        };
+        auto stage_bc = [&](int t0, int cnt, bool with_c) __attribute__((always_inline)) {
+            for (int e = lane; e < N * Q; e += kWave) {
+                const int n = e / Q;
+                const int c = e - n * Q;
+                const bool in = c < cnt;
+                bs[c * NS + n] = in ? to_f32(bgl[(size_t)n * L + t0 + c]) : 0.0f;
+                if (with_c) cs[c * NS + n] = in ? to_f32(cgl[(size_t)n * L + t0 + c]) : 0.0f;
+            }
+        };
+
+        // --- fused aux pad: this row's mean, float64 in index order (as the forward)
+        float mean = 0.0f;
+        if (p.pad_in) {
+            double acc = 0.0;
+            for (int c0 = 0; c0 < XL; c0 += XW) {
+                const int cnt = min(XW, XL - c0);
+                wave_lds_sync();
+                for (int e = lane; e < kWave * XW; e += kWave) {
+                    const int r = e / XW;
+                    const int c = e - r * XW;
+                    xs[r * XW + c] = (r < nrows && c < cnt) ? xg[(size_t)r * XL + c0 + c] : Io<IO>::zero();
+                }
+                wave_lds_sync();
+                for (int c = 0; c < cnt; ++c) acc += (double)to_f32(xs[lane * XW + c]);
+            }
+            mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+        }
+        // conv/scan input at padded position q = t0 - P + c (column c of the staged window)
+        auto xv = [&](int t0, int c) __attribute__((always_inline)) {
+            const int q = t0 - P + c;
+            float v = to_f32(xs[lane * XW + c]);
+            if (p.pad_in && (q == 0 || q == L - 1)) v = mean;
+            return v;
+        };
+        // z (pre-activation), u, v (pre-softplus) and Delta*log2e at position t0 + i
+        auto pre = [&](int t0, int i, float& z, float& u, float& v, float& dt) __attribute__((always_inline)) {
+            if constexpr (CONV) {
+                float acc = cb;
+#pragma unroll
+                for (int jj = 0; jj < KW; ++jj) acc = __builtin_fmaf(cw[jj], xv(t0, i + jj), acc);
+                z = acc;
+                u = SILU ? silu(acc) : acc;
+            } else {
+                z = xv(t0, i + P);
+                u = z;
+            }
+            v = to_f32(dls[lane * Q + i]) + db;
+            dt = SP ? softplus_log2e(v) * kLn2 : v;
+        };
+
+        // --- sweep 1: forward, checkpoint the state entering each chunk
+        float h[NS];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+        for (int c = 0; c < p.nchk; ++c) {
+            const int t0 = c * Q;
+            const int cnt = min(Q, L - t0);
+            if (c > 0) {
+#pragma unroll
+                for (int n = 0; n < NS; ++n) ws[((size_t)c * NS + n) * kWave + lane] = h[n];
+            }
+            wave_lds_sync();
+            stage_x(t0);
+            stage_d(t0, cnt, false);
+            stage_bc(t0, cnt, false);
+            wave_lds_sync();
+            for (int i = 0; i < cnt; ++i) {
+                float z, u, v, dt;
+                pre(t0, i, z, u, v, dt);
+                const float du_ = dt * u;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const float bx = du_ * bs[i * NS + n];
+                    h[n] = (t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dt * kLog2e * A[n]), h[n], bx);
+                }
+            }
+        }
+
+        // --- sweep 2: chunks in reverse
+        float G[NS];  // a_{t+1} G_{t+1} carried to position t
+#pragma unroll
+        for (int n = 0; n < NS; ++n) G[n] = 0.0f;
+        float wdx[KW];  // dx of padded positions t - P + jj, still collecting contributions
+#pragma unroll
+        for (int jj = 0; jj < KW; ++jj) wdx[jj] = 0.0f;
+        for (int c = p.nchk - 1; c >= 0; --c) {
+            const int t0 = c * Q;
+            const int cnt = min(Q, L - t0);
+            wave_lds_sync();
+            stage_x(t0);
+            stage_d(t0, cnt, true);
+            stage_bc(t0, cnt, true);
+            for (int e = lane; e < kWave * XW; e += kWave) dxs[e] = 0.0f;
+            float hin[NS];
+#pragma unroll
+            for (int n = 0; n < NS; ++n) hin[n] = c > 0 ? ws[((size_t)c * NS + n) * kWave + lane] : 0.0f;
+            wave_lds_sync();
+            // re-run the chunk forward, keeping every state
+            float hs[Q][NS];
+            float zs[Q], us[Q], vs[Q], dts[Q];
+#pragma unroll
+            for (int i = 0; i < Q; ++i) {
+                if (i < cnt) {
+                    pre(t0, i, zs[i], us[i], vs[i], dts[i]);
+                    const float du_ = dts[i] * us[i];
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        const float hp = i > 0 ? hs[i - 1][n] : hin[n];
+                        const float bx = du_ * bs[i * NS + n];
+                        hs[i][n] = (t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dts[i] * kLog2e * A[n]), hp, bx);
+                    }
+                }
+            }
+            // backwards through the chunk, R positions per dB/dC transpose round
+#pragma unroll
+            for (int r0 = Q - R; r0 >= 0; r0 -= R) {
+#pragma unroll
+                for (int ii = R - 1; ii >= 0; --ii) {
+                    const int i = r0 + ii;
+                    float dBv[NS], dCv[NS];
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) dBv[n] = dCv[n] = 0.0f;
+                    if (i < cnt) {
+                        const int t = t0 + i;
+                        const float gy = to_f32(dys[lane * Q + i]);
+                        const float u = us[i], dt = dts[i];
+                        float du_ = Dk * gy;
+                        float ddt = 0.0f;
+                        gD = __builtin_fmaf(gy, u, gD);
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            const float Bv = bs[i * NS + n], Cv = cs[i * NS + n];
+                            const float Gn = __builtin_fmaf(gy, Cv, G[n]);
+                            dCv[n] = gy * hs[i][n];
+                            dBv[n] = Gn * dt * u;
+                            du_ = __builtin_fmaf(Gn * dt, Bv, du_);
+                            ddt = __builtin_fmaf(Gn * Bv, u, ddt);
+                            if (t > 0) {
+                                const float hp = i > 0 ? hs[i - 1][n] : hin[n];
+                                const float a = exp2_fast(dt * kLog2e * A[n]);
+                                const float dat = Gn * hp * a;  // dLoss/da_t times a_t
+                                ddt = __builtin_fmaf(dat, A[n], ddt);
+                                gA[n] = __builtin_fmaf(dat, dt, gA[n]);
+                                G[n] = a * Gn;
+                            } else {
+                                G[n] = 0.0f;  // reset: nothing reaches the previous sample
+                            }
+                        }
+                        float dv = ddt;
+                        if constexpr (SP) dv = vs[i] > 20.0f ? ddt : ddt * sigmoid_f(vs[i]);
+                        dls[lane * Q + i] = from_f32<IO>(dv);
+                        gb += dv;
+                        float dz = du_;
+                        if constexpr (CONV && SILU) {
+                            const float s = sigmoid_f(zs[i]);
+                            dz = du_ * (s + zs[i] * s * (1.0f - s));
+                        }
+                        if constexpr (CONV) {
+                            gcb += dz;
+#pragma unroll
+                            for (int jj = 0; jj < KW; ++jj) {
+                                gw[jj] = __builtin_fmaf(dz, xv(t0, i + jj), gw[jj]);
+                                wdx[jj] = __builtin_fmaf(dz, cw[jj], wdx[jj]);
+                            }
+                            // padded position t + lag is complete: it gets no later contribution
+                            dxs[lane * XW + i + KW - 1] = wdx[KW - 1];
+#pragma unroll
+                            for (int jj = KW - 1; jj > 0; --jj) wdx[jj] = wdx[jj - 1];
+                            wdx[0] = 0.0f;
+                        } else {
+                            dxs[lane * XW + i + P] = dz;
+                        }
+                    }
+                    // transpose buffer: row (ii, k), column lane
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        red[(ii * 2 * NS + n) * kRedStride + lane] = dBv[n];
+                        red[(ii * 2 * NS + NS + n) * kRedStride + lane] = dCv[n];
+                    }
+                }
+                wave_lds_sync();
+                {
+                    // lane l sums row l: position r0 + l / (2NS), state l % NS, B or C
+                    const int ii = lane / (2 * NS);
+                    const int k = lane - ii * 2 * NS;
+                    const int n = k % NS;
+                    const int t = t0 + r0 + ii;
+                    const float4* row = reinterpret_cast<const float4*>(red + lane * kRedStride);
+                    float s = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < kWave / 4; ++m) {
+                        const float4 v4 = row[m];
+                        s += (v4.x + v4.y) + (v4.z + v4.w);
+                    }
+                    if (n < N && r0 + ii < cnt) atomicAdd((k < NS ? p.dBm : p.dCm) + ((size_t)b * N + n) * L + t, s);
+                }
+                wave_lds_sync();
+            }
+            if constexpr (CONV) {
+                // positions t0 - P .. t0 + lag - 1 are complete once the sample start is passed
+                if (c == 0) {
+                    // after the last shift wdx[m] holds padded position m - 1 - P,
+                    // i.e. window column m - 1
+#pragma unroll
+                    for (int jj = 0; jj < KW - 1; ++jj) dxs[lane * XW + jj] = wdx[jj + 1];
+                }
+            }
+            wave_lds_sync();
+            // write this chunk's ddelta and the completed dx positions (coalesced)
+            for (int e = lane; e < kWave * Q; e += kWave) {
+                const int r = e / Q;
+                const int cc = e - r * Q;
+                if (r < nrows && cc < cnt) ddg[(size_t)r * L + t0 + cc] = dls[r * Q + cc];
+            }
+            // dx columns finished in this chunk: padded positions [lo, hi)
+            const int lag = CONV ? KW - 1 - P : 0;
+            const int lo = CONV ? (c == 0 ? 0 : t0 + lag) : t0;
+            const int hi = CONV ? min(L, t0 + cnt + lag) : t0 + cnt;
+            for (int e = lane; e < kWave * XW; e += kWave) {
+                const int r = e / XW;
+                const int cc = e - r * XW;
+                const int q = t0 - P + cc;
+                if (r < nrows && q >= lo && q < hi) dug[(size_t)r * L + q] = from_f32<IO>(dxs[r * XW + cc]);
+            }
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+            if (n < N) atomicAdd(p.dA + (size_t)d * N + n, gA[n]);
+        if (p.dDskip) atomicAdd(p.dDskip + d, gD);
+        if (p.ddbias) atomicAdd(p.ddbias + d, gb);
+        if constexpr (CONV) {
+#pragma unroll
+            for (int jj = 0; jj < KW; ++jj)
+                if (jj < p.K && p.dconv_w) atomicAdd(p.dconv_w + (size_t)d * p.K + jj, gw[jj]);
+            if (p.dconv_b) atomicAdd(p.dconv_b + d, gcb);
+        }
+    }
+}
+
+__global__ void zero_kernel(float* a, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        a[i] = 0.0f;
+}
+
+hipError_t zero_f32(float* a, size_t n, hipStream_t s) {
+    if (!a || n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<size_t>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, a, n);
+    return hipGetLastError();
+}
+
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
+hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
+    constexpr int Q = NS == 16 ? 4 : 8;
+    hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)), dim3(kWave),
+                       (size_t)p.lds_bytes, s, p);
+    return hipGetLastError();
+}
+
+template <typename IO, int NS, int KW, bool CONV>
+hipError_t launch_bsp(const BwdParams& p, hipStream_t s) {
+    const bool silu = CONV && p.act == 1;
+    if (p.softplus)
+        return silu ? launch_bt<IO, NS, KW, CONV, true, CONV>(p, s) : launch_bt<IO, NS, KW, CONV, true, false>(p, s);
+    return silu ? launch_bt<IO, NS, KW, CONV, false, CONV>(p, s) : launch_bt<IO, NS, KW, CONV, false, false>(p, s);
+}
+
+template <typename IO, int NS>
+hipError_t launch_bns(const BwdParams& p, hipStream_t s) {
+    if (!p.conv_w) return launch_bsp<IO, NS, 4, false>(p, s);
+    if (p.K <= 4) return launch_bsp<IO, NS, 4, true>(p, s);
+    return launch_bsp<IO, NS, 8, true>(p, s);
+}
+
+template <typename IO>
+hipError_t launch_bio(const BwdParams& p, hipStream_t s) {
+    if (p.ns == 4) return launch_bns<IO, 4>(p, s);
+    if (p.ns == 8) return launch_bns<IO, 8>(p, s);
+    return launch_bns<IO, 16>(p, s);
+}
+
+}  // namespace
+
+bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
+    p.ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
+    p.tiles = (p.D + kWave - 1) / kWave;
+    p.q = p.ns == 16 ? 4 : 8;
+    p.nchk = (p.L + p.q - 1) / p.q;
+    const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 4;
+    const int xw = p.q + kw - 1;
+    auto up16 = [](int v) { return (v + 15) & ~15; };
+    int off = 0;
+    p.xs_off = off;
+    off += up16(kWave * xw * io_bytes);
+    p.ds_off = off;
+    off += up16(kWave * p.q * io_bytes);
+    p.dys_off = off;
+    off += up16(kWave * p.q * io_bytes);
+    p.bc_off = off;
+    off += up16(2 * p.q * p.ns * 4);
+    p.red_off = off;
+    off += kWave * kRedStride * 4;
+    p.mean_off = off;  // fp32 dx window
+    off += up16(kWave * xw * 4);
+    p.lds_bytes = off;
+    *ws_bytes = (size_t)p.B1 * p.tiles * p.nchk * p.ns * kWave * sizeof(float);
+    return p.lds_bytes <= 64 * 1024;
+}
+
+hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t s) {
+    const size_t B = (size_t)p.B1 * p.B2;
+    hipError_t e;
+    if ((e = zero_f32(p.dA, (size_t)p.D * p.N, s)) != hipSuccess) return e;
+    if ((e = zero_f32(p.dBm, B * p.N * p.L, s)) != hipSuccess) return e;
+    if ((e = zero_f32(p.dCm, B * p.N * p.L, s)) != hipSuccess) return e;
+    if ((e = zero_f32(p.dDskip, p.D, s)) != hipSuccess) return e;
+    if ((e = zero_f32(p.ddbias, p.D, s)) != hipSuccess) return e;
+    if (p.conv_w) {
+        if ((e = zero_f32(p.dconv_w, (size_t)p.D * p.K, s)) != hipSuccess) return e;
+        if ((e = zero_f32(p.dconv_b, p.D, s)) != hipSuccess) return e;
+    }
+    if (io_dtype == 0) return launch_bio<float>(p, s);
+    return launch_bio<__bf16>(p, s);
+}
+
+}  // namespace sfm

@@ -314,3 +314,141 @@ extern "C" sfm_status sfm_pick_b1(int64_t B, int64_t L, int64_t D, int64_t N, in
     *B1_out = B / b2;
     return ok();
 }
+
+// ---------------------------------------------------------------- backward
+namespace {
+
+sfm_status bwd_common(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                      const void* dy, const float* conv_w, int conv_k, int conv_pad_left, int conv_act,
+                      int delta_softplus, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype,
+                      int flags, const char* who) {
+    if (!u || !delta || !A || !Bm || !Cm || !dy) return fail(SFM_ERR_NULL, "%s: u, delta, A, Bm, Cm, dy are required", who);
+    if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP)) return fail(SFM_ERR_SHAPE, "%s: unknown flags 0x%x", who, flags);
+    if ((flags & SFM_FUSE_PAD) && L < 3) return fail(SFM_ERR_SHAPE, "%s: SFM_FUSE_PAD needs L >= 3", who);
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "%s: io_dtype %d", who, io_dtype);
+    if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24))
+        return fail(SFM_ERR_SHAPE, "%s: B1=%lld B2=%lld D=%lld L=%lld out of range", who, (long long)B1,
+                    (long long)B2, (long long)D, (long long)L);
+    if (N < 1 || N > SFM_MAX_N) return fail(SFM_ERR_SHAPE, "%s: N=%lld not in [1, %d]", who, (long long)N, SFM_MAX_N);
+    if (B1 * B2 * D * L > (1LL << 40)) return fail(SFM_ERR_SHAPE, "%s: tensor too large", who);
+    if (delta_softplus != 0 && delta_softplus != 1) return fail(SFM_ERR_SHAPE, "%s: delta_softplus must be 0 or 1", who);
+    if (conv_w) {
+        if (conv_k < 1 || conv_k > SFM_MAX_K) return fail(SFM_ERR_SHAPE, "%s: conv_k=%d not in [1, %d]", who, conv_k, SFM_MAX_K);
+        if (conv_pad_left < 0 || conv_pad_left >= conv_k)
+            return fail(SFM_ERR_SHAPE, "%s: conv_pad_left=%d not in [0, %d)", who, conv_pad_left, conv_k);
+        if (conv_act != SFM_ACT_NONE && conv_act != SFM_ACT_SILU) return fail(SFM_ERR_SHAPE, "%s: conv_act=%d", who, conv_act);
+    }
+    return ok();
+}
+
+void fill_bwd(sfm::BwdParams& p, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, const float* conv_w,
+              int conv_k, int conv_pad_left, int conv_act, int delta_softplus, int flags) {
+    p.B1 = (int)B1;
+    p.B2 = (int)B2;
+    p.D = (int)D;
+    p.N = (int)N;
+    p.L = (int)L;
+    p.conv_w = conv_w;
+    p.K = conv_w ? conv_k : 1;
+    p.P = conv_w ? conv_pad_left : 0;
+    p.act = conv_w ? conv_act : 0;
+    p.softplus = delta_softplus;
+    p.pad_in = (flags & SFM_FUSE_PAD) ? 1 : 0;
+    p.swap_dy = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+    p.xrow = p.pad_in ? (int)L - 2 : (int)L;
+}
+
+}  // namespace
+
+extern "C" sfm_status sfm_selective_scan_bwd_workspace_size(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
+                                                             int conv_k, int io_dtype, int flags, int64_t* bytes) {
+    if (!bytes) return fail(SFM_ERR_NULL, "sfm_selective_scan_bwd_workspace_size: bytes is required");
+    static const float dummy = 0.0f;
+    static const char dummy_io[16] = {0};
+    sfm_status st = bwd_common(dummy_io, dummy_io, &dummy, dummy_io, dummy_io, dummy_io, conv_k ? &dummy : nullptr,
+                               conv_k ? conv_k : 1, 0, 0, 1, B1, B2, D, N, L, io_dtype, flags,
+                               "sfm_selective_scan_bwd_workspace_size");
+    if (st != SFM_OK) return st;
+    sfm::BwdParams p{};
+    fill_bwd(p, B1, B2, D, N, L, conv_k ? &dummy : nullptr, conv_k ? conv_k : 1, 0, 0, 1, flags);
+    size_t ws = 0;
+    if (!sfm::plan_bwd(p, io_bytes(io_dtype), &ws))
+        return fail(SFM_ERR_UNSUPPORTED, "sfm_selective_scan_bwd_workspace_size: no plan fits LDS");
+    *bytes = (int64_t)ws;
+    return ok();
+}
+
+extern "C" sfm_status sfm_selective_scan_bwd(
+    const void* u, const void* delta, const float* A, const void* Bm, const void* Cm, const float* Dskip,
+    const float* delta_bias, int delta_softplus, const float* conv_w, const float* conv_b, int conv_k,
+    int conv_pad_left, int conv_act, const void* dy, void* du, void* ddelta, float* dA, float* dBm, float* dCm,
+    float* dDskip, float* ddelta_bias, float* dconv_w, float* dconv_b, int64_t B1, int64_t B2, int64_t D, int64_t N,
+    int64_t L, int io_dtype, int flags, void* workspace, int64_t workspace_bytes, void* stream) {
+    const char* who = "sfm_selective_scan_bwd";
+    sfm_status st = bwd_common(u, delta, A, Bm, Cm, dy, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, B1,
+                               B2, D, N, L, io_dtype, flags, who);
+    if (st != SFM_OK) return st;
+    if (!du || !ddelta || !dA || !dBm || !dCm) return fail(SFM_ERR_NULL, "%s: du, ddelta, dA, dBm, dCm are required", who);
+    if (conv_w && !dconv_w) return fail(SFM_ERR_NULL, "%s: dconv_w is required with conv_w", who);
+    if (!aligned16(u) || !aligned16(delta) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(dy) || !aligned16(du) ||
+        !aligned16(ddelta))
+        return fail(SFM_ERR_ALIGN, "%s: io base pointers must be 16-byte aligned", who);
+    const int64_t B = B1 * B2;
+    const int eb = io_bytes(io_dtype);
+    const int64_t XL = (flags & SFM_FUSE_PAD) ? L - 2 : L;
+    const Range ins[] = {rng("u", u, B * D * XL * eb), rng("delta", delta, B * D * L * eb),
+                         rng("Bm", Bm, B * N * L * eb), rng("Cm", Cm, B * N * L * eb), rng("dy", dy, B * D * L * eb)};
+    const Range outs[] = {rng("du", du, B * D * L * eb), rng("ddelta", ddelta, B * D * L * eb),
+                          rng("dA", dA, D * N * 4), rng("dBm", dBm, B * N * L * 4), rng("dCm", dCm, B * N * L * 4),
+                          rng("workspace", workspace, workspace_bytes)};
+    for (const Range& o : outs)
+        for (const Range& i : ins)
+            if (o.lo && overlap(o, i)) return fail(SFM_ERR_ALIAS, "%s: %s overlaps %s", who, o.name, i.name);
+    for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a)
+        for (size_t c = a + 1; c < sizeof(outs) / sizeof(outs[0]); ++c)
+            if (outs[a].lo && outs[c].lo && overlap(outs[a], outs[c]))
+                return fail(SFM_ERR_ALIAS, "%s: %s overlaps %s", who, outs[a].name, outs[c].name);
+    sfm::BwdParams p{};
+    fill_bwd(p, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, flags);
+    size_t need = 0;
+    if (!sfm::plan_bwd(p, eb, &need)) return fail(SFM_ERR_UNSUPPORTED, "%s: no plan fits LDS", who);
+    if (!workspace || workspace_bytes < (int64_t)need)
+        return fail(SFM_ERR_SHAPE, "%s: workspace of %lld bytes needed (see sfm_selective_scan_bwd_workspace_size)",
+                    who, (long long)need);
+    p.u = u;
+    p.delta = delta;
+    p.A = A;
+    p.Bm = Bm;
+    p.Cm = Cm;
+    p.Dskip = Dskip;
+    p.dbias = delta_bias;
+    p.conv_b = conv_b;
+    p.dy = dy;
+    p.du = du;
+    p.ddelta = ddelta;
+    p.dA = dA;
+    p.dBm = dBm;
+    p.dCm = dCm;
+    p.dDskip = dDskip;
+    p.ddbias = ddelta_bias;
+    p.dconv_w = dconv_w;
+    p.dconv_b = dconv_b;
+    p.ws = static_cast<float*>(workspace);
+    return hip_status(sfm::launch_bwd(p, io_dtype, static_cast<hipStream_t>(stream)), who);
+}
+
+extern "C" sfm_status sfm_aux_pad_bwd(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,
+                                      void* stream) {
+    if (!gpad || !gx) return fail(SFM_ERR_NULL, "sfm_aux_pad_bwd: gpad and gx are required");
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "sfm_aux_pad_bwd: io_dtype %d", io_dtype);
+    if (!sane(B, 1 << 24) || !sane(D, 1 << 20) || !sane(T, 1 << 24))
+        return fail(SFM_ERR_SHAPE, "sfm_aux_pad_bwd: B=%lld D=%lld T=%lld out of range", (long long)B, (long long)D,
+                    (long long)T);
+    if (B * D * (T + 2) > (1LL << 40)) return fail(SFM_ERR_SHAPE, "sfm_aux_pad_bwd: tensor too large");
+    if (!aligned16(gpad) || !aligned16(gx)) return fail(SFM_ERR_ALIGN, "sfm_aux_pad_bwd: io base pointers must be 16-byte aligned");
+    const int eb = io_bytes(io_dtype);
+    if (overlap(rng("gx", gx, B * D * T * eb), rng("gpad", gpad, B * D * (T + 2) * eb)))
+        return fail(SFM_ERR_ALIAS, "sfm_aux_pad_bwd: gx overlaps gpad");
+    return hip_status(sfm::launch_aux_pad_bwd(gpad, gx, B * D, T, io_dtype, static_cast<hipStream_t>(stream)),
+                      "sfm_aux_pad_bwd");
+}

@@ -45,6 +45,42 @@ struct ScanParams {
     int stagger_period, stagger_ticks;
 };
 
+// Launch description of one backward call (see bwd.hip).
+struct BwdParams {
+    const void* u;        // conv input x (unpadded with pad_in), or the scan input without conv
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const float* dbias;
+    const float* conv_w;
+    const float* conv_b;
+    const void* dy;
+    void* du;             // gradient of the (padded) conv input, [B, D, L] io
+    void* ddelta;         // [B, D, L] io
+    float* dA;            // [D, N]
+    float* dBm;           // [B, N, L]
+    float* dCm;           // [B, N, L]
+    float* dDskip;        // [D] or null
+    float* ddbias;        // [D] or null
+    float* dconv_w;       // [D, K] or null
+    float* dconv_b;       // [D] or null
+    float* ws;            // checkpoints: [B1 * tiles][nchk][ns][64] float32
+    int B1, B2, D, N, L;
+    int K, P, act, softplus;
+    int pad_in;           // u holds unpadded rows of L-2 tokens
+    int swap_dy;          // dy is the gradient of the output with positions 0 and L-1 exchanged
+    int xrow;             // row length of u
+    // plan
+    int ns, tiles, q, nchk;
+    int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, lds_bytes;
+};
+
+// Backward planning; returns false when no plan fits.  ws_bytes: workspace size.
+bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes);
+hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t stream);
+
 // Fills the plan fields; waves_hint / ch_hint <= 0 select automatically,
 // stagger_hint < 0 selects automatically, 0 turns the staggered start off and
 // > 0 sets the delay per dispatch round in 10 ns ticks.
@@ -63,5 +99,6 @@ hipError_t launch_dwconv1d(const void* x, const float* w, const float* bias, voi
 
 hipError_t launch_aux_pad(const void* in, void* out, int64_t rows, int64_t T, int io_dtype, hipStream_t stream);
 hipError_t launch_aux_swap(const void* in, void* out, int64_t rows, int64_t L, int io_dtype, hipStream_t stream);
+hipError_t launch_aux_pad_bwd(const void* gp, void* gx, int64_t rows, int64_t T, int io_dtype, hipStream_t stream);
 
 }  // namespace sfm
