@@ -149,6 +149,83 @@ def cpu_baseline(w, li, seconds: float):
                       f"chain pad->conv->scan->swap, {el:.1f} s wall on {threads} threads"}
 
 
+def alg_bwd_slots(w) -> int:
+    """Algorithmic VALU work of the backward of the fused conv+scan, in fp32 issue
+    slots: one forward (alg_scan_slots) plus the reverse step -- per state the
+    gradient carry, dC, dB, du, dDelta and dA terms (10 fp32 ops) and the decay
+    exp (4 slots) -- and per position the softplus and conv derivatives (~20)."""
+    return alg_scan_slots(w) + w.B * w.D * w.L * (w.N * (10 + 4) + 20)
+
+
+def alg_bwd_bytes(w, io_bytes: int) -> int:
+    """Algorithmic HBM bytes of the backward: x (T tokens), delta, dy read and
+    du (L), ddelta written in io; B and C read once per sample; dB and dC
+    (float32) written once per sample; per-channel parameters and gradients."""
+    return (w.B * w.D * (w.T + 4 * w.L) * io_bytes + 2 * w.B * w.N * w.L * io_bytes
+            + 2 * w.B * w.N * w.L * 4 + 2 * w.D * (w.N + 3 + w.K) * 4)
+
+
+def run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io):
+    import numpy as np
+    import torch
+    import selective_scan_segmented_amd as sfm
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    rng = np.random.default_rng(7)
+    dy32 = rng.standard_normal((w.B, w.D, w.L)).astype(np.float32)
+    from selective_scan_segmented_amd import synth
+    dy = dev_io(synth.f32_to_bf16_bits(dy32) if w.io == "bf16" else dy32)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dA=torch.empty((w.D, w.N), **f32), dBm=torch.empty((w.B, w.N, w.L), **f32),
+             dCm=torch.empty((w.B, w.N, w.L), **f32), dDskip=torch.empty(w.D, **f32),
+             ddelta_bias=torch.empty(w.D, **f32), dconv_w=torch.empty((w.D, w.K), **f32))
+    flags = 3
+    need = sfm.sfm_selective_scan_bwd_workspace_size(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, flags)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    calls = []
+    for s in sets:
+        # du / ddelta reuse the set's padded-x and y buffers ([B, D, L] io)
+        calls.append((vp(s["x"]), vp(s["delta"]), vp(prm["A"]), vp(s["Bm"]), vp(s["Cm"]), vp(prm["Dskip"]),
+                      vp(prm["delta_bias"]), 1, vp(prm["conv_w"]), None, w.K, 1, 0, vp(dy),
+                      vp(s["xp"]), vp(s["y"]), vp(g["dA"]), vp(g["dBm"]), vp(g["dCm"]), vp(g["dDskip"]),
+                      vp(g["ddelta_bias"]), vp(g["dconv_w"]), None, w.B // b2, b2, w.D, w.N, w.L, io, flags,
+                      vp(ws), need, sp))
+    fn = lib.sfm_selective_scan_bwd
+
+    def step(i):
+        rc = fn(*calls[i % len(calls)])
+        if rc:
+            raise RuntimeError(f"bwd failed: {lib.sfm_last_error().decode()}")
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = a.steps
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, sp)
+    for i in range(K):
+        step(a.warmup + i)
+    hip.record(t1, sp)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(t0, t1) / K
+    tc = w.B * w.D * w.L
+    slots = alg_bwd_slots(w)
+    nbytes = alg_bwd_bytes(w, io_bytes)
+    alu = slots / (ms * 1e-3) / 1e12
+    hbm = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "backward of the fused folded selective scan, token*channels/s (T+2 aux tokens counted)",
+        "value": tc / (ms * 1e-3), "unit": "token*channels/s", "n_gpus": 1, "steps": K, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "dtype": w.io, "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}", "B2": b2,
+                   "mode": "bwd", "input_sets": len(sets), "workspace_bytes": need,
+                   "step": "zero the float32 sums + one backward launch (pad and swap fused)"},
+        "roofline": {"bound": "alu" if alu / VALU_PEAK_TSLOT >= hbm / HBM_PEAK_GBPS else "hbm",
+                     "alu_achieved": round(alu, 3), "alu_peak": round(VALU_PEAK_TSLOT, 3),
+                     "alu_frac": round(alu / VALU_PEAK_TSLOT, 4), "hbm_GBps": round(hbm, 1),
+                     "hbm_frac": round(hbm / HBM_PEAK_GBPS, 4), "alg_valu_slots": slots, "alg_bytes": nbytes},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,8 +236,9 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets; 0 = enough for 2 GiB")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy", "scan"], default="step",
+    ap.add_argument("--mode", choices=["step", "copy", "scan", "bwd"], default="step",
                     help="step: the whole hot path (default); scan: the scan launch alone; "
+                         "bwd: the backward of the fused step (one sfm_selective_scan_bwd call); "
                          "copy: a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (pad, conv+scan, swap) instead of one")
@@ -231,6 +309,9 @@ def main():
     lib = sfm.load_library()
     io = 0 if w.io == "f32" else 1
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    if a.mode == "bwd":
+        run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io)
+        return
     # fused (default): one launch does pad + conv + scan + swap from the unpadded x
     fused = a.mode == "step" and not a.unfused
     calls = []

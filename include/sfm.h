@@ -168,8 +168,8 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  *   dconv_w     [D, conv_k] f32 (required with conv_w);  dconv_b [D] f32 or NULL
  * workspace: device memory of at least sfm_selective_scan_bwd_workspace_size()
  *   bytes, owned by the caller, not overlapping anything else; it holds float32
- *   state checkpoints (every 8 positions, 4 with N > 8) for the duration of the
- *   call.  The library allocates nothing.  The f32 sums are accumulated with
+ *   state checkpoints (every 32/Np positions, Np = N rounded up to 4, 8 or 16)
+ *   for the duration of the call.  The library allocates nothing.  The f32 sums are accumulated with
  *   atomics, so their summation order (and last bits) may vary between runs.
  * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN (nothing launched), HIP.
  */

@@ -16,7 +16,7 @@
 //
 // Work mapping: one wave per (folded row b1, tile of 64 channels); lanes are
 // channels, the B2 samples of the row run one after the other.  Per sample:
-//  * sweep 1 runs the forward recurrence in chunks of Q positions and writes
+//  * sweep 1 runs the forward recurrence in chunks of Q = 32/N positions and writes
 //    the state entering every chunk (fp32) to a caller-provided workspace;
 //  * sweep 2 visits the chunks in reverse: it re-runs the chunk forward from
 //    its checkpoint keeping the Q states in registers, then steps backwards.
@@ -26,6 +26,8 @@
 // it to the output with a float32 atomic (one per channel tile).  Per-channel
 // sums (dA, dD, dbias, dconv) stay in registers over the wave's samples and are
 // added with atomics at the end.  All float32 outputs are zeroed first.
+#include <type_traits>
+
 #include "sfm_device.h"
 #include "sfm_internal.h"
 
@@ -55,13 +57,15 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     const int P = CONV ? p.P : 0;
     const int sh = p.pad_in ? 1 : 0;  // padded position q reads u row index q - sh
 
-    IO* xs = reinterpret_cast<IO*>(smem + p.xs_off);     // [64][XW]: column c = position t0 - P + c
-    IO* dls = reinterpret_cast<IO*>(smem + p.ds_off);    // [64][Q]   delta, then ddelta
-    IO* dys = reinterpret_cast<IO*>(smem + p.dys_off);   // [64][Q]   dy
+    // staged io elements sit in 4-byte slots (raw bits in the low bytes; see dma_at)
+    uint32_t* xs = reinterpret_cast<uint32_t*>(smem + p.xs_off);    // [64][XW]: column c = position t0 - P + c
+    uint32_t* dls = reinterpret_cast<uint32_t*>(smem + p.ds_off);   // [64][Q]   delta, then ddelta as float32
+    uint32_t* dys = reinterpret_cast<uint32_t*>(smem + p.dys_off);  // [64][Q]   dy
     float* bs = reinterpret_cast<float*>(smem + p.bc_off);  // [Q][NS]
     float* cs = bs + Q * NS;                               // [Q][NS]
     float* red = reinterpret_cast<float*>(smem + p.red_off);  // [64][kRedStride]
     float* dxs = reinterpret_cast<float*>(smem + p.mean_off);  // [64][XW] fp32 dx of the chunk's window
+    uint32_t* braw = reinterpret_cast<uint32_t*>(smem + p.braw_off);  // [64] raw B then C of the chunk
 
     // per-channel parameters
     float A[NS], Dk, db, cw[KW], cb;
@@ -94,44 +98,60 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         IO* dug = static_cast<IO*>(p.du) + ((size_t)b * p.D + d0) * L;
         IO* ddg = static_cast<IO*>(p.ddelta) + ((size_t)b * p.D + d0) * L;
 
-        // --- staging helpers (coalesced: consecutive lanes take consecutive positions of a row)
-        // x window of the chunk at t0: padded positions [t0 - P, t0 - P + XW); zero outside the
-        // sample; the aux-token ends (pad_in) are filled in by xv() from `mean`.
-        auto stage_x = [&](int t0) __attribute__((always_inline)) {
-            for (int e = lane; e < kWave * XW; e += kWave) {
-                const int r = e / XW;
-                const int c = e - r * XW;
-                const int q = t0 - P + c;
-                IO v = Io<IO>::zero();
-                if (r < nrows && q - sh >= 0 && q - sh < XL) v = xg[(size_t)r * XL + q - sh];
-                xs[r * XW + c] = v;
-            }
+        // --- staging of one chunk by direct global->LDS transfers of single io elements
+        // (consecutive lanes take consecutive positions of a row, so the reads coalesce).
+        // Element e of a tile lands in slot tile[e]; elements outside the rows or the sample read
+        // a valid dummy element instead and are never used (xv and the widening mask them).
+        // Tiles: the x window (padded positions [t0 - P, t0 - P + XW)), delta and dy of
+        // positions [t0, t0 + cnt) (dy with its ends exchanged when swap_dy), raw B then C.
+        constexpr int EB = (int)sizeof(IO);
+        constexpr int kPer = 4096 / (kWave * 4);  // transfers per LDS base (4-byte slots)
+        auto dma_tile = [&](auto colsc, uint32_t* tile, auto addr) __attribute__((always_inline)) {
+            constexpr int COLS = decltype(colsc)::value;
+            static_for<COLS>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                const int e = k * kWave + lane;
+                const int r = e / COLS;
+                dma_at<EB, (k % kPer) * kWave * 4>(addr(r, e - r * COLS), tile + (k / kPer) * kPer * kWave);
+            });
         };
-        // delta and dy of positions [t0, t0 + cnt); dy read with the ends exchanged when swap_dy
-        auto stage_d = [&](int t0, int cnt, bool with_dy) __attribute__((always_inline)) {
-            for (int e = lane; e < kWave * Q; e += kWave) {
-                const int r = e / Q;
-                const int c = e - r * Q;
-                const int t = t0 + c;
-                IO v = Io<IO>::zero(), w = Io<IO>::zero();
-                if (r < nrows && c < cnt) {
-                    v = dg[(size_t)r * L + t];
-                    if (with_dy) {
-                        const int ts = (p.swap_dy && L > 1) ? (t == 0 ? L - 1 : (t == L - 1 ? 0 : t)) : t;
-                        w = yg[(size_t)r * L + ts];
-                    }
-                }
-                dls[r * Q + c] = v;
-                if (with_dy) dys[r * Q + c] = w;
+        auto stage = [&](int t0, int cnt, bool with_dy) __attribute__((always_inline)) {
+            const IO* dummy = xg;
+            dma_tile(std::integral_constant<int, XW>{}, xs, [&](int r, int c) {
+                const int q = t0 - P + c - sh;
+                return (r < nrows && q >= 0 && q < XL) ? xg + (size_t)r * XL + q : dummy;
+            });
+            dma_tile(std::integral_constant<int, Q>{}, dls, [&](int r, int c) {
+                return (r < nrows && c < cnt) ? dg + (size_t)r * L + t0 + c : dummy;
+            });
+            if (with_dy) {
+                dma_tile(std::integral_constant<int, Q>{}, dys, [&](int r, int c) {
+                    const int t = t0 + c;
+                    const int ts = (p.swap_dy && L > 1) ? (t == 0 ? L - 1 : (t == L - 1 ? 0 : t)) : t;
+                    return (r < nrows && c < cnt) ? yg + (size_t)r * L + ts : dummy;
+                });
             }
-        };
-        auto stage_bc = [&](int t0, int cnt, bool with_c) __attribute__((always_inline)) {
-            for (int e = lane; e < N * Q; e += kWave) {
-                const int n = e / Q;
-                const int c = e - n * Q;
-                const bool in = c < cnt;
-                bs[c * NS + n] = in ? to_f32(bgl[(size_t)n * L + t0 + c]) : 0.0f;
-                if (with_c) cs[c * NS + n] = in ? to_f32(cgl[(size_t)n * L + t0 + c]) : 0.0f;
+            {
+                // raw B then C: element e < N*Q is B[n = e / Q][t0 + e % Q], the next N*Q are C
+                const int e = lane;
+                const int half = N * Q;
+                const int e2 = e < half ? e : e - half;
+                const int n = e2 / Q;
+                const int c = e2 - n * Q;
+                const IO* src = (e < 2 * half && c < cnt && (e < half || with_dy))
+                                    ? (e < half ? bgl : cgl) + (size_t)n * L + t0 + c
+                                    : dummy;
+                dma_at<EB, 0>(src, braw);
+            }
+            wait_vmem();
+            wave_lds_sync();
+            // widen B/C to float32 [c][n]; states n >= N and positions past the sample are zero
+            if (lane < Q * NS) {
+                const int c = lane / NS;
+                const int n = lane - c * NS;
+                const bool in = n < N && c < cnt;
+                bs[lane] = in ? Io<IO>::of_bits(braw[n * Q + c]) : 0.0f;
+                cs[lane] = (in && with_dy) ? Io<IO>::of_bits(braw[N * Q + n * Q + c]) : 0.0f;
             }
         };
 
@@ -145,19 +165,19 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 for (int e = lane; e < kWave * XW; e += kWave) {
                     const int r = e / XW;
                     const int c = e - r * XW;
-                    xs[r * XW + c] = (r < nrows && c < cnt) ? xg[(size_t)r * XL + c0 + c] : Io<IO>::zero();
+                    xs[r * XW + c] = (r < nrows && c < cnt) ? Io<IO>::bits(xg[(size_t)r * XL + c0 + c]) : 0u;
                 }
                 wave_lds_sync();
-                for (int c = 0; c < cnt; ++c) acc += (double)to_f32(xs[lane * XW + c]);
+                for (int c = 0; c < cnt; ++c) acc += (double)Io<IO>::of_bits(xs[lane * XW + c]);
             }
             mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
         }
         // conv/scan input at padded position q = t0 - P + c (column c of the staged window)
         auto xv = [&](int t0, int c) __attribute__((always_inline)) {
             const int q = t0 - P + c;
-            float v = to_f32(xs[lane * XW + c]);
+            float v = Io<IO>::of_bits(xs[lane * XW + c]);
             if (p.pad_in && (q == 0 || q == L - 1)) v = mean;
-            return v;
+            return (valid && q >= 0 && q < L) ? v : 0.0f;  // zero taps outside the sample
         };
         // z (pre-activation), u, v (pre-softplus) and Delta*log2e at position t0 + i
         auto pre = [&](int t0, int i, float& z, float& u, float& v, float& dt) __attribute__((always_inline)) {
@@ -171,7 +191,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 z = xv(t0, i + P);
                 u = z;
             }
-            v = to_f32(dls[lane * Q + i]) + db;
+            v = (valid ? Io<IO>::of_bits(dls[lane * Q + i]) : 0.0f) + db;
             dt = SP ? softplus_log2e(v) * kLn2 : v;
         };
 
@@ -187,9 +207,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 for (int n = 0; n < NS; ++n) ws[((size_t)c * NS + n) * kWave + lane] = h[n];
             }
             wave_lds_sync();
-            stage_x(t0);
-            stage_d(t0, cnt, false);
-            stage_bc(t0, cnt, false);
+            stage(t0, cnt, false);
             wave_lds_sync();
             for (int i = 0; i < cnt; ++i) {
                 float z, u, v, dt;
@@ -214,9 +232,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             const int t0 = c * Q;
             const int cnt = min(Q, L - t0);
             wave_lds_sync();
-            stage_x(t0);
-            stage_d(t0, cnt, true);
-            stage_bc(t0, cnt, true);
+            stage(t0, cnt, true);
             for (int e = lane; e < kWave * XW; e += kWave) dxs[e] = 0.0f;
             float hin[NS];
 #pragma unroll
@@ -227,6 +243,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             float zs[Q], us[Q], vs[Q], dts[Q];
 #pragma unroll
             for (int i = 0; i < Q; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
                 if (i < cnt) {
                     pre(t0, i, zs[i], us[i], vs[i], dts[i]);
                     const float du_ = dts[i] * us[i];
@@ -244,12 +261,14 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
                 for (int ii = R - 1; ii >= 0; --ii) {
                     const int i = r0 + ii;
+                    // one position at a time: keeps the schedule (and register use) to one step
+                    __builtin_amdgcn_sched_barrier(0);
                     float dBv[NS], dCv[NS];
 #pragma unroll
                     for (int n = 0; n < NS; ++n) dBv[n] = dCv[n] = 0.0f;
                     if (i < cnt) {
                         const int t = t0 + i;
-                        const float gy = to_f32(dys[lane * Q + i]);
+                        const float gy = valid ? Io<IO>::of_bits(dys[lane * Q + i]) : 0.0f;
                         const float u = us[i], dt = dts[i];
                         float du_ = Dk * gy;
                         float ddt = 0.0f;
@@ -275,7 +294,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                         }
                         float dv = ddt;
                         if constexpr (SP) dv = vs[i] > 20.0f ? ddt : ddt * sigmoid_f(vs[i]);
-                        dls[lane * Q + i] = from_f32<IO>(dv);
+                        dls[lane * Q + i] = __float_as_uint(dv);
                         gb += dv;
                         float dz = du_;
                         if constexpr (CONV && SILU) {
@@ -337,7 +356,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int e = lane; e < kWave * Q; e += kWave) {
                 const int r = e / Q;
                 const int cc = e - r * Q;
-                if (r < nrows && cc < cnt) ddg[(size_t)r * L + t0 + cc] = dls[r * Q + cc];
+                if (r < nrows && cc < cnt) ddg[(size_t)r * L + t0 + cc] = from_f32<IO>(__uint_as_float(dls[r * Q + cc]));
             }
             // dx columns finished in this chunk: padded positions [lo, hi)
             const int lag = CONV ? KW - 1 - P : 0;
@@ -380,7 +399,7 @@ hipError_t zero_f32(float* a, size_t n, hipStream_t s) {
 
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
 hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
-    constexpr int Q = NS == 16 ? 4 : 8;
+    constexpr int Q = 32 / NS;  // 32 states of history in registers
     hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)), dim3(kWave),
                        (size_t)p.lds_bytes, s, p);
     return hipGetLastError();
@@ -410,27 +429,29 @@ hipError_t launch_bio(const BwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
+bool plan_bwd(BwdParams& p, int /*io_bytes*/, size_t* ws_bytes) {
     p.ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
     p.tiles = (p.D + kWave - 1) / kWave;
-    p.q = p.ns == 16 ? 4 : 8;
+    p.q = 32 / p.ns;
     p.nchk = (p.L + p.q - 1) / p.q;
     const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 4;
     const int xw = p.q + kw - 1;
     auto up16 = [](int v) { return (v + 15) & ~15; };
     int off = 0;
     p.xs_off = off;
-    off += up16(kWave * xw * io_bytes);
+    off += up16(kWave * xw * 4);  // staged io elements take 4-byte slots
     p.ds_off = off;
-    off += up16(kWave * p.q * io_bytes);
+    off += up16(kWave * p.q * 4);
     p.dys_off = off;
-    off += up16(kWave * p.q * io_bytes);
+    off += up16(kWave * p.q * 4);
     p.bc_off = off;
     off += up16(2 * p.q * p.ns * 4);
     p.red_off = off;
     off += kWave * kRedStride * 4;
     p.mean_off = off;  // fp32 dx window
     off += up16(kWave * xw * 4);
+    p.braw_off = off;  // raw B/C of a chunk: one 64-element transfer
+    off += up16(kWave * 4);
     p.lds_bytes = off;
     *ws_bytes = (size_t)p.B1 * p.tiles * p.nchk * p.ns * kWave * sizeof(float);
     return p.lds_bytes <= 64 * 1024;

@@ -126,7 +126,9 @@ __device__ __forceinline__ void wait_vmem_at_most(int k) {
 }
 
 // One 64-lane direct global->LDS transfer of SIZE bytes per lane: lane i's
-// bytes at global address g land at LDS address l + OFF + i * SIZE.  OFF is an
+// bytes at global address g land at LDS address l + OFF + i * max(SIZE, 4)
+// (a transfer of fewer than 4 bytes still gives every lane a 4-byte slot, the
+// data in its low bytes: CDNA3 ISA, global loads to LDS).  OFF is an
 // immediate of the instruction (it moves both addresses, so g is passed
 // pre-decremented).  Consecutive transfers that differ only in OFF share one
 // LDS base register; rewriting that register between transfers serialises
@@ -134,7 +136,8 @@ __device__ __forceinline__ void wait_vmem_at_most(int k) {
 // with ten waves per CU).
 template <int SIZE, int OFF>
 __device__ __forceinline__ void dma_at(const void* g, void* l) {
-    static_assert((SIZE == 16 && OFF % 1024 == 0 && OFF < 4096) || (SIZE == 4 && OFF % 256 == 0 && OFF < 4096),
+    static_assert((SIZE == 16 && OFF % 1024 == 0 && OFF < 4096) || (SIZE == 4 && OFF % 256 == 0 && OFF < 4096) ||
+                      (SIZE == 2 && OFF % 256 == 0 && OFF < 4096),
                   "unsupported transfer size / offset");
     const char* gp = static_cast<const char*>(g) - OFF;
     const lds_void_ptr lp = (lds_void_ptr)l;
@@ -146,6 +149,10 @@ __device__ __forceinline__ void dma_at(const void* g, void* l) {
     SFM_DMA_AT(4, 1024) SFM_DMA_AT(4, 1280) SFM_DMA_AT(4, 1536) SFM_DMA_AT(4, 1792)
     SFM_DMA_AT(4, 2048) SFM_DMA_AT(4, 2304) SFM_DMA_AT(4, 2560) SFM_DMA_AT(4, 2816)
     SFM_DMA_AT(4, 3072) SFM_DMA_AT(4, 3328) SFM_DMA_AT(4, 3584) SFM_DMA_AT(4, 3840)
+    SFM_DMA_AT(2, 0) SFM_DMA_AT(2, 256) SFM_DMA_AT(2, 512) SFM_DMA_AT(2, 768)
+    SFM_DMA_AT(2, 1024) SFM_DMA_AT(2, 1280) SFM_DMA_AT(2, 1536) SFM_DMA_AT(2, 1792)
+    SFM_DMA_AT(2, 2048) SFM_DMA_AT(2, 2304) SFM_DMA_AT(2, 2560) SFM_DMA_AT(2, 2816)
+    SFM_DMA_AT(2, 3072) SFM_DMA_AT(2, 3328) SFM_DMA_AT(2, 3584) SFM_DMA_AT(2, 3840)
 #undef SFM_DMA_AT
 }
 

@@ -74,7 +74,7 @@ struct BwdParams {
     int xrow;             // row length of u
     // plan
     int ns, tiles, q, nchk;
-    int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, lds_bytes;
+    int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, braw_off, lds_bytes;
 };
 
 // Backward planning; returns false when no plan fits.  ws_bytes: workspace size.
