@@ -169,8 +169,13 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  * workspace: device memory of at least sfm_selective_scan_bwd_workspace_size()
  *   bytes, owned by the caller, not overlapping anything else; it holds float32
  *   state checkpoints (every 32/Np positions, Np = N rounded up to 4, 8 or 16)
- *   for the duration of the call.  The library allocates nothing.  The f32 sums are accumulated with
- *   atomics, so their summation order (and last bits) may vary between runs.
+ *   for the duration of the call.  The library allocates nothing.  The f32
+ *   sums are accumulated with atomics, so their summation order (and last
+ *   bits) may vary between runs.
+ * Two kernels: when every [rows][length] block of a sample and 64-channel tile
+ * is a whole number of 16-byte units on 16-byte boundaries and fits in LDS,
+ * each sample is staged once; otherwise chunk by chunk.  Environment override
+ * (diagnostics): SFM_BWD_CHUNKED=1 forces the chunked kernel.
  * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN (nothing launched), HIP.
  */
 sfm_status sfm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,

@@ -26,6 +26,10 @@
 // it to the output with a float32 atomic (one per channel tile).  Per-channel
 // sums (dA, dD, dbias, dconv) stay in registers over the wave's samples and are
 // added with atomics at the end.  All float32 outputs are zeroed first.
+#include <stdlib.h>
+
+#include <algorithm>
+
 #include <type_traits>
 
 #include "sfm_device.h"
@@ -35,6 +39,10 @@ namespace sfm {
 
 namespace {
 
+#ifndef SFM_BWD_HIST
+#define SFM_BWD_HIST 32
+#endif
+constexpr int kHist = SFM_BWD_HIST;  // states of history per chunk held in registers
 constexpr int kRedStride = 68;  // floats per row of the transpose buffer (16-byte rows, no 16-lane bank clash)
 
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + exp2_fast(-v * kLog2e)); }
@@ -43,7 +51,7 @@ template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     constexpr int XW = Q + KW - 1;  // x window columns of a chunk
-    constexpr int R = 32 / NS;      // positions per dB/dC transpose round (2*NS*R = 64 rows)
+    constexpr int R = Q < 32 / NS ? Q : 32 / NS;  // positions per dB/dC transpose round (2*NS*R <= 64 rows)
     static_assert(Q % R == 0, "chunk must hold whole transpose rounds");
     const int lane = threadIdx.x;
     const int g = blockIdx.x;
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                         const float4 v4 = row[m];
                         s += (v4.x + v4.y) + (v4.z + v4.w);
                     }
-                    if (n < N && r0 + ii < cnt) atomicAdd((k < NS ? p.dBm : p.dCm) + ((size_t)b * N + n) * L + t, s);
+                    if (lane < 2 * NS * R && n < N && r0 + ii < cnt) atomicAdd((k < NS ? p.dBm : p.dCm) + ((size_t)b * N + n) * L + t, s);
                 }
                 wave_lds_sync();
             }
@@ -385,23 +393,396 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     }
 }
 
-__global__ void zero_kernel(float* a, size_t n) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-        a[i] = 0.0f;
+// Whole-sample variant.  The x, delta and dy blocks of one sample and channel
+// tile are each one contiguous range of memory ([rows][length], rows = the
+// tile's channels), so they are staged once per sample with 16-byte direct
+// transfers and serve both sweeps.  ddelta replaces delta in place (position t
+// is overwritten after its last read) and the conv-input gradient replaces dy
+// (position q is complete only after dy at q was read; the two dy values at the
+// sample ends are read up front because swap_dy moves them).  Both blocks leave
+// with 16-byte stores once the sample is done.  B and C of the sample are
+// widened to float32 once.  The dB/dC transpose uses 32 rows; two lanes sum
+// the two halves of a row.
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_whole_kernel(BwdParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    constexpr int R = 16 / NS;  // positions per dB/dC transpose round (2 * NS * R = 32 rows)
+    static_assert(Q % R == 0, "chunk must hold whole transpose rounds");
+    constexpr int EB = (int)sizeof(IO);
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    const int b1 = g / p.tiles;
+    const int tile = g - b1 * p.tiles;
+    const int d0 = tile * kWave;
+    const int nrows = min(kWave, p.D - d0);
+    const int d = d0 + lane;
+    const bool valid = lane < nrows;
+    const int L = p.L, XL = p.xrow, N = p.N;
+    const int P = CONV ? p.P : 0;
+    const int sh = p.pad_in ? 1 : 0;  // padded position q reads u row index q - sh
+    const int lag = CONV ? KW - 1 - P : 0;  // dx of position t + lag is complete after step t
+
+    IO* xs = reinterpret_cast<IO*>(smem + p.xs_off);        // [rows][XL] x
+    IO* ds = reinterpret_cast<IO*>(smem + p.ds_off);        // [rows][L]  delta, then ddelta
+    IO* ys = reinterpret_cast<IO*>(smem + p.dys_off);       // [rows][L]  dy, then dx
+    float* bs = reinterpret_cast<float*>(smem + p.bc_off);  // [L][NS]
+    float* cs = bs + L * NS;                                // [L][NS]
+    float* red = reinterpret_cast<float*>(smem + p.red_off);  // [32][kRedStride]
+    const int xrow = valid ? lane * XL : 0;  // lanes past the tile read row 0 and mask the value
+    const int row = valid ? lane * L : 0;
+    // one position's NS float32 values of B (or C) as whole 16-byte reads
+    auto bc_row = [&](const float* base, int t, float (&v)[NS]) __attribute__((always_inline)) {
+        const float4* r = reinterpret_cast<const float4*>(base + t * NS);
+#pragma unroll
+        for (int k = 0; k < NS / 4; ++k) {
+            const float4 w = r[k];
+            v[4 * k] = w.x;
+            v[4 * k + 1] = w.y;
+            v[4 * k + 2] = w.z;
+            v[4 * k + 3] = w.w;
+        }
+    };
+
+    float A[NS], Dk, db, cw[KW], cb;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) A[n] = (valid && n < N) ? p.A[(size_t)d * N + n] : 0.0f;
+    Dk = (valid && p.Dskip) ? p.Dskip[d] : 0.0f;
+    db = (valid && p.dbias) ? p.dbias[d] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) cw[j] = (CONV && valid && j < p.K) ? p.conv_w[(size_t)d * p.K + j] : 0.0f;
+    cb = (CONV && valid && p.conv_b) ? p.conv_b[d] : 0.0f;
+    float gA[NS], gD = 0.0f, gb = 0.0f, gw[KW], gcb = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) gA[n] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) gw[j] = 0.0f;
+    // states n >= N stay zero in the B/C stage
+    for (int e = lane; e < L * NS; e += kWave)
+        if (e % NS >= N) bs[e] = cs[e] = 0.0f;
+    float* ws = p.ws + (size_t)g * p.nchk * NS * kWave + lane;
+    const int NL = N * L;
+    const float inv_L = 1.0f / (float)L;
+
+    for (int j = 0; j < p.B2; ++j) {
+        const int b = b1 * p.B2 + j;
+        const size_t xoff = ((size_t)b * p.D + d0) * XL;
+        const size_t toff = ((size_t)b * p.D + d0) * L;
+        const IO* bgl = static_cast<const IO*>(p.Bm) + (size_t)b * NL;
+        const IO* cgl = static_cast<const IO*>(p.Cm) + (size_t)b * NL;
+        wave_lds_sync();  // the previous sample's LDS reads are done
+        // --- staging: B/C element loads (8 per lane in flight), then the three blocks
+        for (int e0 = 0; e0 < NL; e0 += 8 * kWave) {
+            IO bv[8], cv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = e0 + k * kWave + lane;
+                bv[k] = e < NL ? bgl[e] : Io<IO>::zero();
+                cv[k] = e < NL ? cgl[e] : Io<IO>::zero();
+            }
+            if (e0 == 0) {
+                dma_to_lds(static_cast<const IO*>(p.u) + xoff, xs, nrows * XL * EB, lane);
+                dma_to_lds(static_cast<const IO*>(p.delta) + toff, ds, nrows * L * EB, lane);
+                dma_to_lds(static_cast<const IO*>(p.dy) + toff, ys, nrows * L * EB, lane);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = e0 + k * kWave + lane;
+                if (e < NL) {
+                    const int n = div_small(e, inv_L);
+                    const int t = e - n * L;
+                    bs[t * NS + n] = to_f32(bv[k]);
+                    cs[t * NS + n] = to_f32(cv[k]);
+                }
+            }
+        }
+        wait_vmem();
+        wave_lds_sync();
+
+        // --- fused aux pad: this row's mean, float64 in index order (as the forward)
+        float mean = 0.0f;
+        if (p.pad_in) {
+            double acc = 0.0;
+            for (int c = 0; c < XL; ++c) acc += (double)to_f32(xs[xrow + c]);
+            mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+        }
+        // conv/scan input at padded position q (zero outside the sample)
+        auto xv = [&](int q) __attribute__((always_inline)) {
+            const int qc = min(max(q - sh, 0), XL - 1);
+            float v = to_f32(xs[xrow + qc]);
+            if (p.pad_in && (q == 0 || q == L - 1)) v = mean;
+            return (valid && q >= 0 && q < L) ? v : 0.0f;
+        };
+        constexpr int XW = Q + KW - 1;  // conv input window of a chunk
+        // window of the chunk at t0: xw[c] = input at padded position t0 - P + c
+        auto window = [&](int t0, float (&xw)[XW]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int c = 0; c < XW; ++c) xw[c] = xv(t0 - P + c);
+        };
+        // z (pre-activation), u, v (pre-softplus), Delta and Delta*log2e at position t = t0 + i
+        auto pre = [&](const float (&xw)[XW], int t, int i, float& z, float& u, float& v, float& dt, float& dtl)
+            __attribute__((always_inline)) {
+            if constexpr (CONV) {
+                float acc = cb;
+#pragma unroll
+                for (int jj = 0; jj < KW; ++jj) acc = __builtin_fmaf(cw[jj], xw[i + jj], acc);
+                z = acc;
+                u = SILU ? silu(acc) : acc;
+            } else {
+                z = xw[i];
+                u = z;
+            }
+            v = (valid ? to_f32(ds[row + t]) : 0.0f) + db;
+            if constexpr (SP) {
+                dtl = softplus_log2e(v);
+                dt = dtl * kLn2;
+            } else {
+                dt = v;
+                dtl = v * kLog2e;
+            }
+        };
+        // dy at the two sample ends, before the dx written in place can cover them
+        const int ce0 = (p.swap_dy && L > 1) ? L - 1 : 0;
+        const float gy_first = valid ? to_f32(ys[row + ce0]) : 0.0f;
+        const float gy_last = valid ? to_f32(ys[row + (L - 1 - ce0)]) : 0.0f;
+
+        // --- sweep 1: forward, checkpoint the state entering each chunk
+        {
+            float h[NS];
+#pragma unroll
+            for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+            for (int c = 0; c < p.nchk; ++c) {
+                const int t0 = c * Q;
+                const int cnt = min(Q, L - t0);
+                if (c > 0) {
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) ws[((size_t)c * NS + n) * kWave] = h[n];
+                }
+                float xw[XW];
+                window(t0, xw);
+                // the chunk's per-position inputs first (independent), then the state chain
+                float dus[Q], dtls[Q];
+#pragma unroll
+                for (int i = 0; i < Q; ++i) {
+                    float z, u, v, dt;
+                    pre(xw, t0 + min(i, cnt - 1), i, z, u, v, dt, dtls[i]);
+                    dus[i] = dt * u;
+                }
+#pragma unroll
+                for (int i = 0; i < Q; ++i) {
+                    if (i < cnt) {
+                        float Bv[NS];
+                        bc_row(bs, t0 + i, Bv);
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            const float bx = dus[i] * Bv[n];
+                            h[n] = (c == 0 && i == 0) ? bx : __builtin_fmaf(exp2_fast(dtls[i] * A[n]), h[n], bx);
+                        }
+                    }
+                }
+            }
+        }
+
+        // --- sweep 2: chunks in reverse
+        float G[NS];  // a_{t+1} G_{t+1} carried to position t
+#pragma unroll
+        for (int n = 0; n < NS; ++n) G[n] = 0.0f;
+        float wdx[KW];  // dx of padded positions t - P + jj, still collecting contributions
+#pragma unroll
+        for (int jj = 0; jj < KW; ++jj) wdx[jj] = 0.0f;
+        float hnext[NS];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) hnext[n] = p.nchk > 1 ? ws[((size_t)(p.nchk - 1) * NS + n) * kWave] : 0.0f;
+        for (int c = p.nchk - 1; c >= 0; --c) {
+            const int t0 = c * Q;
+            const int cnt = min(Q, L - t0);
+            float hin[NS];
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+                hin[n] = c > 0 ? hnext[n] : 0.0f;
+                // the next chunk's checkpoint, in flight while this chunk runs
+                if (c > 1) hnext[n] = ws[((size_t)(c - 1) * NS + n) * kWave];
+            }
+            // re-run the chunk forward, keeping every state
+            float hs[Q][NS];
+            float zs[Q], us[Q], vs[Q], dts[Q], dtls[Q];
+            float xw[XW];
+            window(t0, xw);
+            // the chunk's per-position inputs first (independent), then the state chain
+            float gys[Q];
+#pragma unroll
+            for (int i = 0; i < Q; ++i) {
+                const int t = t0 + min(i, cnt - 1);
+                pre(xw, t, i, zs[i], us[i], vs[i], dts[i], dtls[i]);
+                gys[i] = t == 0 ? gy_first : (t == L - 1 ? gy_last : (valid ? to_f32(ys[row + t]) : 0.0f));
+            }
+#pragma unroll
+            for (int i = 0; i < Q; ++i) {
+                if (i < cnt) {
+                    const float du_ = dts[i] * us[i];
+                    float Bv[NS];
+                    bc_row(bs, t0 + i, Bv);
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        const float hp = i > 0 ? hs[i - 1][n] : hin[n];
+                        const float bx = du_ * Bv[n];
+                        hs[i][n] = (c == 0 && i == 0) ? bx : __builtin_fmaf(exp2_fast(dtls[i] * A[n]), hp, bx);
+                    }
+                }
+            }
+            // backwards through the chunk, R positions per dB/dC transpose round
+#pragma unroll
+            for (int r0 = Q - R; r0 >= 0; r0 -= R) {
+#pragma unroll
+                for (int ii = R - 1; ii >= 0; --ii) {
+                    const int i = r0 + ii;
+                    // one position at a time: keeps the schedule (and register use) to one step
+                    __builtin_amdgcn_sched_barrier(0);
+                    float dBv[NS], dCv[NS];
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) dBv[n] = dCv[n] = 0.0f;
+                    if (i < cnt) {
+                        const int t = t0 + i;
+                        const float gy = gys[i];
+                        const float u = us[i], dt = dts[i], dtu = dt * u;
+                        float sb = 0.0f;  // sum_n G_n B_n
+                        float sa = 0.0f;  // sum_n G_n h_{t-1,n} a_n A_n
+                        gD = __builtin_fmaf(gy, u, gD);
+                        float Bt[NS], Ct[NS];
+                        bc_row(bs, t, Bt);
+                        bc_row(cs, t, Ct);
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) {
+                            const float Bv = Bt[n], Cv = Ct[n];
+                            const float Gn = __builtin_fmaf(gy, Cv, G[n]);
+                            dCv[n] = gy * hs[i][n];
+                            dBv[n] = Gn * dtu;
+                            sb = __builtin_fmaf(Gn, Bv, sb);
+                            if (c > 0 || i > 0) {
+                                const float hp = i > 0 ? hs[i - 1][n] : hin[n];
+                                const float a = exp2_fast(dtls[i] * A[n]);
+                                const float dat = Gn * hp * a;  // dLoss/da_t times a_t
+                                sa = __builtin_fmaf(dat, A[n], sa);
+                                gA[n] = __builtin_fmaf(dat, dt, gA[n]);
+                                G[n] = a * Gn;
+                            } else {
+                                G[n] = 0.0f;  // reset: nothing reaches the previous sample
+                            }
+                        }
+                        const float ddt = __builtin_fmaf(sb, u, sa);
+                        float dv = ddt;
+                        if constexpr (SP) dv = vs[i] > 20.0f ? ddt : ddt * sigmoid_f(vs[i]);
+                        if (valid) ds[row + t] = from_f32<IO>(dv);
+                        gb += dv;
+                        const float du_ = __builtin_fmaf(dt, sb, Dk * gy);
+                        float dz = du_;
+                        if constexpr (CONV && SILU) {
+                            const float s = sigmoid_f(zs[i]);
+                            dz = du_ * (s + zs[i] * s * (1.0f - s));
+                        }
+                        if constexpr (CONV) {
+                            gcb += dz;
+#pragma unroll
+                            for (int jj = 0; jj < KW; ++jj) {
+                                gw[jj] = __builtin_fmaf(dz, xw[i + jj], gw[jj]);
+                                wdx[jj] = __builtin_fmaf(dz, cw[jj], wdx[jj]);
+                            }
+                            // padded position t + lag gets no later contribution
+                            if (valid && t + lag < L) ys[row + t + lag] = from_f32<IO>(wdx[KW - 1]);
+#pragma unroll
+                            for (int jj = KW - 1; jj > 0; --jj) wdx[jj] = wdx[jj - 1];
+                            wdx[0] = 0.0f;
+                        } else {
+                            if (valid) ys[row + t] = from_f32<IO>(dz);
+                        }
+                    }
+                    // transpose buffer: row (ii, k), column lane
+#pragma unroll
+                    for (int n = 0; n < NS; ++n) {
+                        red[(ii * 2 * NS + n) * kRedStride + lane] = dBv[n];
+                        red[(ii * 2 * NS + NS + n) * kRedStride + lane] = dCv[n];
+                    }
+                }
+                wave_lds_sync();
+                {
+                    // lanes l and l + 32 sum the two halves of row l % 32:
+                    // position r0 + row / (2NS), state row % NS, B or C
+                    const int rr = lane & 31;
+                    const int ii = rr / (2 * NS);
+                    const int k = rr - ii * 2 * NS;
+                    const int n = k % NS;
+                    const float4* rp = reinterpret_cast<const float4*>(red + rr * kRedStride + (lane >> 5) * 32);
+                    float s = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        const float4 v4 = rp[m];
+                        s += (v4.x + v4.y) + (v4.z + v4.w);
+                    }
+                    s += __shfl_xor(s, 32);
+                    if (lane < 32 && n < N && r0 + ii < cnt)
+                        atomicAdd((k < NS ? p.dBm : p.dCm) + ((size_t)b * N + n) * L + t0 + r0 + ii, s);
+                }
+                wave_lds_sync();
+            }
+        }
+        if constexpr (CONV) {
+            // after the step at t = 0 and its shift, wdx[m] holds padded position m - 1 - P
+#pragma unroll
+            for (int m = 1; m < KW; ++m) {
+                const int q = m - 1 - P;
+                if (valid && q >= 0 && q < L) ys[row + q] = from_f32<IO>(wdx[m]);
+            }
+        }
+        wave_lds_sync();
+        // --- ddelta and dx leave as whole blocks
+        {
+            const int units = nrows * L * EB / 16;
+            const uint4* sd = reinterpret_cast<const uint4*>(ds);
+            const uint4* sy = reinterpret_cast<const uint4*>(ys);
+            uint4* gd = reinterpret_cast<uint4*>(static_cast<IO*>(p.ddelta) + toff);
+            uint4* gu = reinterpret_cast<uint4*>(static_cast<IO*>(p.du) + toff);
+            for (int u = lane; u < units; u += kWave) {
+                gd[u] = sd[u];
+                gu[u] = sy[u];
+            }
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+            if (n < N) atomicAdd(p.dA + (size_t)d * N + n, gA[n]);
+        if (p.dDskip) atomicAdd(p.dDskip + d, gD);
+        if (p.ddbias) atomicAdd(p.ddbias + d, gb);
+        if constexpr (CONV) {
+#pragma unroll
+            for (int jj = 0; jj < KW; ++jj)
+                if (jj < p.K && p.dconv_w) atomicAdd(p.dconv_w + (size_t)d * p.K + jj, gw[jj]);
+            if (p.dconv_b) atomicAdd(p.dconv_b + d, gcb);
+        }
+    }
 }
 
-hipError_t zero_f32(float* a, size_t n, hipStream_t s) {
-    if (!a || n == 0) return hipSuccess;
-    const unsigned blocks = (unsigned)std::min<size_t>(1024, (n + 255) / 256);
-    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, a, n);
-    return hipGetLastError();
+// Zeroes up to eight float32 arrays in one launch (the sums the backward adds into).
+struct ZeroList {
+    float* p[8];
+    unsigned long long n[8];
+    int count;
+};
+
+__global__ void zero_kernel(ZeroList z) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (int k = 0; k < z.count; ++k)
+        for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < z.n[k]; i += stride) z.p[k][i] = 0.0f;
 }
 
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
 hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
-    constexpr int Q = 32 / NS;  // 32 states of history in registers
-    hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)), dim3(kWave),
-                       (size_t)p.lds_bytes, s, p);
+    constexpr int Q = kHist / NS;  // kHist states of history in registers
+    if (p.whole)
+        hipLaunchKernelGGL((bwd_whole_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)),
+                           dim3(kWave), (size_t)p.lds_bytes, s, p);
+    else
+        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)), dim3(kWave),
+                           (size_t)p.lds_bytes, s, p);
     return hipGetLastError();
 }
 
@@ -429,23 +810,54 @@ hipError_t launch_bio(const BwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-bool plan_bwd(BwdParams& p, int /*io_bytes*/, size_t* ws_bytes) {
+bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     p.ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
     p.tiles = (p.D + kWave - 1) / kWave;
-    p.q = 32 / p.ns;
+    p.q = kHist / p.ns;
     p.nchk = (p.L + p.q - 1) / p.q;
+    *ws_bytes = (size_t)p.B1 * p.tiles * p.nchk * p.ns * kWave * sizeof(float);
+    auto up16 = [](long long v) { return (int)((v + 15) & ~15LL); };
+    // Whole-sample staging: every [rows][length] block (x, delta, dy, ddelta, du)
+    // of every sample and tile must start on 16 bytes and span whole 16-byte
+    // units (rows = 64, or D mod 64 for the last tile), and everything must
+    // leave room for at least two workgroups per compute unit.
+    {
+        const long long XL = p.xrow, L = p.L, eb = io_bytes;
+        const int last = p.D - (p.tiles - 1) * kWave;
+        bool ok = (p.D * XL * eb) % 16 == 0 && (p.D * L * eb) % 16 == 0 && (kWave * XL * eb) % 16 == 0 &&
+                  (kWave * L * eb) % 16 == 0 && (last * XL * eb) % 16 == 0 && (last * L * eb) % 16 == 0;
+        int off = 0;
+        p.xs_off = off;
+        off += up16(kWave * XL * eb);
+        p.ds_off = off;
+        off += up16(kWave * L * eb);
+        p.dys_off = off;
+        off += up16(kWave * L * eb);
+        p.bc_off = off;
+        off += up16(2 * L * p.ns * 4);
+        p.red_off = off;
+        off += 32 * kRedStride * 4;
+        const char* force = getenv("SFM_BWD_CHUNKED");  // diagnostics: force the chunked kernel
+        if (ok && L <= 4096 && off <= 64 * 1024 && !(force && atoi(force) > 0)) {
+            p.whole = 1;
+            p.mean_off = p.braw_off = 0;
+            p.lds_bytes = off;
+            return true;
+        }
+    }
+    p.whole = 0;
+    const int q = p.q;
     const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 4;
-    const int xw = p.q + kw - 1;
-    auto up16 = [](int v) { return (v + 15) & ~15; };
+    const int xw = q + kw - 1;
     int off = 0;
     p.xs_off = off;
     off += up16(kWave * xw * 4);  // staged io elements take 4-byte slots
     p.ds_off = off;
-    off += up16(kWave * p.q * 4);
+    off += up16(kWave * q * 4);
     p.dys_off = off;
-    off += up16(kWave * p.q * 4);
+    off += up16(kWave * q * 4);
     p.bc_off = off;
-    off += up16(2 * p.q * p.ns * 4);
+    off += up16(2 * q * p.ns * 4);
     p.red_off = off;
     off += kWave * kRedStride * 4;
     p.mean_off = off;  // fp32 dx window
@@ -453,22 +865,32 @@ bool plan_bwd(BwdParams& p, int /*io_bytes*/, size_t* ws_bytes) {
     p.braw_off = off;  // raw B/C of a chunk: one 64-element transfer
     off += up16(kWave * 4);
     p.lds_bytes = off;
-    *ws_bytes = (size_t)p.B1 * p.tiles * p.nchk * p.ns * kWave * sizeof(float);
     return p.lds_bytes <= 64 * 1024;
 }
 
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t s) {
     const size_t B = (size_t)p.B1 * p.B2;
-    hipError_t e;
-    if ((e = zero_f32(p.dA, (size_t)p.D * p.N, s)) != hipSuccess) return e;
-    if ((e = zero_f32(p.dBm, B * p.N * p.L, s)) != hipSuccess) return e;
-    if ((e = zero_f32(p.dCm, B * p.N * p.L, s)) != hipSuccess) return e;
-    if ((e = zero_f32(p.dDskip, p.D, s)) != hipSuccess) return e;
-    if ((e = zero_f32(p.ddbias, p.D, s)) != hipSuccess) return e;
+    ZeroList z{};
+    size_t most = 0;
+    auto add = [&](float* a, size_t n) {
+        if (!a || n == 0) return;
+        z.p[z.count] = a;
+        z.n[z.count++] = n;
+        most = std::max(most, n);
+    };
+    add(p.dA, (size_t)p.D * p.N);
+    add(p.dBm, B * p.N * p.L);
+    add(p.dCm, B * p.N * p.L);
+    add(p.dDskip, p.D);
+    add(p.ddbias, p.D);
     if (p.conv_w) {
-        if ((e = zero_f32(p.dconv_w, (size_t)p.D * p.K, s)) != hipSuccess) return e;
-        if ((e = zero_f32(p.dconv_b, p.D, s)) != hipSuccess) return e;
+        add(p.dconv_w, (size_t)p.D * p.K);
+        add(p.dconv_b, p.D);
     }
+    const unsigned blocks = (unsigned)std::min<size_t>(1024, (most + 255) / 256);
+    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, z);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (io_dtype == 0) return launch_bio<float>(p, s);
     return launch_bio<__bf16>(p, s);
 }

@@ -396,14 +396,19 @@ extern "C" sfm_status sfm_selective_scan_bwd(
     const int64_t B = B1 * B2;
     const int eb = io_bytes(io_dtype);
     const int64_t XL = (flags & SFM_FUSE_PAD) ? L - 2 : L;
+    const int64_t K = conv_w ? conv_k : 0;
     const Range ins[] = {rng("u", u, B * D * XL * eb), rng("delta", delta, B * D * L * eb),
-                         rng("Bm", Bm, B * N * L * eb), rng("Cm", Cm, B * N * L * eb), rng("dy", dy, B * D * L * eb)};
+                         rng("Bm", Bm, B * N * L * eb), rng("Cm", Cm, B * N * L * eb), rng("dy", dy, B * D * L * eb),
+                         rng("A", A, D * N * 4), rng("Dskip", Dskip, D * 4), rng("delta_bias", delta_bias, D * 4),
+                         rng("conv_w", conv_w, D * K * 4), rng("conv_b", conv_b, conv_w ? D * 4 : 0)};
     const Range outs[] = {rng("du", du, B * D * L * eb), rng("ddelta", ddelta, B * D * L * eb),
                           rng("dA", dA, D * N * 4), rng("dBm", dBm, B * N * L * 4), rng("dCm", dCm, B * N * L * 4),
+                          rng("dDskip", dDskip, D * 4), rng("ddelta_bias", ddelta_bias, D * 4),
+                          rng("dconv_w", dconv_w, D * K * 4), rng("dconv_b", dconv_b, conv_w ? D * 4 : 0),
                           rng("workspace", workspace, workspace_bytes)};
     for (const Range& o : outs)
         for (const Range& i : ins)
-            if (o.lo && overlap(o, i)) return fail(SFM_ERR_ALIAS, "%s: %s overlaps %s", who, o.name, i.name);
+            if (o.lo && i.lo && overlap(o, i)) return fail(SFM_ERR_ALIAS, "%s: %s overlaps %s", who, o.name, i.name);
     for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a)
         for (size_t c = a + 1; c < sizeof(outs) / sizeof(outs[0]); ++c)
             if (outs[a].lo && outs[c].lo && overlap(outs[a], outs[c]))

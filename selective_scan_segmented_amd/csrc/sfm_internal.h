@@ -74,6 +74,7 @@ struct BwdParams {
     int xrow;             // row length of u
     // plan
     int ns, tiles, q, nchk;
+    int whole;            // 1: whole-sample slabs staged once per sample; 0: chunk by chunk
     int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, braw_off, lds_bytes;
 };
 

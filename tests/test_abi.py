@@ -119,3 +119,56 @@ def test_pick_b1_env_table_overrides(lib, tmp_path, monkeypatch):
     assert sfm.sfm_pick_b1(256, 51, 640, 8) == 32
     # nearest key, then the largest divisor of B not above the table's B2
     assert sfm.sfm_pick_b1(12, 51, 640, 8) == 2
+
+
+def bwd(lib, **kw):
+    a = dict(u=P, delta=2 * P, A=3 * P, Bm=4 * P, Cm=5 * P, Dskip=None, dbias=None, sp=1, cw=None, cb=None, k=4,
+             pad=1, act=0, dy=6 * P, du=7 * P, ddelta=8 * P, dA=9 * P, dBm=10 * P, dCm=11 * P, dD=None, db=None,
+             dcw=None, dcb=None, B1=2, B2=2, D=4, N=4, L=10, io=0, flags=0, ws=12 * P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.sfm_selective_scan_bwd(
+        a["u"], a["delta"], a["A"], a["Bm"], a["Cm"], a["Dskip"], a["dbias"], a["sp"], a["cw"], a["cb"], a["k"],
+        a["pad"], a["act"], a["dy"], a["du"], a["ddelta"], a["dA"], a["dBm"], a["dCm"], a["dD"], a["db"], a["dcw"],
+        a["dcb"], a["B1"], a["B2"], a["D"], a["N"], a["L"], a["io"], a["flags"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, dy=None) == NULL
+    assert bwd(lib, du=None) == NULL
+    assert bwd(lib, dCm=None) == NULL
+    assert bwd(lib, cw=13 * P, dcw=None) == NULL      # conv weights need their gradient
+    assert bwd(lib, io=2) == DTYPE
+    assert bwd(lib, N=17) == SHAPE
+    assert bwd(lib, flags=4) == SHAPE                  # unknown flag
+    assert bwd(lib, flags=1, L=2) == SHAPE             # fused pad needs L >= 3
+    assert bwd(lib, cw=13 * P, dcw=14 * P, k=4, pad=4) == SHAPE
+    assert bwd(lib, sp=3) == SHAPE
+    assert bwd(lib, du=7 * P + 4) == ALIGN
+    assert bwd(lib, du=P) == ALIAS                     # du on top of u
+    assert bwd(lib, dA=8 * P + 8) == ALIAS             # dA inside ddelta
+    assert bwd(lib, dD=3 * P) == ALIAS                 # dDskip on top of A
+    assert bwd(lib, ws=10 * P) == ALIAS                # workspace on top of dBm
+    assert bwd(lib, ws=None) == SHAPE                  # no workspace
+    assert bwd(lib, wsb=16) == SHAPE                   # too small
+    assert b"workspace" in lib.sfm_last_error()
+
+
+def test_bwd_workspace_size(lib):
+    out = ctypes.c_int64(0)
+    f = lib.sfm_selective_scan_bwd_workspace_size
+    assert f(2, 2, 4, 4, 10, 4, 0, 0, ctypes.byref(out)) == OK
+    # one float32 state checkpoint per (row, channel tile, chunk, state, lane): chunks of 32/Np positions
+    assert out.value == 2 * 1 * ((10 + 7) // 8) * 4 * 64 * 4
+    assert f(2, 2, 4, 4, 10, 4, 0, 0, None) == NULL
+    assert f(2, 2, 4, 0, 10, 4, 0, 0, ctypes.byref(out)) == SHAPE
+    assert f(2, 2, 4, 4, 10, 4, 9, 0, ctypes.byref(out)) == DTYPE
+    assert sfm.sfm_selective_scan_bwd_workspace_size(256, 1, 640, 8, 51, 4, "bf16", 3) == 256 * 10 * 13 * 8 * 64 * 4
+
+
+def test_aux_pad_bwd_validation(lib):
+    f = lib.sfm_aux_pad_bwd
+    assert f(None, P, 2, 3, 4, 0, None) == NULL
+    assert f(P, 2 * P, 2, 3, 0, 0, None) == SHAPE
+    assert f(P, 2 * P, 2, 3, 4, 5, None) == DTYPE
+    assert f(P, P + 16, 2, 3, 4, 0, None) == ALIAS
+    assert f(P, P + 8, 2, 3, 4, 0, None) == ALIGN

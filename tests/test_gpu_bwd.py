@@ -116,6 +116,25 @@ def test_bwd_variants_f32(B, D, N, T, B2, K, P, act, sp, flags):
     run_case(B=B, D=D, N=N, T=T, B2=B2, K=K, P=P, act=act, softplus=sp, flags=flags, io="f32", seed=B * 7 + T)
 
 
+@pytest.mark.parametrize("B,D,N,T,B2,K,P,act,sp,flags", [
+    (3, 72, 8, 14, 3, 4, 1, 1, True, 3),      # whole-sample kernel: partial tile of 8 rows, pad and swap
+    (2, 16, 4, 8, 2, 4, 1, 0, True, 3),       # the same shape through both kernels
+    (2, 24, 16, 21, 1, 4, 3, 0, True, 0),     # causal conv (lag 0), N = 16
+])
+@pytest.mark.parametrize("chunked", [False, True])
+def test_bwd_kernels_f32(B, D, N, T, B2, K, P, act, sp, flags, chunked, monkeypatch):
+    """Both backward kernels (whole-sample staging and chunk by chunk) on the same cases."""
+    if chunked:
+        monkeypatch.setenv("SFM_BWD_CHUNKED", "1")
+    run_case(B=B, D=D, N=N, T=T, B2=B2, K=K, P=P, act=act, softplus=sp, flags=flags, io="f32", seed=B * 5 + T)
+
+
+def test_bwd_stage4_bf16_chunked(monkeypatch):
+    """The chunked kernel at the stage-4 shape (the default plan stages whole samples there)."""
+    monkeypatch.setenv("SFM_BWD_CHUNKED", "1")
+    run_case(B=64, D=640, N=8, T=49, B2=2, K=4, P=1, act=0, softplus=True, flags=3, io="bf16", seed=12)
+
+
 def test_bwd_no_conv_f32():
     run_case(B=3, D=16, N=4, T=10, B2=1, K=1, P=0, act=0, softplus=True, flags=0, io="f32", seed=5,
              use_conv=False)
