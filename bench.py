@@ -242,7 +242,12 @@ def main():
                          "copy: a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (pad, conv+scan, swap) instead of one")
+    ap.add_argument("--layout", choices=["bdl", "bld"], default="bdl",
+                    help="bdl: channel-first [B, D, L] (default); bld: channel-last [B, L, D] activations and "
+                         "[B, L, N] B/C (fused step only)")
     a = ap.parse_args()
+    if a.layout == "bld" and (a.mode != "step" or a.unfused):
+        raise SystemExit("--layout bld times the fused step only")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -295,13 +300,16 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
 
     base = {"x": dev_io(li.x), "delta": dev_io(li.delta), "Bm": dev_io(li.Bm), "Cm": dev_io(li.Cm)}
+    cl = a.layout == "bld"
+    if cl:  # channel-last copies of the same values (outside the timed region)
+        base = {k: v.transpose(1, 2).contiguous() for k, v in base.items()}
     prm = {k: torch.from_numpy(getattr(li, k)).to(dev) for k in ("A", "Dskip", "delta_bias", "conv_w")}
     set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + 2 * w.B * w.D * w.L * io_bytes
     nsets = a.sets if a.sets > 0 else max(2, math.ceil((2 << 30) / set_bytes))
     sets = []
     for _ in range(nsets):
         s = {k: v.clone() for k, v in base.items()}
-        s["xp"] = torch.empty((w.B, w.D, w.L), dtype=base["x"].dtype, device=dev)
+        s["xp"] = torch.empty((w.B, w.L, w.D) if cl else (w.B, w.D, w.L), dtype=base["x"].dtype, device=dev)
         s["y"] = torch.empty_like(s["xp"])
         sets.append(s)
     torch.cuda.synchronize()
@@ -320,7 +328,7 @@ def main():
         scan_in = s["x"] if fused else s["xp"]
         scan_args = (vp(scan_in), vp(s["delta"]), vp(prm["A"]), vp(s["Bm"]), vp(s["Cm"]), vp(prm["Dskip"]),
                      vp(prm["delta_bias"]), 1, vp(prm["conv_w"]), None, w.K, 1, 0, vp(s["y"]),
-                     w.B // b2, b2, w.D, w.N, w.L, io, 3 if fused else 0, sp)
+                     w.B // b2, b2, w.D, w.N, w.L, io, (3 | (4 if cl else 0)) if fused else 0, sp)
         swap_args = (vp(s["y"]), vp(s["y"]), w.B, w.D, w.L - 2, 1, io, sp)
         calls.append((pad_args, scan_args, swap_args))
     b1_out = ctypes.c_int64()
@@ -384,10 +392,13 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(hbm_frac, 4)}
-    roof["traffic"] = traffic
+    roof["traffic"] = None if cl else traffic
     roof["kernel"] = ("sfm scan_kernel (aux pad + boundary-masked conv + folded segmented scan + aux swap, "
                       "one launch)" if fused else "sfm scan_kernel (conv + folded segmented scan)")
-    roof["plan"] = sfm.sfm_scan_plan_string(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, 3 if fused else 0)
+    if cl:
+        roof["kernel"] = "sfm scan_cl_kernel (channel-last; aux pad + conv + folded segmented scan + aux swap)"
+    roof["plan"] = sfm.sfm_scan_plan_string(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io,
+                                            (3 | (4 if cl else 0)) if fused else 0)
     roof["kernel_ms_avg"] = round(scan_avg, 5)
     roof["kernel_ms_median"] = round(scan_med, 5)
     roof["alg_bytes_per_launch"] = sbytes
@@ -407,6 +418,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 + Box-Muller, stage-shaped)",
         "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}",
                    "B2": b2, "B1": w.B // b2, "mode": a.mode, "input_sets": nsets,
+                   "layout": "channel-last [B, L, D]" if cl else "channel-first [B, D, L]",
                    "step": ("pick_b1 + one launch of pad/conv/scan/swap" if fused else
                             "pick_b1 + pad + conv/scan + swap (3 launches)") if a.mode == "step" else "scan only"},
         "roofline": roof,

@@ -124,10 +124,18 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
  * Results are bit-identical to the unfused sequence pad -> scan -> swap.  With
  * either flag the launch keeps every sample inside one wave (no carried state),
  * so very long single-sample rows run with less parallelism.
+ *   flags & SFM_LAYOUT_BLD: channel-last layout ("SF-Mamba" README and the
+ *       pages' per-model choice of the faster of channel-first and channel-last):
+ *       u, delta, y are [B1*B2, L, D] (u [B1*B2, L-2, D] with SFM_FUSE_PAD),
+ *       Bm, Cm [B1*B2, L, N]; every element has the same value as in the
+ *       channel-first call on the transposed tensors, bit for bit.  D times the
+ *       io element size must be a multiple of 16 bytes (else SFM_ERR_SHAPE).
+ *       Override (diagnostics): SFM_CL_CHUNK=w caps the positions staged at once.
  * Other arguments as sfm_selective_scan_fwd; flags = 0 is that function.
  */
 #define SFM_FUSE_PAD 1
 #define SFM_FUSE_SWAP 2
+#define SFM_LAYOUT_BLD 4
 sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* Bm,
                                      const void* Cm, const float* Dskip, const float* delta_bias,
                                      int delta_softplus, const float* conv_w, const float* conv_b,

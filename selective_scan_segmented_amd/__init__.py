@@ -121,7 +121,7 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-SFM_FUSE_PAD, SFM_FUSE_SWAP = 1, 2
+SFM_FUSE_PAD, SFM_FUSE_SWAP, SFM_LAYOUT_BLD = 1, 2, 4
 
 
 def sfm_selective_scan_fwd(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, delta_softplus=True,
@@ -141,19 +141,26 @@ def sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, 
                               conv_w=None, conv_b=None, conv_pad_left=1, conv_act=None, y=None, B2=1,
                               flags=0, stream=None):
     """sfm_selective_scan_fwd with the aux pad (flags & SFM_FUSE_PAD: u is the unpadded
-    [B, D, L-2] stage input) and/or the aux swap of y (flags & SFM_FUSE_SWAP) fused in."""
+    [B, D, L-2] stage input) and/or the aux swap of y (flags & SFM_FUSE_SWAP) fused in.
+    flags & SFM_LAYOUT_BLD: channel-last tensors, u/delta/y [B, L, D] (u [B, L-2, D] with
+    the pad), Bm/Cm [B, L, N]."""
     torch = _torch()
     io = _io_code(u)
-    B, D, XL = u.shape
+    cl = bool(flags & SFM_LAYOUT_BLD)
+    if cl:
+        B, XL, D = u.shape
+    else:
+        B, D, XL = u.shape
     L = XL + 2 if flags & SFM_FUSE_PAD else XL
     N = A.shape[1]
     if B % B2:
         raise ValueError(f"B2={B2} must divide B={B}")
+    tl = (lambda a, b_: (B, b_, a)) if cl else (lambda a, b_: (B, a, b_))  # [B, a, b] in this layout
     _dev(u, "u")
-    _dev(delta, "delta", u.dtype, (B, D, L))
+    _dev(delta, "delta", u.dtype, tl(D, L))
     _dev(A, "A", torch.float32, (D, N))
-    _dev(Bm, "Bm", u.dtype, (B, N, L))
-    _dev(Cm, "Cm", u.dtype, (B, N, L))
+    _dev(Bm, "Bm", u.dtype, tl(N, L))
+    _dev(Cm, "Cm", u.dtype, tl(N, L))
     _dev(Dskip, "Dskip", torch.float32, (D,))
     _dev(delta_bias, "delta_bias", torch.float32, (D,))
     K = 0
@@ -164,8 +171,8 @@ def sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, 
         K = conv_w.shape[1]
         _dev(conv_b, "conv_b", torch.float32, (D,))
     if y is None:
-        y = torch.empty((B, D, L), dtype=u.dtype, device=u.device)
-    _dev(y, "y", u.dtype, (B, D, L))
+        y = torch.empty(tl(D, L), dtype=u.dtype, device=u.device)
+    _dev(y, "y", u.dtype, tl(D, L))
     rc = load_library().sfm_selective_scan_fwd_ex(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(delta_bias), int(bool(delta_softplus)),
         _ptr(conv_w), _ptr(conv_b), K, int(conv_pad_left), _ACT[conv_act], _ptr(y),

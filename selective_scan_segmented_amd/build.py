@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsfm.so")
-SOURCES = ["scan.hip", "conv.hip", "aux.hip", "bwd.hip", "sfm_api.cpp"] + [
+SOURCES = ["scan.hip", "scan_cl.hip", "conv.hip", "aux.hip", "bwd.hip", "sfm_api.cpp"] + [
     f"scan_{io}_n{n}.hip" for io in ("f32", "bf16") for n in (4, 8, 16)]
 ARCH = os.environ.get("SFM_OFFLOAD_ARCH", "gfx950")
 

@@ -97,7 +97,7 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
                                      int64_t N, int64_t L, int io_dtype, int flags, void* stream) {
     if (!u || !delta || !A || !Bm || !Cm || !y)
         return fail(SFM_ERR_NULL, "sfm_selective_scan_fwd: u, delta, A, Bm, Cm and y are required");
-    if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP))
+    if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP | SFM_LAYOUT_BLD))
         return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd_ex: unknown flags 0x%x", flags);
     const bool pad_in = (flags & SFM_FUSE_PAD) != 0;
     if (pad_in && L < 3)
@@ -136,6 +136,38 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
     for (const Range& r : ins)
         if (overlap(ry, r)) return fail(SFM_ERR_ALIAS, "sfm_selective_scan_fwd: y overlaps %s", r.name);
 
+    if (flags & SFM_LAYOUT_BLD) {
+        sfm::ClParams c{};
+        c.u = u;
+        c.delta = delta;
+        c.A = A;
+        c.Bm = Bm;
+        c.Cm = Cm;
+        c.Dskip = Dskip;
+        c.dbias = delta_bias;
+        c.conv_w = conv_w;
+        c.conv_b = conv_w ? conv_b : nullptr;
+        c.y = y;
+        c.B1 = (int)B1;
+        c.B2 = (int)B2;
+        c.D = (int)D;
+        c.N = (int)N;
+        c.L = (int)L;
+        c.K = conv_w ? conv_k : 1;
+        c.P = conv_w ? conv_pad_left : 0;
+        c.act = conv_w ? conv_act : 0;
+        c.softplus = delta_softplus;
+        c.pad_in = pad_in ? 1 : 0;
+        c.swap_out = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+        c.xrow = (int)XL;
+        int w_hint = 0;
+        if (const char* e = std::getenv("SFM_CL_CHUNK")) w_hint = std::atoi(e);
+        if (!sfm::plan_scan_cl(c, eb, w_hint))
+            return fail(SFM_ERR_SHAPE, "sfm_selective_scan_fwd_ex: channel-last rows of D=%lld channels must be whole "
+                                       "16-byte units", (long long)D);
+        return hip_status(sfm::launch_scan_cl(c, io_dtype, static_cast<hipStream_t>(stream)),
+                          "sfm_selective_scan_fwd_ex");
+    }
     sfm::ScanParams p{};
     p.u = u;
     p.delta = delta;
@@ -176,8 +208,31 @@ sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, in
     if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24) || N < 1 ||
         N > SFM_MAX_N || conv_k < 0 || conv_k > SFM_MAX_K)
         return fail(SFM_ERR_SHAPE, "sfm_scan_plan_string: sizes out of range");
-    sfm::ScanParams p{};
     static const float dummy = 0.0f;
+    if (flags & SFM_LAYOUT_BLD) {
+        if ((flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP | SFM_LAYOUT_BLD)) || ((flags & SFM_FUSE_PAD) && L < 3))
+            return fail(SFM_ERR_SHAPE, "sfm_scan_plan_string: bad flags for these sizes");
+        sfm::ClParams c{};
+        c.conv_w = conv_k ? &dummy : nullptr;
+        c.B1 = (int)B1;
+        c.B2 = (int)B2;
+        c.D = (int)D;
+        c.N = (int)N;
+        c.L = (int)L;
+        c.K = conv_k ? conv_k : 1;
+        c.pad_in = (flags & SFM_FUSE_PAD) ? 1 : 0;
+        c.swap_out = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+        c.xrow = c.pad_in ? (int)L - 2 : (int)L;
+        int w_hint = 0;
+        if (const char* e = std::getenv("SFM_CL_CHUNK")) w_hint = std::atoi(e);
+        if (!sfm::plan_scan_cl(c, io_bytes(io_dtype), w_hint))
+            return fail(SFM_ERR_SHAPE, "sfm_scan_plan_string: channel-last rows must be whole 16-byte units");
+        snprintf(buf, (size_t)cap, "layout=bld chunk=%d chunks=%d ns=%d cw=%d lds=%d grid=%d block=%d stagger=%d/%d",
+                 c.W, c.nchunk, c.ns, c.cw, c.lds_bytes, c.B1 * c.tgroups, 64 * c.cw, c.stagger_ticks,
+                 c.stagger_period);
+        return ok();
+    }
+    sfm::ScanParams p{};
     p.conv_w = conv_k ? &dummy : nullptr;
     p.B1 = (int)B1;
     p.B2 = (int)B2;
