@@ -226,6 +226,57 @@ def run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io):
     }))
 
 
+def run_block(a, w, hip, sp, dev):
+    """Mixer-block forward (random-weight projection GEMMs around the channel-last
+    scan launch) at several fold ratios B2: block time, the scan's share of it."""
+    import torch
+
+    import selective_scan_segmented_amd as sfm
+    from selective_scan_segmented_amd import block, synth
+    C = w.D // 2                   # model width: expand factor 2 to the scan's D channels
+    R = math.ceil(C / 16)          # rank of the step projection
+    bi = synth.make_block(B=w.B, T=w.T, C=C, D=w.D, N=w.N, K=w.K, R=R, io=w.io, seed=11)
+    blk = block.MixerBlock(bi, device=dev)
+    pick = w.B // sfm.sfm_pick_b1(w.B, w.L, w.D, w.N)
+    b2s = [pick] + [b for b in (1, 2, 4, 8, 16) if b != pick and w.B % b == 0]
+    rows = []
+    for b2 in b2s:
+        for _ in range(a.warmup):
+            blk.forward(B2=b2)
+        torch.cuda.synchronize()
+        K = a.steps
+        sev = [(hip.event(), hip.event()) for _ in range(K)]
+        t0, t1 = hip.event(), hip.event()
+        hip.record(t0, sp)
+        for i in range(K):
+            blk.forward(B2=b2, scan_events=(lambda e=sev[i][0]: hip.record(e, sp),
+                                            lambda e=sev[i][1]: hip.record(e, sp)))
+        hip.record(t1, sp)
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(t0, t1) / K
+        scan_ms = sum(hip.elapsed_ms(e0, e1) for e0, e1 in sev) / K
+        rows.append({"B2": b2, "ms_per_block": round(ms, 5), "scan_ms": round(scan_ms, 5),
+                     "scan_share": round(scan_ms / ms, 3)})
+    base = next(r for r in rows if r["B2"] == 1)
+    for r in rows:
+        r["speedup_vs_B2_1"] = round(base["ms_per_block"] / r["ms_per_block"], 3)
+    top = rows[0]
+    tc = w.B * w.L * w.D
+    flops = block.gemm_flops(bi)
+    print(json.dumps({
+        "metric": "mixer-block forward, token*channels/s (scan channels, T+2 aux tokens counted)",
+        "value": tc / (top["ms_per_block"] * 1e-3), "unit": "token*channels/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": top["ms_per_block"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.io, "data": "synthetic (seeded random weights and tokens)",
+        "config": {"workload": f"{w.name} mixer block: B={w.B} L={w.L} C={C} D={w.D} N={w.N} K={w.K} R={R}",
+                   "mode": "block", "B2": top["B2"], "layout": "channel-last [B, L, D]",
+                   "step": "6 projection GEMMs + one fused conv/scan launch + silu gate + out-projection GEMM"},
+        "gemm_flops_per_block": flops,
+        "gemm_TFLOPs_outside_scan": round(flops / ((top["ms_per_block"] - top["scan_ms"]) * 1e-3) / 1e12, 1),
+        "b2_sweep": rows,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,9 +287,10 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets; 0 = enough for 2 GiB")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy", "scan", "bwd"], default="step",
+    ap.add_argument("--mode", choices=["step", "copy", "scan", "bwd", "block"], default="step",
                     help="step: the whole hot path (default); scan: the scan launch alone; "
                          "bwd: the backward of the fused step (one sfm_selective_scan_bwd call); "
+                         "block: a random-weight mixer block around the channel-last scan, per fold ratio; "
                          "copy: a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (pad, conv+scan, swap) instead of one")
@@ -287,6 +339,9 @@ def main():
         return
 
     w = synth.WORKLOADS[a.workload]
+    if a.mode == "block":
+        run_block(a, w, hip, sp, dev)
+        return
     io_bytes = 4 if w.io == "f32" else 2
     B1 = sfm.sfm_pick_b1(w.B, w.L, w.D, w.N)
     b2 = a.b2 if a.b2 > 0 else w.B // B1

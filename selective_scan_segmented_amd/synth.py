@@ -168,3 +168,38 @@ def make_layer(w: Workload, seed: int, layer: int = 0, a_mode: str = "structured
         raise ValueError(a_mode)
     return LayerInputs(io=w.io, x=x, delta=delta, Bm=Bm, Cm=Cm, A=A.astype(np.float32),
                        Dskip=np.ones(D, dtype=np.float32), delta_bias=delta_bias, conv_w=conv_w)
+
+
+# ---------------------------------------------------------------- mixer block
+STREAM_BLOCK = 32  # first sub-stream of the mixer-block draws (independent of the layer draws)
+
+
+class BlockInputs:
+    """Random-weight mixer block around one scan layer, channel-last.  io arrays are
+    float32 (f32 io) or uint16 bf16 bit patterns; A, Dskip, delta_bias, conv_w float32.
+
+    X [B, L, C] is the (already padded) stage token sequence; W_x, W_z [C, D] give
+    the scan input and the gate, W_b, W_c [C, N] give B and C, W_dt1 [C, R] and
+    W_dt2 [R, D] the low-rank step input, W_out [D, C] the output projection.
+    Weights are N(0, 1) / sqrt(fan_in)."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def make_block(B: int, T: int, C: int, D: int, N: int, K: int, R: int, io: str, seed: int) -> BlockInputs:
+    L = T + 2
+    s = STREAM_BLOCK
+    g = lambda k, n, scale=1.0: normal(seed, s + k, n) * scale
+    X = _io_cast(g(0, B * L * C), io).reshape(B, L, C)
+    W = {}
+    for k, (name, rows, cols) in enumerate([("W_x", C, D), ("W_z", C, D), ("W_b", C, N), ("W_c", C, N),
+                                             ("W_dt1", C, R), ("W_dt2", R, D), ("W_out", D, C)]):
+        W[name] = _io_cast(g(1 + k, rows * cols, 1.0 / math.sqrt(rows)), io).reshape(rows, cols)
+    u = uniform53(seed, s + 8, D)
+    dt0 = np.exp(math.log(1e-3) + u * (math.log(1e-1) - math.log(1e-3)))
+    return BlockInputs(io=io, B=B, T=T, L=L, C=C, D=D, N=N, K=K, R=R, X=X, **W,
+                       A=-np.tile(np.arange(1, N + 1, dtype=np.float32), (D, 1)),
+                       Dskip=np.ones(D, dtype=np.float32),
+                       delta_bias=np.log(np.expm1(dt0)).astype(np.float32),
+                       conv_w=(uniform53(seed, s + 9, D * K) - 0.5).astype(np.float32).reshape(D, K))
