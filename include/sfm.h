@@ -175,11 +175,12 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  *   dDskip, ddelta_bias [D] f32 or NULL (not computed)
  *   dconv_w     [D, conv_k] f32 (required with conv_w);  dconv_b [D] f32 or NULL
  * workspace: device memory of at least sfm_selective_scan_bwd_workspace_size()
- *   bytes, owned by the caller, not overlapping anything else; it holds float32
- *   state checkpoints (every 32/Np positions, Np = N rounded up to 4, 8 or 16)
- *   for the duration of the call.  The library allocates nothing.  The f32
- *   sums are accumulated with atomics, so their summation order (and last
- *   bits) may vary between runs.
+ *   bytes (same B1, B2, D, N, L, conv_k -- 0 without conv -- io_dtype, flags),
+ *   owned by the caller, not overlapping anything else; it holds float32 state
+ *   checkpoints (every 32/Np positions, Np = N rounded up to 4, 8 or 16) and
+ *   the partial sums of the f32 outputs for the duration of the call.  The
+ *   library allocates nothing.  The f32 sums are added in a fixed order by a
+ *   second kernel (no atomics), so repeated calls give identical bits.
  * Two kernels: when every [rows][length] block of a sample and 64-channel tile
  * is a whole number of 16-byte units on 16-byte boundaries and fits in LDS,
  * each sample is staged once; otherwise chunk by chunk.  Environment override

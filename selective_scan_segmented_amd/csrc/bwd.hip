@@ -346,7 +346,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                         const float4 v4 = row[m];
                         s += (v4.x + v4.y) + (v4.z + v4.w);
                     }
-                    if (lane < 2 * NS * R && n < N && r0 + ii < cnt) atomicAdd((k < NS ? p.dBm : p.dCm) + ((size_t)b * N + n) * L + t, s);
+                    if (lane < 2 * NS * R && r0 + ii < cnt)
+                        p.ws[p.pbc_off + (((size_t)tile * p.B1 * p.B2 + b) * L + t) * 2 * NS + k] = s;
                 }
                 wave_lds_sync();
             }
@@ -379,16 +380,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         }
     }
     if (valid) {
+        // this folded row's per-channel sums (rows dA[0..N), dD, dbias, dconv_b, dconv_w[0..K))
+        float* pc = p.ws + p.pch_off + (size_t)b1 * p.kc * p.D + d;
 #pragma unroll
         for (int n = 0; n < NS; ++n)
-            if (n < N) atomicAdd(p.dA + (size_t)d * N + n, gA[n]);
-        if (p.dDskip) atomicAdd(p.dDskip + d, gD);
-        if (p.ddbias) atomicAdd(p.ddbias + d, gb);
+            if (n < N) pc[(size_t)n * p.D] = gA[n];
+        pc[(size_t)N * p.D] = gD;
+        pc[(size_t)(N + 1) * p.D] = gb;
         if constexpr (CONV) {
+            pc[(size_t)(N + 2) * p.D] = gcb;
 #pragma unroll
             for (int jj = 0; jj < KW; ++jj)
-                if (jj < p.K && p.dconv_w) atomicAdd(p.dconv_w + (size_t)d * p.K + jj, gw[jj]);
-            if (p.dconv_b) atomicAdd(p.dconv_b + d, gcb);
+                if (jj < p.K) pc[(size_t)(N + 3 + jj) * p.D] = gw[jj];
         }
     }
 }
@@ -718,8 +721,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                         s += (v4.x + v4.y) + (v4.z + v4.w);
                     }
                     s += __shfl_xor(s, 32);
-                    if (lane < 32 && n < N && r0 + ii < cnt)
-                        atomicAdd((k < NS ? p.dBm : p.dCm) + ((size_t)b * N + n) * L + t0 + r0 + ii, s);
+                    if (lane < 32 && r0 + ii < cnt)
+                        p.ws[p.pbc_off + (((size_t)tile * p.B1 * p.B2 + b) * L + t0 + r0 + ii) * 2 * NS + k] = s;
                 }
                 wave_lds_sync();
             }
@@ -747,31 +750,72 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         }
     }
     if (valid) {
+        // this folded row's per-channel sums (rows dA[0..N), dD, dbias, dconv_b, dconv_w[0..K))
+        float* pc = p.ws + p.pch_off + (size_t)b1 * p.kc * p.D + d;
 #pragma unroll
         for (int n = 0; n < NS; ++n)
-            if (n < N) atomicAdd(p.dA + (size_t)d * N + n, gA[n]);
-        if (p.dDskip) atomicAdd(p.dDskip + d, gD);
-        if (p.ddbias) atomicAdd(p.ddbias + d, gb);
+            if (n < N) pc[(size_t)n * p.D] = gA[n];
+        pc[(size_t)N * p.D] = gD;
+        pc[(size_t)(N + 1) * p.D] = gb;
         if constexpr (CONV) {
+            pc[(size_t)(N + 2) * p.D] = gcb;
 #pragma unroll
             for (int jj = 0; jj < KW; ++jj)
-                if (jj < p.K && p.dconv_w) atomicAdd(p.dconv_w + (size_t)d * p.K + jj, gw[jj]);
-            if (p.dconv_b) atomicAdd(p.dconv_b + d, gcb);
+                if (jj < p.K) pc[(size_t)(N + 3 + jj) * p.D] = gw[jj];
         }
     }
 }
 
-// Zeroes up to eight float32 arrays in one launch (the sums the backward adds into).
-struct ZeroList {
-    float* p[8];
-    unsigned long long n[8];
-    int count;
-};
+// The float32 sums from the partials, each added in a fixed order.  Blocks
+// [0, nb_bc): dB/dC[b, n, t] over the channel tiles (ascending).  Blocks from
+// nb_bc on: the per-channel sums over the folded rows, 16 outputs per block,
+// each split over 16 threads (thread k adds rows b1 = k, k + 16, ... in order)
+// whose results are then added k = 0 .. 15.  Every output element is written.
+constexpr int kRedOut = 16;  // per-channel outputs per block (and threads per output)
 
-__global__ void zero_kernel(ZeroList z) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (int k = 0; k < z.count; ++k)
-        for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < z.n[k]; i += stride) z.p[k][i] = 0.0f;
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int nb_bc) {
+    const int ns = p.ns, L = p.L, N = p.N, D = p.D;
+    const size_t B = (size_t)p.B1 * p.B2;
+    if ((int)blockIdx.x < nb_bc) {
+        const size_t nbc = B * L * 2 * ns;  // partial dB/dC values per channel tile
+        const float* pbc = p.ws + p.pbc_off;
+        for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < nbc;
+             idx += (size_t)nb_bc * blockDim.x) {
+            const int n = (int)(idx % ns);
+            size_t r = idx / ns;
+            const int c = (int)(r % 2);
+            r /= 2;
+            const int t = (int)(r % L);
+            const size_t b = r / L;
+            if (n >= N) continue;
+            float s = 0.0f;
+            for (int tl = 0; tl < p.tiles; ++tl) s += pbc[(size_t)tl * nbc + idx];
+            (c ? p.dCm : p.dBm)[(b * N + n) * L + t] = s;
+        }
+        return;
+    }
+    __shared__ float part[kRedOut][kRedOut + 1];
+    const float* pch = p.ws + p.pch_off;
+    const int oo = threadIdx.x % kRedOut;
+    const int k = threadIdx.x / kRedOut;
+    const long long o = (long long)((int)blockIdx.x - nb_bc) * kRedOut + oo;  // output: row * D + d
+    const bool live = o < (long long)p.kc * D;
+    const int row = live ? (int)(o / D) : 0;
+    const int d = live ? (int)(o % D) : 0;
+    float s = 0.0f;
+    if (live)
+        for (int b1 = k; b1 < p.B1; b1 += kRedOut) s += pch[((size_t)b1 * p.kc + row) * D + d];
+    part[k][oo] = s;
+    __syncthreads();
+    if (k == 0 && live) {
+        float t = 0.0f;
+        for (int m = 0; m < kRedOut; ++m) t += part[m][oo];
+        if (row < N) p.dA[(size_t)d * N + row] = t;
+        else if (row == N) { if (p.dDskip) p.dDskip[d] = t; }
+        else if (row == N + 1) { if (p.ddbias) p.ddbias[d] = t; }
+        else if (row == N + 2) { if (p.dconv_b) p.dconv_b[d] = t; }
+        else p.dconv_w[(size_t)d * p.K + (row - N - 3)] = t;  // rows past N + 1 exist only with the conv
+    }
 }
 
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
@@ -815,7 +859,14 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     p.tiles = (p.D + kWave - 1) / kWave;
     p.q = kHist / p.ns;
     p.nchk = (p.L + p.q - 1) / p.q;
-    *ws_bytes = (size_t)p.B1 * p.tiles * p.nchk * p.ns * kWave * sizeof(float);
+    p.kc = p.N + 2 + (p.conv_w ? 1 + p.K : 0);  // rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
+    auto up64 = [](long long v) { return (v + 63) & ~63LL; };  // 256-byte aligned regions
+    const long long ck = (long long)p.B1 * p.tiles * p.nchk * p.ns * kWave;
+    const long long pbc = (long long)p.tiles * p.B1 * p.B2 * p.L * 2 * p.ns;
+    const long long pch = (long long)p.B1 * p.kc * p.D;
+    p.pbc_off = up64(ck);
+    p.pch_off = p.pbc_off + up64(pbc);
+    *ws_bytes = (size_t)(p.pch_off + up64(pch)) * sizeof(float);
     auto up16 = [](long long v) { return (int)((v + 15) & ~15LL); };
     // Whole-sample staging: every [rows][length] block (x, delta, dy, ddelta, du)
     // of every sample and tile must start on 16 bytes and span whole 16-byte
@@ -869,30 +920,13 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t s) {
-    const size_t B = (size_t)p.B1 * p.B2;
-    ZeroList z{};
-    size_t most = 0;
-    auto add = [&](float* a, size_t n) {
-        if (!a || n == 0) return;
-        z.p[z.count] = a;
-        z.n[z.count++] = n;
-        most = std::max(most, n);
-    };
-    add(p.dA, (size_t)p.D * p.N);
-    add(p.dBm, B * p.N * p.L);
-    add(p.dCm, B * p.N * p.L);
-    add(p.dDskip, p.D);
-    add(p.ddbias, p.D);
-    if (p.conv_w) {
-        add(p.dconv_w, (size_t)p.D * p.K);
-        add(p.dconv_b, p.D);
-    }
-    const unsigned blocks = (unsigned)std::min<size_t>(1024, (most + 255) / 256);
-    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, z);
-    hipError_t e = hipGetLastError();
+    hipError_t e = io_dtype == 0 ? launch_bio<float>(p, s) : launch_bio<__bf16>(p, s);
     if (e != hipSuccess) return e;
-    if (io_dtype == 0) return launch_bio<float>(p, s);
-    return launch_bio<__bf16>(p, s);
+    const size_t nbc = (size_t)p.B1 * p.B2 * p.L * 2 * p.ns;
+    const int nb_bc = (int)std::min<size_t>(2048, (nbc + 255) / 256);
+    const size_t nb_ch = ((size_t)p.kc * p.D + kRedOut - 1) / kRedOut;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(nb_bc + nb_ch)), dim3(256), 0, s, p, nb_bc);
+    return hipGetLastError();
 }
 
 }  // namespace sfm

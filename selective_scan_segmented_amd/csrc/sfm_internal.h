@@ -66,7 +66,7 @@ struct BwdParams {
     float* ddbias;        // [D] or null
     float* dconv_w;       // [D, K] or null
     float* dconv_b;       // [D] or null
-    float* ws;            // checkpoints: [B1 * tiles][nchk][ns][64] float32
+    float* ws;            // workspace: checkpoints [B1 * tiles][nchk][ns][64], then the partial sums below
     int B1, B2, D, N, L;
     int K, P, act, softplus;
     int pad_in;           // u holds unpadded rows of L-2 tokens
@@ -75,6 +75,11 @@ struct BwdParams {
     // plan
     int ns, tiles, q, nchk;
     int whole;            // 1: whole-sample slabs staged once per sample; 0: chunk by chunk
+    // partial sums in the workspace (offsets in floats), added up in a fixed order
+    // by a second kernel: dB/dC per channel tile [tiles][B][L][2][ns] and the
+    // per-channel sums per folded row [B1][kc][D], rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
+    long long pbc_off, pch_off;
+    int kc;
     int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, braw_off, lds_bytes;
 };
 

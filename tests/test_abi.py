@@ -153,16 +153,30 @@ def test_bwd_validation(lib):
     assert b"workspace" in lib.sfm_last_error()
 
 
+def ws_expect(B1, B2, D, N, L, K):
+    """Workspace floats, each region rounded up to 64: state checkpoints per (folded row,
+    channel tile, chunk of 32/Np positions, state, lane); partial dB/dC per (tile, sample,
+    position, B|C, state); per-channel partial sums per (folded row, row, channel) with
+    rows dA (N), dD, dbias and, with the conv, dconv_b and dconv_w (K)."""
+    ns = 4 if N <= 4 else (8 if N <= 8 else 16)
+    tiles, q = (D + 63) // 64, 32 // ns
+    up = lambda v: (v + 63) // 64 * 64
+    kc = N + 2 + (1 + K if K else 0)
+    return 4 * (up(B1 * tiles * ((L + q - 1) // q) * ns * 64) + up(tiles * B1 * B2 * L * 2 * ns) + up(B1 * kc * D))
+
+
 def test_bwd_workspace_size(lib):
     out = ctypes.c_int64(0)
     f = lib.sfm_selective_scan_bwd_workspace_size
     assert f(2, 2, 4, 4, 10, 4, 0, 0, ctypes.byref(out)) == OK
-    # one float32 state checkpoint per (row, channel tile, chunk, state, lane): chunks of 32/Np positions
-    assert out.value == 2 * 1 * ((10 + 7) // 8) * 4 * 64 * 4
+    assert out.value == ws_expect(2, 2, 4, 4, 10, 4)
+    assert f(2, 2, 4, 4, 10, 0, 0, 0, ctypes.byref(out)) == OK
+    assert out.value == ws_expect(2, 2, 4, 4, 10, 0)
     assert f(2, 2, 4, 4, 10, 4, 0, 0, None) == NULL
     assert f(2, 2, 4, 0, 10, 4, 0, 0, ctypes.byref(out)) == SHAPE
     assert f(2, 2, 4, 4, 10, 4, 9, 0, ctypes.byref(out)) == DTYPE
-    assert sfm.sfm_selective_scan_bwd_workspace_size(256, 1, 640, 8, 51, 4, "bf16", 3) == 256 * 10 * 13 * 8 * 64 * 4
+    assert sfm.sfm_selective_scan_bwd_workspace_size(256, 1, 640, 8, 51, 4, "bf16", 3) == \
+        ws_expect(256, 1, 640, 8, 51, 4)
 
 
 def test_aux_pad_bwd_validation(lib):

@@ -173,3 +173,14 @@ def test_bwd_workspace_too_small():
     with pytest.raises(sfm.SFMError):
         sfm.sfm_selective_scan_bwd(z(B, D, L), z(B, D, L), z(D, N), z(B, N, L), z(B, N, L), z(B, D, L),
                                    conv_w=z(D, 4), workspace=torch.zeros(16, dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("chunked", [False, True])
+def test_bwd_repeatable(chunked, monkeypatch):
+    """The float32 sums are added in a fixed order: two calls give the same bits."""
+    if chunked:
+        monkeypatch.setenv("SFM_BWD_CHUNKED", "1")
+    g1, _ = run_case(B=8, D=192, N=8, T=14, B2=2, K=4, P=1, act=0, softplus=True, flags=3, io="bf16", seed=21)
+    g2, _ = run_case(B=8, D=192, N=8, T=14, B2=2, K=4, P=1, act=0, softplus=True, flags=3, io="bf16", seed=21)
+    for k in ("du", "ddelta", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dconv_w"):
+        assert np.array_equal(from_dev(g1[k]), from_dev(g2[k])), k
