@@ -16,6 +16,7 @@
 // SWAP: in place it touches only the two end tokens of every row; out of place
 // it is a coalesced copy with the two ends exchanged.
 #include "sfm_device.h"
+#include "sfm_bwd.h"
 #include "sfm_internal.h"
 
 namespace sfm {

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "sfm_device.h"
+#include "sfm_bwd.h"
 #include "sfm_internal.h"
 
 namespace sfm {

@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "sfm_device.h"
+#include "sfm_cl.h"
 #include "sfm_internal.h"
 
 namespace sfm {

@@ -13,6 +13,8 @@
 #include <string>
 #include <vector>
 
+#include "sfm_bwd.h"
+#include "sfm_cl.h"
 #include "sfm_internal.h"
 
 namespace {

@@ -1,0 +1,54 @@
+// sfm_bwd.h -- host/device contract of the backward kernels (bwd.hip, and the
+// aux-pad gradient in aux.hip) and the C-ABI layer.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfm {
+
+// Launch description of one backward call (see bwd.hip).
+struct BwdParams {
+    const void* u;        // conv input x (unpadded with pad_in), or the scan input without conv
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const float* dbias;
+    const float* conv_w;
+    const float* conv_b;
+    const void* dy;
+    void* du;             // gradient of the (padded) conv input, [B, D, L] io
+    void* ddelta;         // [B, D, L] io
+    float* dA;            // [D, N]
+    float* dBm;           // [B, N, L]
+    float* dCm;           // [B, N, L]
+    float* dDskip;        // [D] or null
+    float* ddbias;        // [D] or null
+    float* dconv_w;       // [D, K] or null
+    float* dconv_b;       // [D] or null
+    float* ws;            // workspace: checkpoints [B1 * tiles][nchk][ns][64], then the partial sums below
+    int B1, B2, D, N, L;
+    int K, P, act, softplus;
+    int pad_in;           // u holds unpadded rows of L-2 tokens
+    int swap_dy;          // dy is the gradient of the output with positions 0 and L-1 exchanged
+    int xrow;             // row length of u
+    // plan
+    int ns, tiles, q, nchk;
+    int whole;            // 1: whole-sample slabs staged once per sample; 0: chunk by chunk
+    // partial sums in the workspace (offsets in floats), added up in a fixed order
+    // by a second kernel: dB/dC per channel tile [tiles][B][L][2][ns] and the
+    // per-channel sums per folded row [B1][kc][D], rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
+    long long pbc_off, pch_off;
+    int kc;
+    int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, braw_off, lds_bytes;
+};
+
+// Backward planning; returns false when no plan fits.  ws_bytes: workspace size.
+bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes);
+hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t stream);
+
+hipError_t launch_aux_pad_bwd(const void* gp, void* gx, int64_t rows, int64_t T, int io_dtype, hipStream_t stream);
+
+}  // namespace sfm
