@@ -80,10 +80,17 @@ class Hip:
 
 
 def scan_source_hash() -> str:
+    """Hash of the code (comments and whitespace removed) of the files that
+    define the channel-first scan kernel: counters taken on one version of that
+    code stay valid across comment-only edits and no longer apply after any
+    other change."""
     h = hashlib.sha256()
     for f in ("scan.hip", "scan_kernel.h", "sfm_device.h", "sfm_internal.h"):
-        with open(os.path.join(ROOT, "selective_scan_segmented_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "selective_scan_segmented_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

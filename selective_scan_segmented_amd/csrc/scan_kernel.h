@@ -266,8 +266,9 @@ struct ScanWave {
         const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * XL;
         const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
         const int nx = nrows * XL, nd = nrows * L;
-        // order: parameters, B/C, x, delta -- everything but the delta rows can
-        // then be waited for (and used) while the delta rows are still landing
+        // order: parameters, B/C, x, delta.  (The compiler inserts a full vmcnt
+        // wait before the first LDS read after these transfers, so the B/C
+        // widening and the row mean start once delta has landed as well.)
         if (!params_loaded) load_params();
         if (p.bc_dma && (p.cw == 1 || wc == 0)) {
             const int nbc = p.N * L * (int)sizeof(IO) / 16;
@@ -303,7 +304,7 @@ struct ScanWave {
             if (!prefetched) issue0(b);
             prefetched = false;
             if (!p.bc_dma && own_bc) stage_bc(bg, cg, 0, L, p.bc_wide != 0);
-            // parameters, B/C and x have landed; delta may still be in flight
+            // parameters, B/C and x have landed (delta too, by the compiler's wait before the first LDS read)
             wait_vmem_at_most(delta_only);
             wave_lds_sync();
             if (p.bc_dma && own_bc) widen_bc();
