@@ -293,10 +293,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                             if (t > 0) {
                                 const float hp = i > 0 ? hs[i - 1][n] : hin[n];
                                 const float a = exp2_fast(dt * kLog2e * A[n]);
-                                const float dat = Gn * hp * a;  // dLoss/da_t times a_t
+                                const float w = a * Gn;    // carried to position t - 1
+                                const float dat = w * hp;  // dLoss/da_t times a_t
                                 ddt = __builtin_fmaf(dat, A[n], ddt);
                                 gA[n] = __builtin_fmaf(dat, dt, gA[n]);
-                                G[n] = a * Gn;
+                                G[n] = w;
                             } else {
                                 G[n] = 0.0f;  // reset: nothing reaches the previous sample
                             }
@@ -664,10 +665,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                             if (c > 0 || i > 0) {
                                 const float hp = i > 0 ? hs[i - 1][n] : hin[n];
                                 const float a = exp2_fast(dtls[i] * A[n]);
-                                const float dat = Gn * hp * a;  // dLoss/da_t times a_t
+                                const float w = a * Gn;    // carried to position t - 1
+                                const float dat = w * hp;  // dLoss/da_t times a_t
                                 sa = __builtin_fmaf(dat, A[n], sa);
                                 gA[n] = __builtin_fmaf(dat, dt, gA[n]);
-                                G[n] = a * Gn;
+                                G[n] = w;
                             } else {
                                 G[n] = 0.0f;  // reset: nothing reaches the previous sample
                             }
