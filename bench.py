@@ -181,11 +181,14 @@ def run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io):
     dy32 = rng.standard_normal((w.B, w.D, w.L)).astype(np.float32)
     from selective_scan_segmented_amd import synth
     dy = dev_io(synth.f32_to_bf16_bits(dy32) if w.io == "bf16" else dy32)
+    cl = a.layout == "bld"
+    if cl:
+        dy = dy.transpose(1, 2).contiguous()
     f32 = dict(dtype=torch.float32, device=dev)
-    g = dict(dA=torch.empty((w.D, w.N), **f32), dBm=torch.empty((w.B, w.N, w.L), **f32),
-             dCm=torch.empty((w.B, w.N, w.L), **f32), dDskip=torch.empty(w.D, **f32),
+    g = dict(dA=torch.empty((w.D, w.N), **f32), dBm=torch.empty((w.B, w.N * w.L), **f32),
+             dCm=torch.empty((w.B, w.N * w.L), **f32), dDskip=torch.empty(w.D, **f32),
              ddelta_bias=torch.empty(w.D, **f32), dconv_w=torch.empty((w.D, w.K), **f32))
-    flags = 3
+    flags = 3 | (sfm.SFM_LAYOUT_BLD if cl else 0)
     need = sfm.sfm_selective_scan_bwd_workspace_size(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, flags)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     calls = []
@@ -225,6 +228,7 @@ def run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io):
         "ms_per_step": ms, "higher_is_better": True, "dtype": w.io, "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}", "B2": b2,
                    "mode": "bwd", "input_sets": len(sets), "workspace_bytes": need,
+                   "layout": "channel-last [B, L, D]" if cl else "channel-first [B, D, L]",
                    "step": "zero the float32 sums + one backward launch (pad and swap fused)"},
         "roofline": {"bound": "alu" if alu / VALU_PEAK_TSLOT >= hbm / HBM_PEAK_GBPS else "hbm",
                      "alu_achieved": round(alu, 3), "alu_peak": round(VALU_PEAK_TSLOT, 3),
@@ -305,8 +309,8 @@ def main():
                     help="bdl: channel-first [B, D, L] (default); bld: channel-last [B, L, D] activations and "
                          "[B, L, N] B/C (fused step only)")
     a = ap.parse_args()
-    if a.layout == "bld" and (a.mode != "step" or a.unfused):
-        raise SystemExit("--layout bld times the fused step only")
+    if a.layout == "bld" and (a.mode not in ("step", "bwd") or a.unfused):
+        raise SystemExit("--layout bld times the fused step or its backward only")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:

@@ -181,11 +181,18 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  *   the partial sums of the f32 outputs for the duration of the call.  The
  *   library allocates nothing.  The f32 sums are added in a fixed order by a
  *   second kernel (no atomics), so repeated calls give identical bits.
+ * flags & SFM_LAYOUT_BLD: channel-last, as the forward: u, delta, dy, du,
+ *   ddelta [B1*B2, L, D] (u [B1*B2, L-2, D] with SFM_FUSE_PAD), Bm, Cm, dBm, dCm
+ *   [B1*B2, L, N]; D times the io element size must be a multiple of 16 bytes
+ *   (else SHAPE), and each sample must fit the whole-sample kernel's LDS (else
+ *   UNSUPPORTED).
  * Two kernels: when every [rows][length] block of a sample and 64-channel tile
  * is a whole number of 16-byte units on 16-byte boundaries and fits in LDS,
- * each sample is staged once; otherwise chunk by chunk.  Environment override
- * (diagnostics): SFM_BWD_CHUNKED=1 forces the chunked kernel.
- * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN (nothing launched), HIP.
+ * each sample is staged once; otherwise chunk by chunk (channel-first only).
+ * Environment override (diagnostics): SFM_BWD_CHUNKED=1 forces the chunked
+ * kernel for channel-first tensors.
+ * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN/UNSUPPORTED (nothing
+ * launched), HIP.
  */
 sfm_status sfm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
                                   const void* Cm, const float* Dskip, const float* delta_bias,
@@ -209,6 +216,11 @@ sfm_status sfm_selective_scan_bwd_workspace_size(int64_t B1, int64_t B2, int64_t
  */
 sfm_status sfm_aux_pad_bwd(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,
                            void* stream);
+
+/* sfm_aux_pad_bwd with flags: SFM_LAYOUT_BLD takes gpad [B, T+2, D] and writes
+ * gx [B, T, D] (the same arithmetic per element); flags = 0 is sfm_aux_pad_bwd. */
+sfm_status sfm_aux_pad_bwd_ex(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,
+                              int flags, void* stream);
 
 /*
  * sfm_aux_pad_swap -- the auxiliary head/tail tokens ([SBW] 3.2, [TL]

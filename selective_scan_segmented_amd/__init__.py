@@ -17,6 +17,7 @@ import os
 
 __all__ = ["sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_selective_scan_bwd",
            "sfm_selective_scan_bwd_workspace_size", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_aux_pad_bwd",
+           "sfm_aux_pad_bwd_ex",
            "sfm_pick_b1", "sfm_scan_plan_string", "sfm_version", "library_path", "load_library", "SFMError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,12 +58,13 @@ def load_library():
     lib.sfm_selective_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci,
                                                           ctypes.POINTER(ctypes.c_int64)]
     lib.sfm_aux_pad_bwd.argtypes = [vp, vp, i64, i64, i64, ci, vp]
+    lib.sfm_aux_pad_bwd_ex.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
     lib.sfm_aux_pad_swap.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
     lib.sfm_pick_b1.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.sfm_scan_plan_string.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci, ctypes.c_char_p, i64]
     for f in ("sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_dwconv1d_fold", "sfm_aux_pad_swap",
               "sfm_pick_b1", "sfm_version", "sfm_scan_plan_string", "sfm_selective_scan_bwd",
-              "sfm_selective_scan_bwd_workspace_size", "sfm_aux_pad_bwd"):
+              "sfm_selective_scan_bwd_workspace_size", "sfm_aux_pad_bwd", "sfm_aux_pad_bwd_ex"):
         getattr(lib, f).restype = ctypes.c_int
     lib.sfm_status_string.argtypes = [ctypes.c_int]
     lib.sfm_status_string.restype = ctypes.c_char_p
@@ -200,17 +202,23 @@ def sfm_selective_scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, delta_bias=None,
     Returns a dict: du (padded layout [B, D, L], io), ddelta (io), dA, dBm, dCm,
     dDskip, ddelta_bias, dconv_w, dconv_b (float32).  `grads` may hold
     preallocated tensors under those names; `workspace` a uint8 GPU tensor of at
-    least sfm_selective_scan_bwd_workspace_size() bytes."""
+    least sfm_selective_scan_bwd_workspace_size() bytes.  flags & SFM_LAYOUT_BLD:
+    channel-last tensors ([B, L, D] and [B, L, N], gradients likewise)."""
     torch = _torch()
     io = _io_code(u)
-    B, D, XL = u.shape
+    cl = bool(flags & SFM_LAYOUT_BLD)
+    if cl:
+        B, XL, D = u.shape
+    else:
+        B, D, XL = u.shape
     L = XL + 2 if flags & SFM_FUSE_PAD else XL
     N = A.shape[1]
     if B % B2:
         raise ValueError(f"B2={B2} must divide B={B}")
+    tl = (lambda a, b_: (B, b_, a)) if cl else (lambda a, b_: (B, a, b_))  # [B, a, b] in this layout
     _dev(u, "u")
-    for t, name, shape in ((delta, "delta", (B, D, L)), (Bm, "Bm", (B, N, L)), (Cm, "Cm", (B, N, L)),
-                           (dy, "dy", (B, D, L))):
+    for t, name, shape in ((delta, "delta", tl(D, L)), (Bm, "Bm", tl(N, L)), (Cm, "Cm", tl(N, L)),
+                           (dy, "dy", tl(D, L))):
         _dev(t, name, u.dtype, shape)
     _dev(A, "A", torch.float32, (D, N))
     _dev(Dskip, "Dskip", torch.float32, (D,))
@@ -224,8 +232,8 @@ def sfm_selective_scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, delta_bias=None,
         _dev(conv_b, "conv_b", torch.float32, (D,))
     g = dict(grads or {})
     f32 = dict(dtype=torch.float32, device=u.device)
-    shapes = dict(du=((B, D, L), u.dtype), ddelta=((B, D, L), u.dtype), dA=((D, N), torch.float32),
-                  dBm=((B, N, L), torch.float32), dCm=((B, N, L), torch.float32))
+    shapes = dict(du=(tl(D, L), u.dtype), ddelta=(tl(D, L), u.dtype), dA=((D, N), torch.float32),
+                  dBm=(tl(N, L), torch.float32), dCm=(tl(N, L), torch.float32))
     if Dskip is not None:
         shapes["dDskip"] = ((D,), torch.float32)
     if delta_bias is not None:
@@ -256,13 +264,25 @@ def sfm_selective_scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, delta_bias=None,
 
 def sfm_aux_pad_bwd(gpad, gx=None, stream=None):
     """Gradient of the aux pad: gpad [B, D, T+2] -> gx [B, D, T]."""
+    return sfm_aux_pad_bwd_ex(gpad, gx, 0, stream)
+
+
+def sfm_aux_pad_bwd_ex(gpad, gx=None, flags=0, stream=None):
+    """Gradient of the aux pad; flags & SFM_LAYOUT_BLD: gpad [B, T+2, D] -> gx [B, T, D]."""
     io = _io_code(gpad)
-    B, D, L = gpad.shape
+    cl = bool(flags & SFM_LAYOUT_BLD)
+    if cl:
+        B, L, D = gpad.shape
+        shape = (B, L - 2, D)
+    else:
+        B, D, L = gpad.shape
+        shape = (B, D, L - 2)
     _dev(gpad, "gpad")
     if gx is None:
-        gx = _torch().empty((B, D, L - 2), dtype=gpad.dtype, device=gpad.device)
-    _dev(gx, "gx", gpad.dtype, (B, D, L - 2))
-    _check(load_library().sfm_aux_pad_bwd(_ptr(gpad), _ptr(gx), B, D, L - 2, io, _stream(stream)), "sfm_aux_pad_bwd")
+        gx = _torch().empty(shape, dtype=gpad.dtype, device=gpad.device)
+    _dev(gx, "gx", gpad.dtype, shape)
+    _check(load_library().sfm_aux_pad_bwd_ex(_ptr(gpad), _ptr(gx), B, D, L - 2, io, int(flags), _stream(stream)),
+           "sfm_aux_pad_bwd")
     return gx
 
 

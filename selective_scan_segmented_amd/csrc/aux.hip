@@ -114,6 +114,23 @@ __global__ void pad_bwd_kernel(const IO* __restrict__ gp, IO* __restrict__ gx, l
     }
 }
 
+// Channel-last: gx[b, i, d] = gp[b, 1 + i, d] + (gp[b, 0, d] + gp[b, L-1, d]) / T
+// (the same float operations, in the same order, as the channel-first kernel).
+template <typename IO>
+__global__ void pad_bwd_cl_kernel(const IO* __restrict__ gp, IO* __restrict__ gx, long long n, int T, int C) {
+    const int L = T + 2;
+    for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < n;
+         e += (long long)gridDim.x * blockDim.x) {
+        const long long bi = e / C;  // b * T + i
+        const int c = (int)(e - bi * C);
+        const long long b = bi / T;
+        const int i = (int)(bi - b * T);
+        const IO* g = gp + b * L * C + c;
+        const float ends = (to_f32(g[0]) + to_f32(g[(size_t)(L - 1) * C])) / (float)T;
+        gx[e] = from_f32<IO>(to_f32(g[(size_t)(1 + i) * C]) + ends);
+    }
+}
+
 unsigned grid_for(long long work, int per_block) {
     long long b = (work + per_block - 1) / per_block;
     if (b > 65536) b = 65536;
@@ -145,7 +162,13 @@ hipError_t swap_t(const void* in, void* out, int64_t rows, int64_t L, hipStream_
 }
 
 template <typename IO>
-hipError_t pad_bwd_t(const void* gp, void* gx, int64_t rows, int64_t T, hipStream_t s) {
+hipError_t pad_bwd_t(const void* gp, void* gx, int64_t rows, int64_t T, hipStream_t s, int64_t channels) {
+    if (channels > 0) {
+        const long long n = rows * T * channels;
+        hipLaunchKernelGGL((pad_bwd_cl_kernel<IO>), dim3(grid_for(n, 256)), dim3(256), 0, s,
+                           static_cast<const IO*>(gp), static_cast<IO*>(gx), n, (int)T, (int)channels);
+        return hipGetLastError();
+    }
     const long long n = rows * T;
     hipLaunchKernelGGL((pad_bwd_kernel<IO>), dim3(grid_for(n, 256)), dim3(256), 0, s, static_cast<const IO*>(gp),
                        static_cast<IO*>(gx), n, (int)T);
@@ -154,8 +177,10 @@ hipError_t pad_bwd_t(const void* gp, void* gx, int64_t rows, int64_t T, hipStrea
 
 }  // namespace
 
-hipError_t launch_aux_pad_bwd(const void* gp, void* gx, int64_t rows, int64_t T, int io_dtype, hipStream_t stream) {
-    return io_dtype == 0 ? pad_bwd_t<float>(gp, gx, rows, T, stream) : pad_bwd_t<__bf16>(gp, gx, rows, T, stream);
+hipError_t launch_aux_pad_bwd(const void* gp, void* gx, int64_t rows, int64_t T, int io_dtype, hipStream_t stream,
+                              int64_t channels) {
+    return io_dtype == 0 ? pad_bwd_t<float>(gp, gx, rows, T, stream, channels)
+                         : pad_bwd_t<__bf16>(gp, gx, rows, T, stream, channels);
 }
 
 hipError_t launch_aux_pad(const void* in, void* out, int64_t rows, int64_t T, int io_dtype, hipStream_t stream) {

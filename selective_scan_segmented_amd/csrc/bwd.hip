@@ -408,7 +408,31 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 // with 16-byte stores once the sample is done.  B and C of the sample are
 // widened to float32 once.  The dB/dC transpose uses 32 rows; two lanes sum
 // the two halves of a row.
-template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q>
+// Channel-last staging: `rows` position rows of this tile (units_per_row 16-byte
+// units each, rows `stride` elements apart from `base`) into LDS back to back,
+// unit u at l + 16 u.  Four transfers share one LDS base; nothing is waited for.
+template <typename IO>
+__device__ __forceinline__ void dma_rows(const IO* base, int rows, int stride, int units_per_row, float inv_upr,
+                                         IO* l, int lane) {
+    const int units = rows * units_per_row;
+    const char* g = reinterpret_cast<const char*>(base);
+    auto src = [&](int u) __attribute__((always_inline)) {
+        const int r = div_small(u, inv_upr);
+        return g + (size_t)r * stride * sizeof(IO) + (size_t)(u - r * units_per_row) * 16;
+    };
+    char* lb = reinterpret_cast<char*>(l);
+    for (int u0 = 0; u0 < units; u0 += 4 * kWave) {
+        char* ll = lb + u0 * 16;
+        const int u = u0 + lane;
+        const int rem = units - u;
+        if (rem > 0) dma_at<16, 0>(src(u), ll);
+        if (rem > 64) dma_at<16, 1024>(src(u + 64), ll);
+        if (rem > 128) dma_at<16, 2048>(src(u + 128), ll);
+        if (rem > 192) dma_at<16, 3072>(src(u + 192), ll);
+    }
+}
+
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q, bool CL>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_whole_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     constexpr int R = 16 / NS;  // positions per dB/dC transpose round (2 * NS * R = 32 rows)
@@ -427,14 +451,22 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     const int sh = p.pad_in ? 1 : 0;  // padded position q reads u row index q - sh
     const int lag = CONV ? KW - 1 - P : 0;  // dx of position t + lag is complete after step t
 
-    IO* xs = reinterpret_cast<IO*>(smem + p.xs_off);        // [rows][XL] x
-    IO* ds = reinterpret_cast<IO*>(smem + p.ds_off);        // [rows][L]  delta, then ddelta
-    IO* ys = reinterpret_cast<IO*>(smem + p.dys_off);       // [rows][L]  dy, then dx
+    // channel-first: [rows][XL] x, [rows][L] delta/ddelta and dy/dx (one row per channel);
+    // channel-last (CL): the same blocks as [XL][rows] and [L][rows] (one row per position)
+    IO* xs = reinterpret_cast<IO*>(smem + p.xs_off);
+    IO* ds = reinterpret_cast<IO*>(smem + p.ds_off);        // delta, then ddelta
+    IO* ys = reinterpret_cast<IO*>(smem + p.dys_off);       // dy, then dx
     float* bs = reinterpret_cast<float*>(smem + p.bc_off);  // [L][NS]
     float* cs = bs + L * NS;                                // [L][NS]
     float* red = reinterpret_cast<float*>(smem + p.red_off);  // [32][kRedStride]
-    const int xrow = valid ? lane * XL : 0;  // lanes past the tile read row 0 and mask the value
-    const int row = valid ? lane * L : 0;
+    const int col = valid ? lane : 0;  // lanes past the tile read channel 0 and mask the value
+    const int xrow = col * XL;
+    const int row = col * L;
+    // LDS element of this lane's channel at x position q / at position t
+    auto xi = [&](int q) __attribute__((always_inline)) { return CL ? q * nrows + col : xrow + q; };
+    auto ti = [&](int t) __attribute__((always_inline)) { return CL ? t * nrows + col : row + t; };
+    const int upr = nrows * EB / 16;  // channel-last: 16-byte units per position row (whole, by the plan)
+    const float inv_upr = 1.0f / (float)upr;
     // one position's NS float32 values of B (or C) as whole 16-byte reads
     auto bc_row = [&](const float* base, int t, float (&v)[NS]) __attribute__((always_inline)) {
         const float4* r = reinterpret_cast<const float4*>(base + t * NS);
@@ -467,11 +499,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     float* ws = p.ws + (size_t)g * p.nchk * NS * kWave + lane;
     const int NL = N * L;
     const float inv_L = 1.0f / (float)L;
+    const float inv_N = 1.0f / (float)N;
 
     for (int j = 0; j < p.B2; ++j) {
         const int b = b1 * p.B2 + j;
-        const size_t xoff = ((size_t)b * p.D + d0) * XL;
-        const size_t toff = ((size_t)b * p.D + d0) * L;
+        const size_t xoff = CL ? (size_t)b * XL * p.D + d0 : ((size_t)b * p.D + d0) * XL;
+        const size_t toff = CL ? (size_t)b * L * p.D + d0 : ((size_t)b * p.D + d0) * L;
         const IO* bgl = static_cast<const IO*>(p.Bm) + (size_t)b * NL;
         const IO* cgl = static_cast<const IO*>(p.Cm) + (size_t)b * NL;
         wave_lds_sync();  // the previous sample's LDS reads are done
@@ -485,16 +518,29 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 cv[k] = e < NL ? cgl[e] : Io<IO>::zero();
             }
             if (e0 == 0) {
-                dma_to_lds(static_cast<const IO*>(p.u) + xoff, xs, nrows * XL * EB, lane);
-                dma_to_lds(static_cast<const IO*>(p.delta) + toff, ds, nrows * L * EB, lane);
-                dma_to_lds(static_cast<const IO*>(p.dy) + toff, ys, nrows * L * EB, lane);
+                if constexpr (CL) {
+                    dma_rows(static_cast<const IO*>(p.u) + xoff, XL, p.D, upr, inv_upr, xs, lane);
+                    dma_rows(static_cast<const IO*>(p.delta) + toff, L, p.D, upr, inv_upr, ds, lane);
+                    dma_rows(static_cast<const IO*>(p.dy) + toff, L, p.D, upr, inv_upr, ys, lane);
+                } else {
+                    dma_to_lds(static_cast<const IO*>(p.u) + xoff, xs, nrows * XL * EB, lane);
+                    dma_to_lds(static_cast<const IO*>(p.delta) + toff, ds, nrows * L * EB, lane);
+                    dma_to_lds(static_cast<const IO*>(p.dy) + toff, ys, nrows * L * EB, lane);
+                }
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int e = e0 + k * kWave + lane;
                 if (e < NL) {
-                    const int n = div_small(e, inv_L);
-                    const int t = e - n * L;
+                    // B, C of the sample: [N][L] channel-first, [L][N] channel-last
+                    int n, t;
+                    if constexpr (CL) {
+                        t = div_small(e, inv_N);
+                        n = e - t * N;
+                    } else {
+                        n = div_small(e, inv_L);
+                        t = e - n * L;
+                    }
                     bs[t * NS + n] = to_f32(bv[k]);
                     cs[t * NS + n] = to_f32(cv[k]);
                 }
@@ -507,13 +553,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         float mean = 0.0f;
         if (p.pad_in) {
             double acc = 0.0;
-            for (int c = 0; c < XL; ++c) acc += (double)to_f32(xs[xrow + c]);
+            for (int c = 0; c < XL; ++c) acc += (double)to_f32(xs[xi(c)]);
             mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
         }
         // conv/scan input at padded position q (zero outside the sample)
         auto xv = [&](int q) __attribute__((always_inline)) {
             const int qc = min(max(q - sh, 0), XL - 1);
-            float v = to_f32(xs[xrow + qc]);
+            float v = to_f32(xs[xi(qc)]);
             if (p.pad_in && (q == 0 || q == L - 1)) v = mean;
             return (valid && q >= 0 && q < L) ? v : 0.0f;
         };
@@ -536,7 +582,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 z = xw[i];
                 u = z;
             }
-            v = (valid ? to_f32(ds[row + t]) : 0.0f) + db;
+            v = (valid ? to_f32(ds[ti(t)]) : 0.0f) + db;
             if constexpr (SP) {
                 dtl = softplus_log2e(v);
                 dt = dtl * kLn2;
@@ -547,8 +593,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         };
         // dy at the two sample ends, before the dx written in place can cover them
         const int ce0 = (p.swap_dy && L > 1) ? L - 1 : 0;
-        const float gy_first = valid ? to_f32(ys[row + ce0]) : 0.0f;
-        const float gy_last = valid ? to_f32(ys[row + (L - 1 - ce0)]) : 0.0f;
+        const float gy_first = valid ? to_f32(ys[ti(ce0)]) : 0.0f;
+        const float gy_last = valid ? to_f32(ys[ti(L - 1 - ce0)]) : 0.0f;
 
         // --- sweep 1: forward, checkpoint the state entering each chunk
         {
@@ -618,7 +664,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int i = 0; i < Q; ++i) {
                 const int t = t0 + min(i, cnt - 1);
                 pre(xw, t, i, zs[i], us[i], vs[i], dts[i], dtls[i]);
-                gys[i] = t == 0 ? gy_first : (t == L - 1 ? gy_last : (valid ? to_f32(ys[row + t]) : 0.0f));
+                gys[i] = t == 0 ? gy_first : (t == L - 1 ? gy_last : (valid ? to_f32(ys[ti(t)]) : 0.0f));
             }
 #pragma unroll
             for (int i = 0; i < Q; ++i) {
@@ -677,7 +723,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                         const float ddt = __builtin_fmaf(sb, u, sa);
                         float dv = ddt;
                         if constexpr (SP) dv = vs[i] > 20.0f ? ddt : ddt * sigmoid_f(vs[i]);
-                        if (valid) ds[row + t] = from_f32<IO>(dv);
+                        if (valid) ds[ti(t)] = from_f32<IO>(dv);
                         gb += dv;
                         const float du_ = __builtin_fmaf(dt, sb, Dk * gy);
                         float dz = du_;
@@ -693,12 +739,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                                 wdx[jj] = __builtin_fmaf(dz, cw[jj], wdx[jj]);
                             }
                             // padded position t + lag gets no later contribution
-                            if (valid && t + lag < L) ys[row + t + lag] = from_f32<IO>(wdx[KW - 1]);
+                            if (valid && t + lag < L) ys[ti(t + lag)] = from_f32<IO>(wdx[KW - 1]);
 #pragma unroll
                             for (int jj = KW - 1; jj > 0; --jj) wdx[jj] = wdx[jj - 1];
                             wdx[0] = 0.0f;
                         } else {
-                            if (valid) ys[row + t] = from_f32<IO>(dz);
+                            if (valid) ys[ti(t)] = from_f32<IO>(dz);
                         }
                     }
                     // transpose buffer: row (ii, k), column lane
@@ -735,7 +781,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
             for (int m = 1; m < KW; ++m) {
                 const int q = m - 1 - P;
-                if (valid && q >= 0 && q < L) ys[row + q] = from_f32<IO>(wdx[m]);
+                if (valid && q >= 0 && q < L) ys[ti(q)] = from_f32<IO>(wdx[m]);
             }
         }
         wave_lds_sync();
@@ -744,11 +790,17 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             const int units = nrows * L * EB / 16;
             const uint4* sd = reinterpret_cast<const uint4*>(ds);
             const uint4* sy = reinterpret_cast<const uint4*>(ys);
-            uint4* gd = reinterpret_cast<uint4*>(static_cast<IO*>(p.ddelta) + toff);
-            uint4* gu = reinterpret_cast<uint4*>(static_cast<IO*>(p.du) + toff);
+            char* gd = reinterpret_cast<char*>(static_cast<IO*>(p.ddelta) + toff);
+            char* gu = reinterpret_cast<char*>(static_cast<IO*>(p.du) + toff);
             for (int u = lane; u < units; u += kWave) {
-                gd[u] = sd[u];
-                gu[u] = sy[u];
+                size_t off = (size_t)u * 16;  // channel-first: one contiguous block
+                if constexpr (CL) {
+                    // channel-last: unit u is part u % upr of position row u / upr
+                    const int r = div_small(u, inv_upr);
+                    off = (size_t)r * p.D * EB + (size_t)(u - r * upr) * 16;
+                }
+                *reinterpret_cast<uint4*>(gd + off) = sd[u];
+                *reinterpret_cast<uint4*>(gu + off) = sy[u];
             }
         }
     }
@@ -793,7 +845,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int nb_bc)
             if (n >= N) continue;
             float s = 0.0f;
             for (int tl = 0; tl < p.tiles; ++tl) s += pbc[(size_t)tl * nbc + idx];
-            (c ? p.dCm : p.dBm)[(b * N + n) * L + t] = s;
+            (c ? p.dCm : p.dBm)[p.cl ? (b * L + t) * N + n : (b * N + n) * L + t] = s;
         }
         return;
     }
@@ -824,8 +876,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int nb_bc)
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
 hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
     constexpr int Q = kHist / NS;  // kHist states of history in registers
-    if (p.whole)
-        hipLaunchKernelGGL((bwd_whole_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)),
+    if (p.whole && p.cl)
+        hipLaunchKernelGGL((bwd_whole_kernel<IO, NS, KW, CONV, SP, SILU, Q, true>), dim3((unsigned)(p.B1 * p.tiles)),
+                           dim3(kWave), (size_t)p.lds_bytes, s, p);
+    else if (p.whole)
+        hipLaunchKernelGGL((bwd_whole_kernel<IO, NS, KW, CONV, SP, SILU, Q, false>), dim3((unsigned)(p.B1 * p.tiles)),
                            dim3(kWave), (size_t)p.lds_bytes, s, p);
     else
         hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)), dim3(kWave),
@@ -880,6 +935,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         const int last = p.D - (p.tiles - 1) * kWave;
         bool ok = (p.D * XL * eb) % 16 == 0 && (p.D * L * eb) % 16 == 0 && (kWave * XL * eb) % 16 == 0 &&
                   (kWave * L * eb) % 16 == 0 && (last * XL * eb) % 16 == 0 && (last * L * eb) % 16 == 0;
+        if (p.cl) ok = (p.D * eb) % 16 == 0;  // position rows of D channels in whole 16-byte units
         int off = 0;
         p.xs_off = off;
         off += up16(kWave * XL * eb);
@@ -892,7 +948,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         p.red_off = off;
         off += 32 * kRedStride * 4;
         const char* force = getenv("SFM_BWD_CHUNKED");  // diagnostics: force the chunked kernel
-        if (ok && L <= 4096 && off <= 64 * 1024 && !(force && atoi(force) > 0)) {
+        if (ok && L <= 4096 && off <= 64 * 1024 && (p.cl || !(force && atoi(force) > 0))) {
             p.whole = 1;
             p.mean_off = p.braw_off = 0;
             p.lds_bytes = off;
@@ -900,6 +956,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         }
     }
     p.whole = 0;
+    if (p.cl) return false;  // channel-last runs only the whole-sample kernel
     const int q = p.q;
     const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 4;
     const int xw = q + kw - 1;

@@ -380,7 +380,8 @@ sfm_status bwd_common(const void* u, const void* delta, const float* A, const vo
                       int delta_softplus, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype,
                       int flags, const char* who) {
     if (!u || !delta || !A || !Bm || !Cm || !dy) return fail(SFM_ERR_NULL, "%s: u, delta, A, Bm, Cm, dy are required", who);
-    if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP)) return fail(SFM_ERR_SHAPE, "%s: unknown flags 0x%x", who, flags);
+    if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP | SFM_LAYOUT_BLD))
+        return fail(SFM_ERR_SHAPE, "%s: unknown flags 0x%x", who, flags);
     if ((flags & SFM_FUSE_PAD) && L < 3) return fail(SFM_ERR_SHAPE, "%s: SFM_FUSE_PAD needs L >= 3", who);
     if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "%s: io_dtype %d", who, io_dtype);
     if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24))
@@ -389,6 +390,9 @@ sfm_status bwd_common(const void* u, const void* delta, const float* A, const vo
     if (N < 1 || N > SFM_MAX_N) return fail(SFM_ERR_SHAPE, "%s: N=%lld not in [1, %d]", who, (long long)N, SFM_MAX_N);
     if (B1 * B2 * D * L > (1LL << 40)) return fail(SFM_ERR_SHAPE, "%s: tensor too large", who);
     if (delta_softplus != 0 && delta_softplus != 1) return fail(SFM_ERR_SHAPE, "%s: delta_softplus must be 0 or 1", who);
+    if ((flags & SFM_LAYOUT_BLD) && (D * io_bytes(io_dtype)) % 16 != 0)
+        return fail(SFM_ERR_SHAPE, "%s: channel-last rows of D=%lld channels must be whole 16-byte units", who,
+                    (long long)D);
     if (conv_w) {
         if (conv_k < 1 || conv_k > SFM_MAX_K) return fail(SFM_ERR_SHAPE, "%s: conv_k=%d not in [1, %d]", who, conv_k, SFM_MAX_K);
         if (conv_pad_left < 0 || conv_pad_left >= conv_k)
@@ -412,6 +416,7 @@ void fill_bwd(sfm::BwdParams& p, int64_t B1, int64_t B2, int64_t D, int64_t N, i
     p.softplus = delta_softplus;
     p.pad_in = (flags & SFM_FUSE_PAD) ? 1 : 0;
     p.swap_dy = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+    p.cl = (flags & SFM_LAYOUT_BLD) ? 1 : 0;
     p.xrow = p.pad_in ? (int)L - 2 : (int)L;
 }
 
@@ -499,18 +504,27 @@ extern "C" sfm_status sfm_selective_scan_bwd(
     return hip_status(sfm::launch_bwd(p, io_dtype, static_cast<hipStream_t>(stream)), who);
 }
 
-extern "C" sfm_status sfm_aux_pad_bwd(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,
-                                      void* stream) {
-    if (!gpad || !gx) return fail(SFM_ERR_NULL, "sfm_aux_pad_bwd: gpad and gx are required");
-    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "sfm_aux_pad_bwd: io_dtype %d", io_dtype);
+extern "C" sfm_status sfm_aux_pad_bwd_ex(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,
+                                         int flags, void* stream) {
+    const char* who = "sfm_aux_pad_bwd";
+    if (!gpad || !gx) return fail(SFM_ERR_NULL, "%s: gpad and gx are required", who);
+    if (flags & ~SFM_LAYOUT_BLD) return fail(SFM_ERR_SHAPE, "%s: unknown flags 0x%x", who, flags);
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "%s: io_dtype %d", who, io_dtype);
     if (!sane(B, 1 << 24) || !sane(D, 1 << 20) || !sane(T, 1 << 24))
-        return fail(SFM_ERR_SHAPE, "sfm_aux_pad_bwd: B=%lld D=%lld T=%lld out of range", (long long)B, (long long)D,
+        return fail(SFM_ERR_SHAPE, "%s: B=%lld D=%lld T=%lld out of range", who, (long long)B, (long long)D,
                     (long long)T);
-    if (B * D * (T + 2) > (1LL << 40)) return fail(SFM_ERR_SHAPE, "sfm_aux_pad_bwd: tensor too large");
-    if (!aligned16(gpad) || !aligned16(gx)) return fail(SFM_ERR_ALIGN, "sfm_aux_pad_bwd: io base pointers must be 16-byte aligned");
+    if (B * D * (T + 2) > (1LL << 40)) return fail(SFM_ERR_SHAPE, "%s: tensor too large", who);
+    if (!aligned16(gpad) || !aligned16(gx)) return fail(SFM_ERR_ALIGN, "%s: io base pointers must be 16-byte aligned", who);
     const int eb = io_bytes(io_dtype);
     if (overlap(rng("gx", gx, B * D * T * eb), rng("gpad", gpad, B * D * (T + 2) * eb)))
-        return fail(SFM_ERR_ALIAS, "sfm_aux_pad_bwd: gx overlaps gpad");
-    return hip_status(sfm::launch_aux_pad_bwd(gpad, gx, B * D, T, io_dtype, static_cast<hipStream_t>(stream)),
-                      "sfm_aux_pad_bwd");
+        return fail(SFM_ERR_ALIAS, "%s: gx overlaps gpad", who);
+    const bool cl = (flags & SFM_LAYOUT_BLD) != 0;
+    return hip_status(sfm::launch_aux_pad_bwd(gpad, gx, cl ? B : B * D, T, io_dtype, static_cast<hipStream_t>(stream),
+                                              cl ? D : 0),
+                      who);
+}
+
+extern "C" sfm_status sfm_aux_pad_bwd(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,
+                                      void* stream) {
+    return sfm_aux_pad_bwd_ex(gpad, gx, B, D, T, io_dtype, 0, stream);
 }

@@ -37,6 +37,7 @@ struct BwdParams {
     // plan
     int ns, tiles, q, nchk;
     int whole;            // 1: whole-sample slabs staged once per sample; 0: chunk by chunk
+    int cl;               // channel-last tensors: u, delta, dy, du, ddelta [B, L, D]; B, C, dB, dC [B, L, N]
     // partial sums in the workspace (offsets in floats), added up in a fixed order
     // by a second kernel: dB/dC per channel tile [tiles][B][L][2][ns] and the
     // per-channel sums per folded row [B1][kc][D], rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
@@ -49,6 +50,9 @@ struct BwdParams {
 bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes);
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t stream);
 
-hipError_t launch_aux_pad_bwd(const void* gp, void* gx, int64_t rows, int64_t T, int io_dtype, hipStream_t stream);
+// Gradient of the aux pad: channel-first rows [rows][T+2] -> [rows][T], or
+// channel-last (channels > 0) [B][T+2][channels] -> [B][T][channels] with rows = B.
+hipError_t launch_aux_pad_bwd(const void* gp, void* gx, int64_t rows, int64_t T, int io_dtype, hipStream_t stream,
+                              int64_t channels = 0);
 
 }  // namespace sfm

@@ -139,7 +139,8 @@ def test_bwd_validation(lib):
     assert bwd(lib, cw=13 * P, dcw=None) == NULL      # conv weights need their gradient
     assert bwd(lib, io=2) == DTYPE
     assert bwd(lib, N=17) == SHAPE
-    assert bwd(lib, flags=4) == SHAPE                  # unknown flag
+    assert bwd(lib, flags=8) == SHAPE                  # unknown flag
+    assert bwd(lib, flags=4, D=6, io=1) == SHAPE       # channel-last rows of 6 bf16 channels: not whole 16-byte units
     assert bwd(lib, flags=1, L=2) == SHAPE             # fused pad needs L >= 3
     assert bwd(lib, cw=13 * P, dcw=14 * P, k=4, pad=4) == SHAPE
     assert bwd(lib, sp=3) == SHAPE
@@ -180,6 +181,9 @@ def test_bwd_workspace_size(lib):
 
 
 def test_aux_pad_bwd_validation(lib):
+    fx = lib.sfm_aux_pad_bwd_ex
+    assert fx(P, 2 * P, 2, 3, 4, 0, 2, None) == SHAPE     # unknown flag
+    assert fx(None, P, 2, 3, 4, 0, 4, None) == NULL
     f = lib.sfm_aux_pad_bwd
     assert f(None, P, 2, 3, 4, 0, None) == NULL
     assert f(P, 2 * P, 2, 3, 0, 0, None) == SHAPE
