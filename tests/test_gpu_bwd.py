@@ -231,3 +231,8 @@ def test_bwd_channel_last_rejects_unaligned_rows():
     with pytest.raises(sfm.SFMError):
         sfm.sfm_selective_scan_bwd(z(B, L, D), z(B, L, D), z(D, N, dt=torch.float32), z(B, L, N), z(B, L, N),
                                    z(B, L, D), conv_w=z(D, 4, dt=torch.float32), flags=sfm.SFM_LAYOUT_BLD)
+
+
+def test_bwd_long_rows_bf16():
+    """Rows of 4002 positions (the long workload's length, N = 16), chunked kernel."""
+    run_case(B=2, D=128, N=16, T=4000, B2=1, K=4, P=1, act=0, softplus=True, flags=3, io="bf16", seed=31)
