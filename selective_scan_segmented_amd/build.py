@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -21,6 +22,7 @@ LIB = os.path.join(HERE, "libsfm.so")
 SOURCES = ["scan.hip", "scan_cl.hip", "conv.hip", "aux.hip", "bwd.hip", "sfm_api.cpp"] + [
     f"scan_{io}_n{n}.hip" for io in ("f32", "bf16") for n in (4, 8, 16)]
 ARCH = os.environ.get("SFM_OFFLOAD_ARCH", "gfx950")
+SPILL_OK = {"bwd.hip"}  # sources whose kernels may use scratch (register spills)
 
 
 def _hipcc() -> str:
@@ -37,14 +39,39 @@ def _flags():
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
+_REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|Dynamic Stack):\s+(\S+)")
+
+
+def scratch_users(remarks: str):
+    """Kernels whose resource-usage remarks report scratch (private) memory or a dynamic stack."""
+    bad, name = [], None
+    for key, val in _REMARK.findall(remarks):
+        if key == "Function Name":
+            name = val
+        elif key.startswith("ScratchSize") and val != "0":
+            bad.append(f"{name} ({val} bytes/lane)")
+        elif key == "Dynamic Stack" and val != "False":
+            bad.append(f"{name} (dynamic stack)")
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [_hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *_flags(), "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # No forward kernel may keep state in scratch: a per-wave object that lands
+    # there (e.g. through an array indexed at run time) also turns its LDS
+    # accesses into flat accesses through pointers reloaded from scratch.  The
+    # backward kernels' wide variants (f32, 8-tap conv, 16 states) spill
+    # registers there by design.
+    bad = [] if src in SPILL_OK else scratch_users(r.stderr)
+    if bad:
+        os.remove(obj)
+        raise RuntimeError(f"{src}: kernels use scratch memory: " + "; ".join(bad))
     return obj
 
 

@@ -30,7 +30,7 @@ static int device_cus() {
     return cus;
 }
 
-bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint) {
+bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint, int stages_hint) {
     const int L = p.L, S = p.B2 * p.L;
     if (p.xrow <= 0) p.xrow = p.pad_in ? L - 2 : L;
     const int XL = p.xrow;
@@ -58,8 +58,10 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
             xsb = kWave * xrs * io_bytes;
             dsb = kWave * drs * io_bytes;
         }
-        xsb = (xsb + 15) & ~15;
-        dsb = (dsb + 15) & ~15;
+        // mode 1 transfers go in groups of four 256-byte instructions
+        const int unit = mode == 1 ? 1024 : 16;
+        xsb = (xsb + unit - 1) / unit * unit;
+        dsb = (dsb + unit - 1) / unit * unit;
         return xsb + dsb;
     };
     // B/C stage: float32 [ch][ns] for B and C, plus (mode 0, aligned blocks) the
@@ -68,6 +70,9 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     auto bc_bytes = [&](int ch, int m) {
         return 2 * ch * p.ns * (int)sizeof(float) + (m == 0 && p.bc_wide ? bcr_bytes : 0);
     };
+    // mode 1 raw B/C rows of one stage: a chunk plus word alignment at both ends
+    auto rb_rs_of = [&](int ch) { return (ch + 2 * (ew - 1) + ew - 1) / ew * ew; };
+    auto rb_bytes_of = [&](int ch) { return 2 * ((p.N * rb_rs_of(ch) * io_bytes + 1023) / 1024 * 1024); };
     int xsb = 0, dsb = 0, xrs = 0, drs = 0;
     // pieces per folded row
     int W;
@@ -108,13 +113,62 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
         mode = ((long long)L * io_bytes) % 4 == 0 && ((long long)XL * io_bytes) % 4 == 0 ? 1 : 2;
         if (ch > L) ch = L;
     }
+    // mode 1: pieces that start on sample boundaries need no exchange, so each
+    // is a workgroup of its own (one wave), which packs LDS per wave, not per row
+    const int wsplit = mode == 1 && !carry ? 1 : 0;
+    const int per_wg = wsplit ? 1 : W;
+    int stages = stages_hint == 2 ? 2 : 1;
     auto lds_total = [&](int cw, int chv, int& grp) {
-        grp = bc_bytes(chv, mode) + cw * xd_bytes(chv, mode, xsb, dsb, xrs, drs);
+        if (mode == 1)  // one wave per group: stages of x, delta and raw B/C, one float32 B/C area
+            grp = stages * (xd_bytes(chv, mode, xsb, dsb, xrs, drs) + rb_bytes_of(chv)) + bc_bytes(chv, mode);
+        else
+            grp = bc_bytes(chv, mode) + cw * xd_bytes(chv, mode, xsb, dsb, xrs, drs);
         const int agg = carry ? agg_fixed + W * kWave * (int)sizeof(float) * (1 + p.ns) : 0;
-        return W * grp + agg;
+        return per_wg * grp + agg;
     };
-    // shrink the chunk until one workgroup of cw = 1 fits
+    const int vgpr_waves_per_cu = p.ns <= 8 ? 12 : 8;
+    const int cus = device_cus();
     int grp = 0;
+    if (mode == 1 && ch_hint <= 0) {
+        // Chunk length: every chunk costs a fixed set-up (waits, conv window,
+        // loop entry and exit), so long chunks come first; the first that lets
+        // as many waves share a CU as the grid (or the register file) can use
+        // wins, else the one with the most waves per CU.  One LDS stage per
+        // wave unless two are asked for: measured on MI355X, the waves sharing
+        // a SIMD hide each other's transfers, and a second stage (which halves
+        // the chunk that fits) was slower on every workload but the longest
+        // rows (stage-3: 102.5 vs 110.8 us; base stage-3: 319 vs 370 us).
+        const long long total_waves = (long long)p.tiles * p.B1 * W;
+        const long long need = (total_waves + cus - 1) / cus;
+        const int target = (int)(need < vgpr_waves_per_cu ? need : vgpr_waves_per_cu);
+        const int cap_ch = (L + ew - 1) / ew * ew;
+        static const int cand[][2] = {{1, 64}, {1, 32}, {1, 16}, {1, 8}, {2, 64}, {2, 32}, {2, 16}, {2, 8}};
+        int best = -1, best_st = 2, best_per_cu = -1;
+        for (const auto& c : cand) {
+            if (stages_hint == 1 || stages_hint == 2) {
+                if (c[0] != stages_hint) continue;
+            }
+            stages = c[0];
+            const int cc = c[1] < cap_ch ? c[1] : cap_ch;
+            const int tot = lds_total(1, cc, grp);
+            if (tot > kLdsCap) continue;
+            const int per_cu = kLdsCap / ((tot + kLdsUnit - 1) / kLdsUnit * kLdsUnit) * per_wg;
+            if (per_cu >= target) {
+                best = cc;
+                best_st = c[0];
+                break;
+            }
+            if (per_cu > best_per_cu) {
+                best_per_cu = per_cu;
+                best = cc;
+                best_st = c[0];
+            }
+        }
+        if (best < 0) return false;
+        ch = best;
+        stages = best_st;
+    }
+    // shrink the chunk until one workgroup of cw = 1 fits
     while (lds_total(1, ch, grp) > kLdsCap) {
         if (mode != 0 && ch > 8) ch /= 2;
         else return false;
@@ -122,12 +176,10 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     // channel tiles per workgroup sharing one B/C stage: the choice that needs
     // the fewest rounds of resident waves (all pieces must then stage the same
     // chunk sequence, so only without carries and with equal pieces)
-    const int vgpr_waves_per_cu = p.ns <= 8 ? 12 : 8;
-    const int cus = device_cus();
     int best_cw = 1, best_per_cu = 1;
     long long best_rounds = -1;
     for (int cw = 1; cw <= 4; cw *= 2) {
-        if (cw > 1 && (carry || S % W || cw * W > kMaxWaves || p.tiles < cw)) break;
+        if (cw > 1 && (mode == 1 || carry || S % W || cw * W > kMaxWaves || p.tiles < cw)) break;
         const int tot = lds_total(cw, ch, grp);
         if (tot > kLdsCap) break;
         const int alloc = (tot + kLdsUnit - 1) / kLdsUnit * kLdsUnit;
@@ -146,6 +198,8 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
         }
     }
     p.cw = best_cw;
+    p.stages = mode == 1 ? stages : 1;
+    p.wsplit = wsplit;
     p.tgroups = (p.tiles + p.cw - 1) / p.cw;
     p.waves = W;
     p.piece = piece;
@@ -154,7 +208,7 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     p.mode = mode;
     p.lds_bytes = lds_total(p.cw, ch, grp);
     p.group_bytes = grp;
-    p.bc_bytes = bc_bytes(ch, mode);
+    p.bc_bytes = mode == 1 ? 0 : bc_bytes(ch, mode);  // mode 1: inside each wave's own area
     p.bc_dma = mode == 0 && p.bc_wide ? 1 : 0;
     p.bcr_off = 2 * ch * p.ns * (int)sizeof(float);
     xd_bytes(ch, mode, xsb, dsb, xrs, drs);
@@ -162,6 +216,8 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     p.drs = drs;
     p.xs_bytes = xsb;
     p.ds_bytes = dsb;
+    p.rb_rs = mode == 1 ? rb_rs_of(ch) : 0;
+    p.rb_bytes = mode == 1 ? rb_bytes_of(ch) : 0;
     // Staggered start.  Whole-row staging loads everything up front; when the
     // whole grid is resident at once, every wave would otherwise wait for the
     // entire input to arrive before its first step.  Delaying dispatch round r

@@ -34,7 +34,11 @@
 //                global->LDS transfers, all in flight at once;
 //      mode 1 -- tiles of even-length rows: 4-byte direct transfers into LDS
 //                rows padded to an odd number of words (no bank conflicts when
-//                the 64 lanes read one column);
+//                the 64 lanes read one column), in groups of four or sixteen
+//                transfers with no lane masks; with two stages per wave the
+//                transfers of chunk k+1 (x, delta and the raw B/C rows) are in
+//                flight while chunk k computes, and y of chunk k is stored
+//                after chunk k+1 has landed, so no wait covers a store;
 //      mode 2 -- element loads (any shape), 16 per lane in flight.
 //    B and C become float32 [t][n] in LDS; y overwrites delta in LDS and is
 //    stored with wide coalesced stores.
@@ -70,6 +74,17 @@ struct ScanWave {
     float* bs;
     float* cs;
     IO* braw;  // mode 0 with bc_dma: raw B then C of one sample, [N][L] each
+    // mode 1: the two stages of this wave (x tile, delta/y tile, raw B/C rows,
+    // stage i at own1 + i * sb1) and the x / delta offsets each was filled with
+    // (scalars, not arrays: a run-time index would put an array in scratch)
+    char* own1;
+    int sb1;
+    int xo0, xo1, do0, do1;
+    __device__ __forceinline__ IO* xs_of(int i) const { return reinterpret_cast<IO*>(own1 + i * sb1); }
+    __device__ __forceinline__ IO* ds_of(int i) const { return reinterpret_cast<IO*>(own1 + i * sb1 + p.xs_bytes); }
+    __device__ __forceinline__ IO* rb_of(int i) const {
+        return reinterpret_cast<IO*>(own1 + i * sb1 + p.xs_bytes + p.ds_bytes);
+    }
     // geometry of the staged chunk: value at position q of this lane's row is
     // xs[lane*xrs + q - xoff], ds[lane*drs + q - doff]; B/C at bs[(q-boff)*NS + n]
     int xrs, xoff, drs, doff, boff;
@@ -87,6 +102,14 @@ struct ScanWave {
         bs = bshared;
         cs = bshared + p.ch * NS;
         braw = reinterpret_cast<IO*>(reinterpret_cast<char*>(bshared) + p.bcr_off);
+        if constexpr (MODE == 1) {
+            // own area: [x | delta | raw B/C] per stage, then float32 B/C (one wave per group)
+            own1 = own;
+            sb1 = p.xs_bytes + p.ds_bytes + p.rb_bytes;
+            xo0 = xo1 = do0 = do1 = 0;
+            bs = reinterpret_cast<float*>(own + p.stages * sb1);
+            cs = bs + p.ch * NS;
+        }
     }
 
     // States n >= N stay zero in B and C for the whole kernel (the first
@@ -204,28 +227,43 @@ struct ScanWave {
         }
     }
 
-    // mode 1: rows x positions [lo, hi) (lo, hi multiples of the elements per
-    // 4-byte word) by 4-byte direct transfers into LDS rows of `rs` elements.
-    // Lane-contiguous LDS words, per-lane global addresses; words outside the
-    // valid rows are not transferred (never read).
-    __device__ __forceinline__ void dma_tile(const IO* g, IO* l, int rs, int lo, int hi, int L) {
+    // Rows x positions [lo, hi) of a [rows, L] slab (lo, hi multiples of the
+    // elements per 4-byte word) by 4-byte direct transfers into LDS rows of
+    // `rs` elements: LDS word e = k * 64 + lane of instruction k holds word
+    // e mod rsw of row e / rsw.  Every lane of every instruction transfers (no
+    // lane masks, so sixteen instructions share one LDS base): a slot past
+    // the valid rows or words re-reads an in-bounds word of this tile (its
+    // byte offset is clamped to the last valid word), and such slots are never
+    // read.  A valid word's offset never exceeds that clamp.  Instructions
+    // go in whole groups of four (the planner allocates tiles in 1 KB units),
+    // sixteen per LDS base where they fill one.
+    __device__ __forceinline__ void dma_tile(const IO* g, IO* l, int rs, int lo, int hi, int L, int rows) {
         constexpr int ew = 4 / (int)sizeof(IO);
-        const int rsw = rs / ew;        // words per LDS row (odd)
+        const int rsw = rs / ew;        // words per LDS row
         const int nw = (hi - lo) / ew;  // words to move per row
+        if (rows <= 0 || nw <= 0) return;
+        const int ninst = ((rows * rsw + kWave - 1) / kWave + 3) & ~3;
         const float inv = 1.0f / (float)rsw;
+        const uint32_t rowb = (uint32_t)L * (uint32_t)sizeof(IO);
+        const uint32_t maxoff = __umul24((uint32_t)(rows - 1), rowb) + (uint32_t)(nw - 1) * 4u;
+        const char* gb = reinterpret_cast<const char*>(g + lo);
         char* lb = reinterpret_cast<char*>(l);
-        // 64 words per instruction, rsw instructions per tile, sixteen per LDS base
-        for (int k0 = 0; k0 < rsw; k0 += 16) {
+        auto one = [&](int kk, auto kc, char* lk) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            const int e = kk * kWave + lane;
+            const int r = div_small(e, inv);
+            const int w = e - r * rsw;
+            const uint32_t off = min(__umul24((uint32_t)r, rowb) + (uint32_t)w * 4u, maxoff);
+            dma_at<4, k * 256>(gb + off, lk);
+        };
+        int k0 = 0;
+        for (; k0 + 16 <= ninst; k0 += 16) {
             char* lk = lb + k0 * 256;
-            static_for<16>([&](auto kc) {
-                constexpr int k = decltype(kc)::value;
-                if (k0 + k < rsw) {
-                    const int e = (k0 + k) * kWave + lane;
-                    const int r = div_small(e, inv);
-                    const int w = e - r * rsw;
-                    if (r < nrows && w < nw) dma_at<4, k * 256>(g + (size_t)r * L + lo + w * ew, lk);
-                }
-            });
+            static_for<16>([&](auto kc) { one(k0 + decltype(kc)::value, kc, lk); });
+        }
+        for (; k0 < ninst; k0 += 4) {
+            char* lk = lb + k0 * 256;
+            static_for<4>([&](auto kc) { one(k0 + decltype(kc)::value, kc, lk); });
         }
     }
 
@@ -296,7 +334,7 @@ struct ScanWave {
         const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
         const IO* bg = static_cast<const IO*>(p.Bm) + (size_t)b * N * L;
         const IO* cg = static_cast<const IO*>(p.Cm) + (size_t)b * N * L;
-        if constexpr (MODE != 0) {
+        if constexpr (MODE == 2) {
             if (p.pad_in && t0 == 0) row_mean(xg);
         }
         if constexpr (MODE == 0) {
@@ -315,25 +353,7 @@ struct ScanWave {
             }
             wait_vmem();
             wave_lds_sync();
-        } else if constexpr (MODE == 1) {
-            constexpr int ew = 4 / (int)sizeof(IO);
-            xrs = p.xrs; drs = p.drs;
-            // padded positions [qa, qb) needed, i.e. u row indices [qa - sh, qb - sh)
-            int qa = (CONV ? t0 - p.P : t0) - sh;
-            int qb = (CONV ? t0 + len + KW - 1 - p.P : t0 + len) - sh;
-            qa = max(qa, 0) / ew * ew;
-            qb = (min(qb, XL) + ew - 1) / ew * ew;
-            xoff = qa + sh;
-            const int da = t0 / ew * ew;
-            const int db = (t0 + len + ew - 1) / ew * ew;
-            doff = da;
-            boff = t0;  // B/C rows hold exactly [t0, t0 + len): ch rows are allocated
-            if (qb > qa) dma_tile(xg, xs, xrs, qa, qb, XL);
-            dma_tile(dg, ds, drs, da, db, L);
-            if (!params_loaded) load_params();
-            if (own_bc) stage_bc(bg, cg, t0, len, false);
-            wait_vmem();
-        } else {
+        } else if constexpr (MODE == 2) {
             xrs = p.xrs; drs = p.drs;
             const int lo = (CONV ? t0 - p.P : t0) - sh;  // u row index of LDS column 0
             xoff = lo + sh;
@@ -362,29 +382,198 @@ struct ScanWave {
         return acc;
     }
 
-    // Fused aux pad, chunked rows: float64 index-order sum of this lane's whole
-    // unpadded row, streamed through the x stage before the sample's first chunk.
+    // Fused aux pad, element-load staging: float64 index-order sum of this
+    // lane's whole unpadded row, streamed through the x stage before the
+    // sample's first chunk.
     __device__ __forceinline__ void row_mean(const IO* xg) {
-        constexpr int ew = 4 / (int)sizeof(IO);
         const int XL = p.xrow;
         const int step = p.ch;
         double acc = 0.0;
         for (int c0 = 0; c0 < XL; c0 += step) {
             const int cl = min(step, XL - c0);
-            int lo = c0;
-            if constexpr (MODE == 1) {
-                lo = c0 / ew * ew;
-                const int hi = (c0 + cl + ew - 1) / ew * ew;
-                dma_tile(xg, xs, p.xrs, lo, min(hi, XL), XL);
-                wait_vmem();
-            } else {
-                stage_rows(xg, xs, p.xrs, c0, cl, XL);
-            }
+            stage_rows(xg, xs, p.xrs, c0, cl, XL);  // positions [c0, c0 + cl) -> columns [0, cl)
             wave_lds_sync();
-            if (lane < nrows) acc = sum_in_order(xs + lane * p.xrs + c0 - lo, cl, acc);
+            if (lane < nrows) acc = sum_in_order(xs + lane * p.xrs, cl, acc);
             wave_lds_sync();
         }
         mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+    }
+
+    // ------------------------------------------------------------ mode 1 pipeline
+    // Put the transfers of chunk (sample b, positions [t0, t0 + len)) into
+    // stage i: the x tile with its conv halo, the delta tile and the raw B and
+    // C rows, each word-aligned; nothing is waited for.
+    __device__ __forceinline__ void issue1(int b, int t0, int len, int i) {
+        constexpr int ew = 4 / (int)sizeof(IO);
+        const int L = p.L, D = p.D, N = p.N, XL = p.xrow;
+        const int sh = p.pad_in ? 1 : 0;  // padded position q reads u row index q - sh
+        const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + d0) * XL;
+        const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + d0) * L;
+        const IO* bg = static_cast<const IO*>(p.Bm) + (size_t)b * N * L;
+        const IO* cg = static_cast<const IO*>(p.Cm) + (size_t)b * N * L;
+        // padded positions [qa, qb) needed, i.e. u row indices [qa - sh, qb - sh)
+        int qa = (CONV ? t0 - p.P : t0) - sh;
+        int qb = (CONV ? t0 + len + KW - 1 - p.P : t0 + len) - sh;
+        qa = max(qa, 0) / ew * ew;
+        qb = (min(qb, XL) + ew - 1) / ew * ew;
+        const int da = t0 / ew * ew;
+        const int db = (t0 + len + ew - 1) / ew * ew;
+        if (i) {
+            xo1 = qa + sh;
+            do1 = da;
+        } else {
+            xo0 = qa + sh;
+            do0 = da;
+        }
+        // the stage was last read by LDS instructions of this wave (y stores);
+        // they have completed before any transfer can write it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (qb > qa) dma_tile(xg, xs_of(i), p.xrs, qa, qb, XL, nrows);
+        dma_tile(dg, ds_of(i), p.drs, da, db, L, nrows);
+        IO* rb = rb_of(i);
+        dma_tile(bg, rb, p.rb_rs, da, db, L, N);
+        dma_tile(cg, rb + p.rb_bytes / 2 / (int)sizeof(IO), p.rb_rs, da, db, L, N);
+        if (!params_loaded) load_params();
+    }
+
+    // Raw B/C rows of stage i -> float32 [q - t0][n] for q in [t0, t0 + len).
+    __device__ __forceinline__ void widen1(int t0, int len, int i) {
+        const int N = p.N, rs = p.rb_rs;
+        const IO* rb = rb_of(i) + t0 - (i ? do1 : do0);
+        const IO* rc = rb + p.rb_bytes / 2 / (int)sizeof(IO);
+        const int tot = N * len;
+        const float inv = 1.0f / (float)len;
+        for (int e = lane; e < tot; e += kWave) {
+            const int n = div_small(e, inv);
+            const int q = e - n * len;
+            bs[q * NS + n] = to_f32(rb[n * rs + q]);
+            cs[q * NS + n] = to_f32(rc[n * rs + q]);
+        }
+    }
+
+    // Point the compute / store geometry at stage i holding positions from t0.
+    __device__ __forceinline__ void use1(int i, int t0) {
+        xs = xs_of(i);
+        ds = ds_of(i);
+        xrs = p.xrs;
+        drs = p.drs;
+        xoff = i ? xo1 : xo0;
+        doff = i ? do1 : do0;
+        boff = t0;  // B/C rows hold exactly [t0, t0 + len): ch rows are allocated
+    }
+
+    // Fused aux pad: float64 index-order sum of this lane's whole unpadded row
+    // of sample b, streamed through the x areas of the stages (with two, the
+    // transfer of piece k+1 is in flight while piece k is summed).  The stages
+    // must be free.
+    __device__ __forceinline__ void mean1(int b) {
+        constexpr int ew = 4 / (int)sizeof(IO);
+        const int XL = p.xrow, step = p.ch;
+        const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * p.D + d0) * XL;
+        auto issue = [&](int c0, int i) __attribute__((always_inline)) {
+            const int lo = c0 / ew * ew;
+            const int hi = min((c0 + min(step, XL - c0) + ew - 1) / ew * ew, XL);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            dma_tile(xg, xs_of(i), p.xrs, lo, hi, XL, nrows);
+        };
+        double acc = 0.0;
+        const int flip = p.stages == 2 ? 1 : 0;
+        int i = 0;
+        issue(0, 0);
+        for (int c0 = 0; c0 < XL; c0 += step, i ^= flip) {
+            wait_vmem();
+            wave_lds_sync();
+            if (flip && c0 + step < XL) issue(c0 + step, i ^ 1);
+            const int cl = min(step, XL - c0);
+            if (lane < nrows) acc = sum_in_order(xs_of(i) + lane * p.xrs + c0 - c0 / ew * ew, cl, acc);
+            if (!flip && c0 + step < XL) {
+                wave_lds_sync();
+                issue(c0 + step, 0);
+            }
+        }
+        wave_lds_sync();
+        mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+    }
+
+    // Folded positions [sa, sb) of row b1 through the stages.  Two stages, per
+    // chunk: wait for its transfers, store the previous chunk's y (from the
+    // other stage), refill the other stage with the next chunk, widen B/C,
+    // compute.  A chunk that starts a sample with the fused pad is not
+    // prefetched: the row mean needs both stages first.  One stage: wait,
+    // widen, compute, store, then fetch the next chunk.
+    __device__ __forceinline__ void run1(bool out, int sa, int sb, float (&h)[NS], float& sd2) {
+        if (sa >= sb) return;
+        const int L = p.L;
+        const bool two = p.stages == 2;
+        // chunk cursor: sample j of the folded row, positions [t0, t0 + len)
+        int s = sa;
+        int j = s / L;
+        int t0 = s - j * L;
+        auto len_at = [&](int ss, int tt) __attribute__((always_inline)) { return min(min(p.ch, L - tt), sb - ss); };
+        int len = len_at(s, t0);
+        const int bb = b1 * p.B2;
+        int i = 0;
+        if (p.pad_in && t0 == 0) mean1(bb + j);
+        issue1(bb + j, t0, len, i);
+        int pb = -1, pt0 = 0, plen = 0;  // chunk whose y waits in stage i ^ 1
+        while (true) {
+            wait_vmem();  // this chunk has landed; so have the stores issued before its transfers
+            wave_lds_sync();
+            if (pb >= 0) {
+                use1(i ^ 1, pt0);
+                store(pb, pt0, plen);
+                pb = -1;
+            }
+            const int sn = s + len;
+            const bool more = sn < sb;
+            int nj = j, nt0 = t0 + len;
+            if (nt0 == L) {
+                nt0 = 0;
+                ++nj;
+            }
+            const int nlen = more ? len_at(sn, nt0) : 0;
+            const bool pre = two && more && !(p.pad_in && nt0 == 0);
+            if (pre) issue1(bb + nj, nt0, nlen, i ^ 1);
+            widen1(t0, len, i);
+            wave_lds_sync();
+            use1(i, t0);
+            if (out) chunk<true>(t0, len, h, sd2);
+            else chunk<false>(t0, len, h, sd2);
+            wave_lds_sync();
+            if (out) {
+                if (two) {
+                    pb = bb + j;
+                    pt0 = t0;
+                    plen = len;
+                } else {
+                    store(bb + j, t0, len);
+                }
+            }
+            if (!more) break;
+            s = sn;
+            j = nj;
+            t0 = nt0;
+            len = nlen;
+            if (two) i ^= 1;
+            if (!pre) {
+                // not prefetched: store the pending y, take the row mean when
+                // the chunk starts a sample with the fused pad, then fetch it
+                if (pb >= 0) {
+                    use1(i ^ 1, pt0);
+                    store(pb, pt0, plen);
+                    pb = -1;
+                }
+                if (p.pad_in && t0 == 0) {
+                    wait_vmem();
+                    mean1(bb + j);
+                }
+                issue1(bb + j, t0, len, i);
+            }
+        }
+        if (pb >= 0) {
+            use1(i, pt0);
+            store(pb, pt0, plen);
+        }
     }
 
     // Store y for positions [t0, t0 + len) of sample b (y sits in ds).  With
@@ -410,22 +599,25 @@ struct ScanWave {
         const int hi = (sw && t0 + len == L) ? L - 1 : t0 + len;
         if (sw && t0 == 0 && lane < nrows) y0 = ds[lane * drs + 0 - doff];
         if constexpr (MODE == 1) {
-            // whole 4-byte words inside [lo, hi), single elements at the edges
+            // whole 4-byte words inside [lo, hi), single elements at the
+            // edges; each lane writes its own row (immediate offsets, no
+            // per-word index arithmetic)
             constexpr int ew = 4 / (int)sizeof(IO);
             const int ta = (lo + ew - 1) / ew * ew;
             const int tb = max(ta, hi / ew * ew);
-            if (tb > ta) {
-                const int nw = (tb - ta) / ew;
-                const int total = nrows * nw;
-                const float inv = 1.0f / (float)nw;
-                for (int e = lane; e < total; e += kWave) {
-                    const int r = div_small(e, inv);
-                    const int w = e - r * nw;
-                    const uint32_t v = *reinterpret_cast<const uint32_t*>(&ds[r * drs + ta - doff + w * ew]);
-                    *reinterpret_cast<uint32_t*>(&yg[(size_t)r * L + ta + w * ew]) = v;
-                }
-            }
             if (lane < nrows) {
+                const int nw = (tb - ta) / ew;
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(ds + lane * drs + ta - doff);
+                uint32_t* dst = reinterpret_cast<uint32_t*>(yg + (size_t)lane * L + ta);
+                int w = 0;
+                for (; w + 4 <= nw; w += 4) {
+                    const uint32_t v0 = src[w], v1 = src[w + 1], v2 = src[w + 2], v3 = src[w + 3];
+                    dst[w] = v0;
+                    dst[w + 1] = v1;
+                    dst[w + 2] = v2;
+                    dst[w + 3] = v3;
+                }
+                for (; w < nw; ++w) dst[w] = src[w];
                 for (int t = lo; t < min(ta, hi); ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
                 for (int t = tb; t < hi; ++t) yg[(size_t)lane * L + t] = ds[lane * drs + t - doff];
             }
@@ -646,21 +838,25 @@ struct ScanWave {
     // out: write y (phase 2); else accumulate the aggregate (phase 1).  One
     // call site, so the staging code is inlined once.
     __device__ __forceinline__ void run(bool out, int sa, int sb, float (&h)[NS], float& sd2) {
-        const int L = p.L;
-        int s = sa;
-        bool first = true;
-        while (s < sb) {
-            const int j = s / L;
-            const int t0 = s - j * L;
-            const int len = min(min(p.ch, L - t0), sb - s);
-            const int b = b1 * p.B2 + j;
-            stage(b, t0, len, first);
-            first = false;
-            if (out) chunk<true>(t0, len, h, sd2);
-            else chunk<false>(t0, len, h, sd2);
-            wave_lds_sync();
-            if (out) store(b, t0, len);
-            s += len;
+        if constexpr (MODE == 1) {
+            run1(out, sa, sb, h, sd2);
+        } else {
+            const int L = p.L;
+            int s = sa;
+            bool first = true;
+            while (s < sb) {
+                const int j = s / L;
+                const int t0 = s - j * L;
+                const int len = min(min(p.ch, L - t0), sb - s);
+                const int b = b1 * p.B2 + j;
+                stage(b, t0, len, first);
+                first = false;
+                if (out) chunk<true>(t0, len, h, sd2);
+                else chunk<false>(t0, len, h, sd2);
+                wave_lds_sync();
+                if (out) store(b, t0, len);
+                s += len;
+            }
         }
     }
 };
@@ -683,14 +879,21 @@ void scan_kernel(ScanParams p) {
     // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
     // giving each XCD a contiguous run of (row, tile) items keeps the B/C of a
     // folded row in one XCD's L2.
-    const int G = p.tgroups * p.B1;
+    // With wsplit every piece of a folded row is a workgroup of its own
+    // (pieces on sample starts need no exchange), consecutive in this order.
+    const int G = p.tgroups * p.B1 * (p.wsplit ? p.waves : 1);
     int g = blockIdx.x;
     if ((G & 7) == 0) g = (g & 7) * (G >> 3) + (g >> 3);
+    int wp = 0;
+    if (p.wsplit) {
+        wp = g % p.waves;
+        g /= p.waves;
+    }
     const int b1 = g / p.tgroups;
     const int tg = g - b1 * p.tgroups;
-    const int wp = wave / p.cw;         // piece of the folded row
-    const int wc = wave - wp * p.cw;    // channel tile within the group
-    char* grp = smem + (size_t)wp * p.group_bytes;
+    if (!p.wsplit) wp = wave / p.cw;    // piece of the folded row
+    const int wc = wave - (p.wsplit ? 0 : wp) * p.cw;  // channel tile within the group
+    char* grp = smem + (size_t)(p.wsplit ? 0 : wp) * p.group_bytes;
     ScanWave<IO, NS, KW, CONV, SP, SILU, MODE> w(p, lane, (tg * p.cw + wc) * kWave, b1,
                                  grp + p.bc_bytes + (size_t)wc * (p.xs_bytes + p.ds_bytes),
                                  reinterpret_cast<float*>(grp), wc);
@@ -763,8 +966,9 @@ hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
             (void)hipGetLastError();  // do not leave a stale error for the launch check
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)(p.tgroups * p.B1)), dim3((unsigned)(kWave * p.cw * p.waves)),
-                       (size_t)p.lds_bytes, stream, p);
+    const unsigned grid = (unsigned)(p.tgroups * p.B1 * (p.wsplit ? p.waves : 1));
+    const unsigned block = (unsigned)(kWave * p.cw * (p.wsplit ? 1 : p.waves));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(block), (size_t)p.lds_bytes, stream, p);
     return hipGetLastError();
 }
 

@@ -196,9 +196,10 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
     int waves_hint = 0, ch_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_WAVES")) waves_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_CHUNK")) ch_hint = std::atoi(e);
-    int stagger_hint = -1;
+    int stagger_hint = -1, stages_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_STAGGER")) stagger_hint = std::atoi(e);
-    if (!sfm::plan_scan(p, eb, waves_hint, ch_hint, stagger_hint))
+    if (const char* e = std::getenv("SFM_SCAN_STAGES")) stages_hint = std::atoi(e);
+    if (!sfm::plan_scan(p, eb, waves_hint, ch_hint, stagger_hint, stages_hint))
         return fail(SFM_ERR_UNSUPPORTED, "sfm_selective_scan_fwd: no launch plan fits LDS for this shape");
     return hip_status(sfm::launch_scan(p, io_dtype, static_cast<hipStream_t>(stream)), "sfm_selective_scan_fwd");
 }
@@ -250,14 +251,17 @@ sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, in
     int waves_hint = 0, ch_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_WAVES")) waves_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_CHUNK")) ch_hint = std::atoi(e);
-    int stagger_hint = -1;
+    int stagger_hint = -1, stages_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_STAGGER")) stagger_hint = std::atoi(e);
-    if (!sfm::plan_scan(p, io_bytes(io_dtype), waves_hint, ch_hint, stagger_hint))
+    if (const char* e = std::getenv("SFM_SCAN_STAGES")) stages_hint = std::atoi(e);
+    if (!sfm::plan_scan(p, io_bytes(io_dtype), waves_hint, ch_hint, stagger_hint, stages_hint))
         return fail(SFM_ERR_UNSUPPORTED, "sfm_scan_plan_string: no launch plan fits LDS");
     snprintf(buf, (size_t)cap,
-             "mode=%d ch=%d pieces=%d piece=%d carry=%d cw=%d ns=%d lds=%d grid=%lld block=%d stagger=%d/%d",
+             "mode=%d ch=%d pieces=%d piece=%d carry=%d cw=%d ns=%d lds=%d grid=%lld block=%d stagger=%d/%d "
+             "stages=%d",
              p.mode, p.ch, p.waves, p.piece, p.need_carry, p.cw, p.ns, p.lds_bytes,
-             (long long)p.tgroups * p.B1, 64 * p.cw * p.waves, p.stagger_ticks, p.stagger_period);
+             (long long)p.tgroups * p.B1 * (p.wsplit ? p.waves : 1), 64 * p.cw * (p.wsplit ? 1 : p.waves),
+             p.stagger_ticks, p.stagger_period, p.stages);
     return ok();
 }
 

@@ -33,8 +33,12 @@ struct ScanParams {
     int piece;       // folded positions per wave
     int need_carry;  // 1 when some piece starts inside a sample
     int ch;          // positions per LDS chunk
-    int mode;        // staging: 0 whole rows (16-byte DMA), 1 tiles (4-byte DMA), 2 element loads
+    int mode;        // staging: 0 whole rows (16-byte DMA), 1 double-buffered tiles (4-byte DMA), 2 element loads
     int xrs, drs;    // LDS row strides (elements) of the x and delta/y stages
+    int stages;      // mode 1: LDS stages per wave (2: the next chunk's transfers overlap this chunk)
+    int wsplit;      // 1: each piece of a folded row is a workgroup of its own (no carries)
+    int rb_rs;       // mode 1: row stride (elements) of a stage's raw B/C rows
+    int rb_bytes;    // mode 1: bytes of one stage's raw B/C area (B rows, then C rows at rb_bytes / 2)
     int bc_wide;     // B/C blocks of whole samples are 16-byte aligned
     int bc_dma;      // mode 0: B/C of a sample arrive by direct transfer into a raw area, then widen in LDS
     int bcr_off;     // byte offset of that raw [2][N][L] io area inside the group's B/C region
@@ -48,7 +52,8 @@ struct ScanParams {
 // Fills the plan fields; waves_hint / ch_hint <= 0 select automatically,
 // stagger_hint < 0 selects automatically, 0 turns the staggered start off and
 // > 0 sets the delay per dispatch round in 10 ns ticks.
-bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint = -1);
+// stages_hint (mode 1): 1 or 2 forces the LDS stages per wave, else automatic.
+bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint = -1, int stages_hint = 0);
 hipError_t launch_scan(const ScanParams& p, int io_dtype, hipStream_t stream);
 // per-(io type, state count) kernel sets, one translation unit each
 hipError_t launch_scan_f32_n4(const ScanParams& p, hipStream_t s);

@@ -190,3 +190,20 @@ def test_aux_pad_bwd_validation(lib):
     assert f(P, 2 * P, 2, 3, 4, 5, None) == DTYPE
     assert f(P, P + 16, 2, 3, 4, 0, None) == ALIAS
     assert f(P, P + 8, 2, 3, 4, 0, None) == ALIGN
+
+
+def test_build_scratch_guard_parses_resource_remarks():
+    """The build rejects forward kernels that keep state in scratch memory."""
+    from selective_scan_segmented_amd import build as b
+    ok = ("x.hip:1:1: remark: Function Name: k_ok [-Rpass-analysis=kernel-resource-usage]\n"
+          "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+          "x.hip:1:1: remark:     Dynamic Stack: False [-Rpass-analysis=kernel-resource-usage]\n")
+    bad = ("x.hip:9:1: remark: Function Name: k_bad [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 512 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:9:1: remark:     Dynamic Stack: False [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:12:1: remark: Function Name: k_dyn [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:12:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:12:1: remark:     Dynamic Stack: True [-Rpass-analysis=kernel-resource-usage]\n")
+    assert b.scratch_users(ok) == []
+    assert b.scratch_users(ok + bad) == ["k_bad (512 bytes/lane)", "k_dyn (dynamic stack)"]
+    assert "bwd.hip" in b.SPILL_OK and "scan_bf16_n8.hip" not in b.SPILL_OK

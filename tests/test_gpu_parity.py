@@ -483,3 +483,55 @@ def test_fused_pad_rejects_short_rows():
     rc = lib.sfm_selective_scan_fwd_ex(u.data_ptr(), u.data_ptr(), A.data_ptr(), BC.data_ptr(), BC.data_ptr(),
                                        None, None, 1, None, None, 0, 0, 0, A.data_ptr(), 2, 1, 4, 2, 2, 0, 1, None)
     assert rc == 2  # SFM_ERR_SHAPE: SFM_FUSE_PAD needs L >= 3
+
+
+# --------------------------------------------- double-buffered chunk staging
+
+@pytest.mark.parametrize("stages", [1, 2])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("ch", [6, 7, 16])
+def test_chunk_pipeline_against_oracle(ch, io, stages):
+    """Tile staging with forced chunk sizes (odd ones start chunks mid-word in
+    bf16) and one or two LDS stages per wave: fused pad/swap with two samples
+    per wave (B2 = 16 over 8 pieces), unfused with pieces that cut samples
+    (carries), a partial channel tile."""
+    import torch
+    say(f"chunk pipeline ch={ch} io={io} stages={stages}")
+    B, D, N, T, K, P = 16, 72, 8, 58, 4, 1
+    L = T + 2
+    r = np.random.default_rng(ch * 31 + len(io))
+    f = lambda *s: r.standard_normal(s).astype(np.float32)
+    x, delta, Bm, Cm = f(B, D, T), f(B, D, L), f(B, N, L), f(B, N, L)
+    cast = synth.f32_to_bf16_bits if io == "bf16" else (lambda a: a)
+    x, delta, Bm, Cm = map(cast, (x, delta, Bm, Cm))
+    A = (-r.uniform(0.5, 4.0, (D, N))).astype(np.float32)
+    Dk, db = f(D), r.uniform(-4, -1, D).astype(np.float32)
+    cw = r.uniform(-0.5, 0.5, (D, K)).astype(np.float32)
+    T_ = lambda a: torch.from_numpy(a).cuda()
+    xd, dd, Bd, Cd = map(to_dev, (x, delta, Bm, Cm))
+    up = lambda a: synth.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+    xp64 = oracle.aux_pad(up(x), io)
+    want = oracle.layer(xp64, up(delta), A, up(Bm), up(Cm), Dk, db, cw, pad_left=P)
+    saved = {k: os.environ.pop(k, None) for k in ("SFM_SCAN_CHUNK", "SFM_SCAN_WAVES", "SFM_SCAN_STAGES")}
+    try:
+        os.environ["SFM_SCAN_CHUNK"] = str(ch)
+        os.environ["SFM_SCAN_STAGES"] = str(stages)
+        plan = sfm.sfm_scan_plan_string(1, B, D, N, L, K, io, 3)
+        assert "mode=1" in plan and f"stages={stages}" in plan
+        fused = sfm.sfm_selective_scan_fwd_ex(xd, dd, T_(A), Bd, Cd, T_(Dk), T_(db), conv_w=T_(cw),
+                                              conv_pad_left=P, B2=B, flags=3)
+        xp = sfm.sfm_aux_pad_swap(xd, mode="pad")
+        sync()
+        assert np.array_equal(from_dev(xp), xp64)
+        os.environ["SFM_SCAN_WAVES"] = "3"
+        assert "carry=1" in sfm.sfm_scan_plan_string(1, B, D, N, L, K, io, 0)
+        carried = sfm.sfm_selective_scan_fwd(xp, dd, T_(A), Bd, Cd, T_(Dk), T_(db), conv_w=T_(cw),
+                                             conv_pad_left=P, B2=B)
+        sync()
+    finally:
+        for k, v in saved.items():
+            os.environ.pop(k, None)
+            if v is not None:
+                os.environ[k] = v
+    assert_close(from_dev(fused), oracle.aux_swap(want), io, f"fused ch={ch}")
+    assert_close(from_dev(carried), want, io, f"carried ch={ch}")
