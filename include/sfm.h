@@ -101,6 +101,7 @@ typedef enum { SFM_AUX_PAD = 0, SFM_AUX_SWAP = 1 } sfm_aux_mode;
  * tests, results do not depend on them beyond float32 summation order):
  *   SFM_SCAN_WAVES=w    pieces per folded row (carried state between pieces)
  *   SFM_SCAN_CHUNK=c    positions per LDS chunk (tiled staging)
+ *   SFM_SCAN_STAGES=2   tiled staging double-buffered per wave (default one stage)
  *   SFM_SCAN_STAGGER=t  delay per dispatch round in 10 ns ticks (0 = off) for
  *                       grids that are resident all at once
  */
