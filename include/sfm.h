@@ -179,7 +179,9 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  *   bytes (same B1, B2, D, N, L, conv_k -- 0 without conv -- io_dtype, flags),
  *   owned by the caller, not overlapping anything else; it holds float32 state
  *   checkpoints (every 32/Np positions, Np = N rounded up to 4, 8 or 16) and
- *   the partial sums of the f32 outputs for the duration of the call.  The
+ *   the partial sums of the f32 outputs for the duration of the call; its size
+ *   depends on B1 and B2 only through B1*B2 (the backward runs one wave per
+ *   sample and channel tile, whatever the fold).  The
  *   library allocates nothing.  The f32 sums are added in a fixed order by a
  *   second kernel (no atomics), so repeated calls give identical bits.
  * flags & SFM_LAYOUT_BLD: channel-last, as the forward: u, delta, dy, du,

@@ -15,7 +15,8 @@
 // crosses from a sample into the one before it in the folded row.
 //
 // Work mapping: one wave per (folded row b1, tile of 64 channels); lanes are
-// channels, the B2 samples of the row run one after the other.  Per sample:
+// channels, the B2 samples of the row run one after the other (the API plans
+// the backward unfolded, B2 = 1: one sample per wave).  Per sample:
 //  * sweep 1 runs the forward recurrence in chunks of Q = 32/N positions and writes
 //    the state entering every chunk (fp32) to a caller-provided workspace;
 //  * sweep 2 visits the chunks in reverse: it re-runs the chunk forward from

@@ -408,8 +408,11 @@ sfm_status bwd_common(const void* u, const void* delta, const float* A, const vo
 
 void fill_bwd(sfm::BwdParams& p, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, const float* conv_w,
               int conv_k, int conv_pad_left, int conv_act, int delta_softplus, int flags) {
-    p.B1 = (int)B1;
-    p.B2 = (int)B2;
+    // The backward runs unfolded: every sample starts from a reset, so a folded
+    // row's samples are independent work, and one wave per (sample, tile)
+    // gives the GPU B2 times the waves of one per (folded row, tile).
+    p.B1 = (int)(B1 * B2);
+    p.B2 = 1;
     p.D = (int)D;
     p.N = (int)N;
     p.L = (int)L;

@@ -155,15 +155,17 @@ def test_bwd_validation(lib):
 
 
 def ws_expect(B1, B2, D, N, L, K):
-    """Workspace floats, each region rounded up to 64: state checkpoints per (folded row,
+    """Workspace floats, each region rounded up to 64: state checkpoints per (sample,
     channel tile, chunk of 32/Np positions, state, lane); partial dB/dC per (tile, sample,
-    position, B|C, state); per-channel partial sums per (folded row, row, channel) with
-    rows dA (N), dD, dbias and, with the conv, dconv_b and dconv_w (K)."""
+    position, B|C, state); per-channel partial sums per (sample, row, channel) with
+    rows dA (N), dD, dbias and, with the conv, dconv_b and dconv_w (K).  The backward
+    runs unfolded, so only B = B1*B2 matters."""
     ns = 4 if N <= 4 else (8 if N <= 8 else 16)
     tiles, q = (D + 63) // 64, 32 // ns
     up = lambda v: (v + 63) // 64 * 64
     kc = N + 2 + (1 + K if K else 0)
-    return 4 * (up(B1 * tiles * ((L + q - 1) // q) * ns * 64) + up(tiles * B1 * B2 * L * 2 * ns) + up(B1 * kc * D))
+    B = B1 * B2
+    return 4 * (up(B * tiles * ((L + q - 1) // q) * ns * 64) + up(tiles * B * L * 2 * ns) + up(B * kc * D))
 
 
 def test_bwd_workspace_size(lib):
@@ -177,6 +179,8 @@ def test_bwd_workspace_size(lib):
     assert f(2, 2, 4, 0, 10, 4, 0, 0, ctypes.byref(out)) == SHAPE
     assert f(2, 2, 4, 4, 10, 4, 9, 0, ctypes.byref(out)) == DTYPE
     assert sfm.sfm_selective_scan_bwd_workspace_size(256, 1, 640, 8, 51, 4, "bf16", 3) == \
+        ws_expect(256, 1, 640, 8, 51, 4)
+    assert sfm.sfm_selective_scan_bwd_workspace_size(64, 4, 640, 8, 51, 4, "bf16", 3) == \
         ws_expect(256, 1, 640, 8, 51, 4)
 
 
