@@ -67,15 +67,27 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     const int P = CONV ? p.P : 0;
     const int sh = p.pad_in ? 1 : 0;  // padded position q reads u row index q - sh
 
-    // staged io elements sit in 4-byte slots (raw bits in the low bytes; see dma_at)
-    uint32_t* xs = reinterpret_cast<uint32_t*>(smem + p.xs_off);    // [64][XW]: column c = position t0 - P + c
-    uint32_t* dls = reinterpret_cast<uint32_t*>(smem + p.ds_off);   // [64][Q]   delta, then ddelta as float32
-    uint32_t* dys = reinterpret_cast<uint32_t*>(smem + p.dys_off);  // [64][Q]   dy
+    // staged io elements sit in 4-byte slots (raw bits in the low bytes; see dma_at).
+    // Two staging buffers, p.stage_bytes apart; xs, dls, dys, braw, hinl point
+    // into the one the current chunk uses (set by use_buf).
+    uint32_t* xs;    // [64][XW]: column c = position t0 - P + c
+    uint32_t* dls;   // [64][Q]   delta, then ddelta as float32
+    uint32_t* dys;   // [64][Q]   dy
+    uint32_t* braw;  // [64] raw B then C of the chunk
+    float* hinl;     // [NS][64] state entering the chunk (reverse sweep)
+    auto buf = [&](int off, int i) __attribute__((always_inline)) { return smem + off + i * p.stage_bytes; };
+    auto use_buf = [&](int i) __attribute__((always_inline)) {
+        xs = reinterpret_cast<uint32_t*>(buf(p.xs_off, i));
+        dls = reinterpret_cast<uint32_t*>(buf(p.ds_off, i));
+        dys = reinterpret_cast<uint32_t*>(buf(p.dys_off, i));
+        braw = reinterpret_cast<uint32_t*>(buf(p.braw_off, i));
+        hinl = reinterpret_cast<float*>(buf(p.hin_off, i));
+    };
+    use_buf(0);
     float* bs = reinterpret_cast<float*>(smem + p.bc_off);  // [Q][NS]
     float* cs = bs + Q * NS;                               // [Q][NS]
     float* red = reinterpret_cast<float*>(smem + p.red_off);  // [64][kRedStride]
     float* dxs = reinterpret_cast<float*>(smem + p.mean_off);  // [64][XW] fp32 dx of the chunk's window
-    uint32_t* braw = reinterpret_cast<uint32_t*>(smem + p.braw_off);  // [64] raw B then C of the chunk
 
     // per-channel parameters
     float A[NS], Dk, db, cw[KW], cb;
@@ -125,17 +137,27 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 dma_at<EB, (k % kPer) * kWave * 4>(addr(r, e - r * COLS), tile + (k / kPer) * kPer * kWave);
             });
         };
-        auto stage = [&](int t0, int cnt, bool with_dy) __attribute__((always_inline)) {
+        // Transfers of chunk (t0, cnt) into staging buffer i; with ck > 0 also the
+        // state entering chunk ck (its checkpoint, [NS][64] floats contiguous in
+        // the workspace, one 4-byte transfer per state).  Nothing is waited for;
+        // the buffer was last read by LDS instructions of this wave, which have
+        // completed before a transfer can write it.
+        auto issue = [&](int t0, int cnt, bool with_dy, int ck, int i) __attribute__((always_inline)) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            uint32_t* xb = reinterpret_cast<uint32_t*>(buf(p.xs_off, i));
+            uint32_t* db_ = reinterpret_cast<uint32_t*>(buf(p.ds_off, i));
+            uint32_t* yb = reinterpret_cast<uint32_t*>(buf(p.dys_off, i));
+            uint32_t* rb = reinterpret_cast<uint32_t*>(buf(p.braw_off, i));
             const IO* dummy = xg;
-            dma_tile(std::integral_constant<int, XW>{}, xs, [&](int r, int c) {
+            dma_tile(std::integral_constant<int, XW>{}, xb, [&](int r, int c) {
                 const int q = t0 - P + c - sh;
                 return (r < nrows && q >= 0 && q < XL) ? xg + (size_t)r * XL + q : dummy;
             });
-            dma_tile(std::integral_constant<int, Q>{}, dls, [&](int r, int c) {
+            dma_tile(std::integral_constant<int, Q>{}, db_, [&](int r, int c) {
                 return (r < nrows && c < cnt) ? dg + (size_t)r * L + t0 + c : dummy;
             });
             if (with_dy) {
-                dma_tile(std::integral_constant<int, Q>{}, dys, [&](int r, int c) {
+                dma_tile(std::integral_constant<int, Q>{}, yb, [&](int r, int c) {
                     const int t = t0 + c;
                     const int ts = (p.swap_dy && L > 1) ? (t == 0 ? L - 1 : (t == L - 1 ? 0 : t)) : t;
                     return (r < nrows && c < cnt) ? yg + (size_t)r * L + ts : dummy;
@@ -151,11 +173,20 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 const IO* src = (e < 2 * half && c < cnt && (e < half || with_dy))
                                     ? (e < half ? bgl : cgl) + (size_t)n * L + t0 + c
                                     : dummy;
-                dma_at<EB, 0>(src, braw);
+                dma_at<EB, 0>(src, rb);
             }
-            wait_vmem();
-            wave_lds_sync();
-            // widen B/C to float32 [c][n]; states n >= N and positions past the sample are zero
+            if (ck > 0) {
+                const float* hsrc = ws + (size_t)ck * NS * kWave + lane;
+                char* hb = buf(p.hin_off, i);
+                static_for<NS>([&](auto nc) {
+                    constexpr int n = decltype(nc)::value;
+                    dma_at<4, n * kWave * 4>(hsrc + n * kWave, hb);
+                });
+            }
+        };
+        // After the chunk in the current buffer has landed: widen B/C to float32
+        // [c][n]; states n >= N and positions past the sample are zero.
+        auto widen = [&](int cnt, bool with_dy) __attribute__((always_inline)) {
             if (lane < Q * NS) {
                 const int c = lane / NS;
                 const int n = lane - c * NS;
@@ -205,19 +236,27 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             dt = SP ? softplus_log2e(v) * kLn2 : v;
         };
 
-        // --- sweep 1: forward, checkpoint the state entering each chunk
+        // --- sweep 1: forward, checkpoint the state entering each chunk.  The
+        // transfers of chunk c+1 go out (into the other buffer) once chunk c has
+        // landed, so they are in flight while chunk c runs.
         float h[NS];
 #pragma unroll
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+        wave_lds_sync();
+        int bi = 0;
+        issue(0, min(Q, L), false, 0, 0);
         for (int c = 0; c < p.nchk; ++c) {
             const int t0 = c * Q;
             const int cnt = min(Q, L - t0);
+            wait_vmem();
+            wave_lds_sync();
             if (c > 0) {
 #pragma unroll
                 for (int n = 0; n < NS; ++n) ws[((size_t)c * NS + n) * kWave + lane] = h[n];
             }
-            wave_lds_sync();
-            stage(t0, cnt, false);
+            if (c + 1 < p.nchk) issue(t0 + Q, min(Q, L - t0 - Q), false, 0, bi ^ 1);
+            use_buf(bi);
+            widen(cnt, false);
             wave_lds_sync();
             for (int i = 0; i < cnt; ++i) {
                 float z, u, v, dt;
@@ -229,24 +268,60 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                     h[n] = (t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dt * kLog2e * A[n]), h[n], bx);
                 }
             }
+            bi ^= 1;
         }
 
-        // --- sweep 2: chunks in reverse
+        // --- sweep 2: chunks in reverse.  Chunk c-1's transfers (with its
+        // entering state) go out once chunk c has landed; chunk c's ddelta (in
+        // its buffer) and finished dx (dxs) leave one chunk later, after that
+        // wait, so no wait covers those stores.
+        auto write_out = [&](int c) __attribute__((always_inline)) {
+            const int t0 = c * Q;
+            const int cnt = min(Q, L - t0);
+            // write this chunk's ddelta and the completed dx positions (coalesced)
+            for (int e = lane; e < kWave * Q; e += kWave) {
+                const int r = e / Q;
+                const int cc = e - r * Q;
+                if (r < nrows && cc < cnt) ddg[(size_t)r * L + t0 + cc] = from_f32<IO>(__uint_as_float(dls[r * Q + cc]));
+            }
+            // dx columns finished in this chunk: padded positions [lo, hi)
+            const int lag = CONV ? KW - 1 - P : 0;
+            const int lo = CONV ? (c == 0 ? 0 : t0 + lag) : t0;
+            const int hi = CONV ? min(L, t0 + cnt + lag) : t0 + cnt;
+            for (int e = lane; e < kWave * XW; e += kWave) {
+                const int r = e / XW;
+                const int cc = e - r * XW;
+                const int q = t0 - P + cc;
+                if (r < nrows && q >= lo && q < hi) dug[(size_t)r * L + q] = from_f32<IO>(dxs[r * XW + cc]);
+            }
+        };
         float G[NS];  // a_{t+1} G_{t+1} carried to position t
 #pragma unroll
         for (int n = 0; n < NS; ++n) G[n] = 0.0f;
         float wdx[KW];  // dx of padded positions t - P + jj, still collecting contributions
 #pragma unroll
         for (int jj = 0; jj < KW; ++jj) wdx[jj] = 0.0f;
+        wait_vmem();  // the checkpoints stored above have landed before they are read back
+        wave_lds_sync();
+        bi = 0;
+        issue((p.nchk - 1) * Q, L - (p.nchk - 1) * Q, true, p.nchk - 1, 0);
+        int pend = -1;  // chunk whose outputs wait in buffer bi ^ 1 and dxs
         for (int c = p.nchk - 1; c >= 0; --c) {
             const int t0 = c * Q;
             const int cnt = min(Q, L - t0);
+            wait_vmem();
             wave_lds_sync();
-            stage(t0, cnt, true);
+            if (pend >= 0) {
+                use_buf(bi ^ 1);
+                write_out(pend);
+            }
+            if (c > 0) issue(t0 - Q, Q, true, c - 1, bi ^ 1);
+            use_buf(bi);
+            widen(cnt, true);
             for (int e = lane; e < kWave * XW; e += kWave) dxs[e] = 0.0f;
             float hin[NS];
 #pragma unroll
-            for (int n = 0; n < NS; ++n) hin[n] = c > 0 ? ws[((size_t)c * NS + n) * kWave + lane] : 0.0f;
+            for (int n = 0; n < NS; ++n) hin[n] = c > 0 ? hinl[n * kWave + lane] : 0.0f;
             wave_lds_sync();
             // re-run the chunk forward, keeping every state
             float hs[Q][NS];
@@ -363,24 +438,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                     for (int jj = 0; jj < KW - 1; ++jj) dxs[lane * XW + jj] = wdx[jj + 1];
                 }
             }
-            wave_lds_sync();
-            // write this chunk's ddelta and the completed dx positions (coalesced)
-            for (int e = lane; e < kWave * Q; e += kWave) {
-                const int r = e / Q;
-                const int cc = e - r * Q;
-                if (r < nrows && cc < cnt) ddg[(size_t)r * L + t0 + cc] = from_f32<IO>(__uint_as_float(dls[r * Q + cc]));
-            }
-            // dx columns finished in this chunk: padded positions [lo, hi)
-            const int lag = CONV ? KW - 1 - P : 0;
-            const int lo = CONV ? (c == 0 ? 0 : t0 + lag) : t0;
-            const int hi = CONV ? min(L, t0 + cnt + lag) : t0 + cnt;
-            for (int e = lane; e < kWave * XW; e += kWave) {
-                const int r = e / XW;
-                const int cc = e - r * XW;
-                const int q = t0 - P + cc;
-                if (r < nrows && q >= lo && q < hi) dug[(size_t)r * L + q] = from_f32<IO>(dxs[r * XW + cc]);
-            }
+            pend = c;
+            bi ^= 1;
         }
+        wave_lds_sync();
+        use_buf(bi ^ 1);
+        write_out(pend);
+        wave_lds_sync();
     }
     if (valid) {
         // this folded row's per-channel sums (rows dA[0..N), dD, dbias, dconv_b, dconv_w[0..K))
@@ -951,7 +1015,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         const char* force = getenv("SFM_BWD_CHUNKED");  // diagnostics: force the chunked kernel
         if (ok && L <= 4096 && off <= 64 * 1024 && (p.cl || !(force && atoi(force) > 0))) {
             p.whole = 1;
-            p.mean_off = p.braw_off = 0;
+            p.mean_off = p.braw_off = p.hin_off = p.stage_bytes = 0;
             p.lds_bytes = off;
             return true;
         }
@@ -961,6 +1025,8 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     const int q = p.q;
     const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 4;
     const int xw = q + kw - 1;
+    // two staging buffers (the next chunk's transfers land while this chunk
+    // runs), each: x window, delta (then ddelta), dy, raw B/C, entering state
     int off = 0;
     p.xs_off = off;
     off += up16(kWave * xw * 4);  // staged io elements take 4-byte slots
@@ -968,14 +1034,18 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     off += up16(kWave * q * 4);
     p.dys_off = off;
     off += up16(kWave * q * 4);
+    p.braw_off = off;  // raw B/C of a chunk: one 64-element transfer
+    off += up16(kWave * 4);
+    p.hin_off = off;
+    off += p.ns * kWave * 4;
+    p.stage_bytes = off;
+    off *= 2;
     p.bc_off = off;
     off += up16(2 * q * p.ns * 4);
     p.red_off = off;
     off += kWave * kRedStride * 4;
     p.mean_off = off;  // fp32 dx window
     off += up16(kWave * xw * 4);
-    p.braw_off = off;  // raw B/C of a chunk: one 64-element transfer
-    off += up16(kWave * 4);
     p.lds_bytes = off;
     return p.lds_bytes <= 64 * 1024;
 }

@@ -44,6 +44,8 @@ struct BwdParams {
     long long pbc_off, pch_off;
     int kc;
     int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, braw_off, lds_bytes;
+    int hin_off;          // chunked kernel: a chunk's entering state [ns][64] f32, staged with the chunk
+    int stage_bytes;      // chunked kernel: bytes of one staging buffer (x, delta, dy, raw B/C, state); two follow each other
 };
 
 // Backward planning; returns false when no plan fits.  ws_bytes: workspace size.
