@@ -463,33 +463,32 @@ struct ScanWave {
     }
 
     // Fused aux pad: float64 index-order sum of this lane's whole unpadded row
-    // of sample b, streamed through the x areas of the stages (with two, the
-    // transfer of piece k+1 is in flight while piece k is summed).  The stages
-    // must be free.
+    // of sample b, streamed in pieces of ch positions through two LDS areas
+    // (the x areas of both stages, or the x and delta areas of the one stage):
+    // the transfer of piece k+1 is in flight while piece k is summed.  The
+    // areas must be free.
     __device__ __forceinline__ void mean1(int b) {
         constexpr int ew = 4 / (int)sizeof(IO);
         const int XL = p.xrow, step = p.ch;
         const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * p.D + d0) * XL;
+        const bool two = p.stages == 2;
+        auto area = [&](int i) __attribute__((always_inline)) { return i ? (two ? xs_of(1) : ds_of(0)) : xs_of(0); };
+        auto stride = [&](int i) __attribute__((always_inline)) { return (i && !two) ? p.drs : p.xrs; };
         auto issue = [&](int c0, int i) __attribute__((always_inline)) {
             const int lo = c0 / ew * ew;
             const int hi = min((c0 + min(step, XL - c0) + ew - 1) / ew * ew, XL);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            dma_tile(xg, xs_of(i), p.xrs, lo, hi, XL, nrows);
+            dma_tile(xg, area(i), stride(i), lo, hi, XL, nrows);
         };
         double acc = 0.0;
-        const int flip = p.stages == 2 ? 1 : 0;
         int i = 0;
         issue(0, 0);
-        for (int c0 = 0; c0 < XL; c0 += step, i ^= flip) {
+        for (int c0 = 0; c0 < XL; c0 += step, i ^= 1) {
             wait_vmem();
             wave_lds_sync();
-            if (flip && c0 + step < XL) issue(c0 + step, i ^ 1);
+            if (c0 + step < XL) issue(c0 + step, i ^ 1);
             const int cl = min(step, XL - c0);
-            if (lane < nrows) acc = sum_in_order(xs_of(i) + lane * p.xrs + c0 - c0 / ew * ew, cl, acc);
-            if (!flip && c0 + step < XL) {
-                wave_lds_sync();
-                issue(c0 + step, 0);
-            }
+            if (lane < nrows) acc = sum_in_order(area(i) + lane * stride(i) + c0 - c0 / ew * ew, cl, acc);
         }
         wave_lds_sync();
         mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
