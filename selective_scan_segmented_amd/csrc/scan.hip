@@ -34,7 +34,11 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     const int L = p.L, S = p.B2 * p.L;
     if (p.xrow <= 0) p.xrow = p.pad_in ? L - 2 : L;
     const int XL = p.xrow;
-    const bool fused = p.pad_in || p.swap_out;  // these keep each sample inside one wave
+    // The fused pad/swap keep each sample inside one wave, except with tile
+    // staging (even row lengths), whose pieces take the row mean and write the
+    // swapped ends themselves
+    const bool tile_rows = ((long long)L * io_bytes) % 4 == 0 && ((long long)XL * io_bytes) % 4 == 0;
+    const bool fused = (p.pad_in || p.swap_out) && !tile_rows;
     p.ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
     const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 0;
     p.tiles = (p.D + kWave - 1) / kWave;

@@ -512,7 +512,15 @@ struct ScanWave {
         int len = len_at(s, t0);
         const int bb = b1 * p.B2;
         int i = 0;
-        if (p.pad_in && t0 == 0) mean1(bb + j);
+        // with the fused pad, the aux tokens at positions 0 and L-1 are the row
+        // mean: a piece's segment of a sample needs it when its conv inputs
+        // reach either end (a new sample inside the piece starts at 0)
+        if (p.pad_in) {
+            const int seg_end = min(sb - (s - t0), L);  // end of this piece's part of sample j
+            const int first_x = CONV ? t0 - p.P : t0;
+            const int last_x = CONV ? seg_end - 1 + KW - 1 - p.P : seg_end - 1;
+            if (first_x <= 0 || last_x >= L - 1) mean1(bb + j);
+        }
         issue1(bb + j, t0, len, i);
         int pb = -1, pt0 = 0, plen = 0;  // chunk whose y waits in stage i ^ 1
         while (true) {
@@ -596,7 +604,13 @@ struct ScanWave {
         // positions written here; the ends go out last when swapping
         const int lo = (sw && t0 == 0) ? 1 : t0;
         const int hi = (sw && t0 + len == L) ? L - 1 : t0 + len;
-        if (sw && t0 == 0 && lane < nrows) y0 = ds[lane * drs + 0 - doff];
+        // mode 1 writes each swapped end as soon as it is computed (pieces of a
+        // sample may sit in different waves; y never overlaps an input), mode 2
+        // holds y at t = 0 until the sample's last chunk
+        if (sw && t0 == 0 && lane < nrows) {
+            if constexpr (MODE == 1) yg[(size_t)lane * L + L - 1] = ds[lane * drs + 0 - doff];
+            else y0 = ds[lane * drs + 0 - doff];
+        }
         if constexpr (MODE == 1) {
             // whole 4-byte words inside [lo, hi), single elements at the
             // edges; each lane writes its own row (immediate offsets, no
@@ -631,7 +645,7 @@ struct ScanWave {
         }
         if (sw && t0 + len == L && lane < nrows) {
             yg[(size_t)lane * L] = ds[lane * drs + (L - 1) - doff];
-            yg[(size_t)lane * L + L - 1] = y0;
+            if constexpr (MODE != 1) yg[(size_t)lane * L + L - 1] = y0;
         }
         wave_lds_sync();
         }

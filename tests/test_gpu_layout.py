@@ -6,6 +6,7 @@ channel-last launch (a) bit for bit against the channel-first launch on the
 transposed tensors and (b) against the float64 oracle (computed channel-first
 and transposed) with the forward's tolerance.
 """
+import os
 import sys
 
 import numpy as np
@@ -32,13 +33,24 @@ def tr(t):
     return t.transpose(1, 2).contiguous()
 
 
-def run(x, delta, A, Bm, Cm, Dk, db, cw, P, act, softplus, B2, flags, io, oracle_samples=None):
-    """x [B, D, T or L], delta [B, D, L], Bm/Cm [B, N, L] as numpy (f32 or bf16 bits)."""
+def run(x, delta, A, Bm, Cm, Dk, db, cw, P, act, softplus, B2, flags, io, oracle_samples=None, cf_whole_samples=False):
+    """x [B, D, T or L], delta [B, D, L], Bm/Cm [B, N, L] as numpy (f32 or bf16 bits).
+    cf_whole_samples: plan the channel-first reference with one piece per folded
+    row (no carried state), the layout the channel-last kernel runs, so that the
+    two are comparable bit for bit (a carry adds in another order)."""
     import torch
     T_ = lambda a: torch.from_numpy(a).cuda() if a is not None else None
     xd, dd, Bd, Cd = map(to_dev, (x, delta, Bm, Cm))
     kw = dict(delta_softplus=softplus, conv_w=T_(cw), conv_pad_left=P, conv_act="silu" if act else None, B2=B2)
-    ref = sfm.sfm_selective_scan_fwd_ex(xd, dd, T_(A), Bd, Cd, T_(Dk), T_(db), flags=flags, **kw)
+    saved = os.environ.pop("SFM_SCAN_WAVES", None)
+    try:
+        if cf_whole_samples:
+            os.environ["SFM_SCAN_WAVES"] = "1"
+        ref = sfm.sfm_selective_scan_fwd_ex(xd, dd, T_(A), Bd, Cd, T_(Dk), T_(db), flags=flags, **kw)
+    finally:
+        os.environ.pop("SFM_SCAN_WAVES", None)
+        if saved is not None:
+            os.environ["SFM_SCAN_WAVES"] = saved
     got = sfm.sfm_selective_scan_fwd_ex(tr(xd), tr(dd), T_(A), tr(Bd), tr(Cd), T_(Dk), T_(db), flags=flags | CL,
                                         **kw)
     torch.cuda.synchronize()
@@ -131,7 +143,7 @@ def test_layout_long_rows():
     say("layout long")
     li = synth.make_layer(synth.WORKLOADS["long"], seed=4)
     run(li.x, li.delta, li.A, li.Bm, li.Cm, li.Dskip, li.delta_bias, li.conv_w, 1, 0, True, 1, 3, "bf16",
-        oracle_samples=np.array([0, 15]))
+        oracle_samples=np.array([0, 15]), cf_whole_samples=True)
 
 
 def test_layout_rejects_unaligned_rows():

@@ -535,3 +535,49 @@ def test_chunk_pipeline_against_oracle(ch, io, stages):
                 os.environ[k] = v
     assert_close(from_dev(fused), oracle.aux_swap(want), io, f"fused ch={ch}")
     assert_close(from_dev(carried), want, io, f"carried ch={ch}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("waves,ch", [(3, 16), (5, 7), (8, 32)])
+def test_fused_pad_swap_with_carries(waves, ch, io):
+    """Fused pad/swap on tile-staged rows whose pieces cut samples (carried
+    state): the pieces holding a sample's ends take the row mean and write the
+    swapped ends themselves.  Bit-identical to pad -> scan -> swap with the same
+    pieces, and within tolerance of the oracle."""
+    import torch
+    say(f"fused carries waves={waves} ch={ch} io={io}")
+    B, D, N, T, K, P = 3, 72, 8, 298, 4, 1
+    L = T + 2
+    r = np.random.default_rng(waves * 13 + ch + len(io))
+    f = lambda *s: r.standard_normal(s).astype(np.float32)
+    x, delta, Bm, Cm = f(B, D, T), f(B, D, L), f(B, N, L), f(B, N, L)
+    cast = synth.f32_to_bf16_bits if io == "bf16" else (lambda a: a)
+    x, delta, Bm, Cm = map(cast, (x, delta, Bm, Cm))
+    A = (-r.uniform(0.5, 4.0, (D, N))).astype(np.float32)
+    Dk, db = f(D), r.uniform(-4, -1, D).astype(np.float32)
+    cw = r.uniform(-0.5, 0.5, (D, K)).astype(np.float32)
+    T_ = lambda a: torch.from_numpy(a).cuda()
+    xd, dd, Bd, Cd = map(to_dev, (x, delta, Bm, Cm))
+    up = lambda a: synth.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+    want = oracle.aux_swap(oracle.layer(oracle.aux_pad(up(x), io), up(delta), A, up(Bm), up(Cm), Dk, db, cw,
+                                        pad_left=P))
+    saved = {k: os.environ.pop(k, None) for k in ("SFM_SCAN_CHUNK", "SFM_SCAN_WAVES", "SFM_SCAN_STAGES")}
+    try:
+        os.environ["SFM_SCAN_WAVES"] = str(waves)
+        os.environ["SFM_SCAN_CHUNK"] = str(ch)
+        plan = sfm.sfm_scan_plan_string(B, 1, D, N, L, K, io, 3)
+        assert "mode=1" in plan and "carry=1" in plan, plan
+        got = sfm.sfm_selective_scan_fwd_ex(xd, dd, T_(A), Bd, Cd, T_(Dk), T_(db), conv_w=T_(cw),
+                                            conv_pad_left=P, B2=1, flags=3)
+        xp = sfm.sfm_aux_pad_swap(xd, mode="pad")
+        ref = sfm.sfm_selective_scan_fwd(xp, dd, T_(A), Bd, Cd, T_(Dk), T_(db), conv_w=T_(cw),
+                                         conv_pad_left=P, B2=1)
+        sfm.sfm_aux_pad_swap(ref, out=ref, mode="swap")
+        sync()
+    finally:
+        for k, v in saved.items():
+            os.environ.pop(k, None)
+            if v is not None:
+                os.environ[k] = v
+    assert np.array_equal(from_dev(got), from_dev(ref))
+    assert_close(from_dev(got), want, io, f"fused carries waves={waves}")
