@@ -128,11 +128,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         // positions [t0, t0 + cnt) (dy with its ends exchanged when swap_dy), raw B then C.
         constexpr int EB = (int)sizeof(IO);
         constexpr int kPer = 4096 / (kWave * 4);  // transfers per LDS base (4-byte slots)
-        auto dma_tile = [&](auto colsc, uint32_t* tile, auto addr) __attribute__((always_inline)) {
+        auto dma_tile = [&](auto colsc, uint32_t* tile, int ln, auto addr) __attribute__((always_inline)) {
             constexpr int COLS = decltype(colsc)::value;
             static_for<COLS>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
-                const int e = k * kWave + lane;
+                const int e = k * kWave + ln;
                 const int r = e / COLS;
                 dma_at<EB, (k % kPer) * kWave * 4>(addr(r, e - r * COLS), tile + (k / kPer) * kPer * kWave);
             });
@@ -144,20 +144,26 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         // completed before a transfer can write it.
         auto issue = [&](int t0, int cnt, bool with_dy, int ck, int i) __attribute__((always_inline)) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // An opaque copy of the lane index: the per-lane transfer addresses are
+            // recomputed here instead of being hoisted out of the chunk loop, where
+            // they would be spilled and their reloads would wait for every transfer
+            // in flight.
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
             uint32_t* xb = reinterpret_cast<uint32_t*>(buf(p.xs_off, i));
             uint32_t* db_ = reinterpret_cast<uint32_t*>(buf(p.ds_off, i));
             uint32_t* yb = reinterpret_cast<uint32_t*>(buf(p.dys_off, i));
             uint32_t* rb = reinterpret_cast<uint32_t*>(buf(p.braw_off, i));
             const IO* dummy = xg;
-            dma_tile(std::integral_constant<int, XW>{}, xb, [&](int r, int c) {
+            dma_tile(std::integral_constant<int, XW>{}, xb, ln, [&](int r, int c) {
                 const int q = t0 - P + c - sh;
                 return (r < nrows && q >= 0 && q < XL) ? xg + (size_t)r * XL + q : dummy;
             });
-            dma_tile(std::integral_constant<int, Q>{}, db_, [&](int r, int c) {
+            dma_tile(std::integral_constant<int, Q>{}, db_, ln, [&](int r, int c) {
                 return (r < nrows && c < cnt) ? dg + (size_t)r * L + t0 + c : dummy;
             });
             if (with_dy) {
-                dma_tile(std::integral_constant<int, Q>{}, yb, [&](int r, int c) {
+                dma_tile(std::integral_constant<int, Q>{}, yb, ln, [&](int r, int c) {
                     const int t = t0 + c;
                     const int ts = (p.swap_dy && L > 1) ? (t == 0 ? L - 1 : (t == L - 1 ? 0 : t)) : t;
                     return (r < nrows && c < cnt) ? yg + (size_t)r * L + ts : dummy;
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             }
             {
                 // raw B then C: element e < N*Q is B[n = e / Q][t0 + e % Q], the next N*Q are C
-                const int e = lane;
+                const int e = ln;
                 const int half = N * Q;
                 const int e2 = e < half ? e : e - half;
                 const int n = e2 / Q;
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 dma_at<EB, 0>(src, rb);
             }
             if (ck > 0) {
-                const float* hsrc = ws + (size_t)ck * NS * kWave + lane;
+                const float* hsrc = ws + (size_t)ck * NS * kWave + ln;
                 char* hb = buf(p.hin_off, i);
                 static_for<NS>([&](auto nc) {
                     constexpr int n = decltype(nc)::value;
@@ -214,26 +220,40 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
         }
         // conv/scan input at padded position q = t0 - P + c (column c of the staged window)
-        auto xv = [&](int t0, int c) __attribute__((always_inline)) {
+        // An interior chunk (full tile, all Q positions, the x window clear of
+        // the sample ends and of the aux tokens, past the sample start) needs
+        // none of the per-position checks; FAST variants drop them.
+        auto xv = [&](auto fastc, int t0, int c) __attribute__((always_inline)) {
+            constexpr bool FAST = decltype(fastc)::value;
             const int q = t0 - P + c;
             float v = Io<IO>::of_bits(xs[lane * XW + c]);
+            if constexpr (FAST) return v;
             if (p.pad_in && (q == 0 || q == L - 1)) v = mean;
             return (valid && q >= 0 && q < L) ? v : 0.0f;  // zero taps outside the sample
         };
         // z (pre-activation), u, v (pre-softplus) and Delta*log2e at position t0 + i
-        auto pre = [&](int t0, int i, float& z, float& u, float& v, float& dt) __attribute__((always_inline)) {
+        auto pre = [&](auto fastc, int t0, int i, float& z, float& u, float& v, float& dt)
+                       __attribute__((always_inline)) {
+            constexpr bool FAST = decltype(fastc)::value;
             if constexpr (CONV) {
                 float acc = cb;
 #pragma unroll
-                for (int jj = 0; jj < KW; ++jj) acc = __builtin_fmaf(cw[jj], xv(t0, i + jj), acc);
+                for (int jj = 0; jj < KW; ++jj) acc = __builtin_fmaf(cw[jj], xv(fastc, t0, i + jj), acc);
                 z = acc;
                 u = SILU ? silu(acc) : acc;
             } else {
-                z = xv(t0, i + P);
+                z = xv(fastc, t0, i + P);
                 u = z;
             }
-            v = (valid ? Io<IO>::of_bits(dls[lane * Q + i]) : 0.0f) + db;
+            v = ((FAST || valid) ? Io<IO>::of_bits(dls[lane * Q + i]) : 0.0f) + db;
             dt = SP ? softplus_log2e(v) * kLn2 : v;
+        };
+        // With 16 states the second copy of a chunk body costs more in spills than
+        // it saves, so only the narrower state widths take the interior path.
+        constexpr bool kInteriorPath = NS <= 8;
+        auto interior = [&](int t0, int cnt) __attribute__((always_inline)) {
+            const int edge = p.pad_in ? 1 : 0;
+            return nrows == kWave && cnt == Q && t0 > 0 && t0 - P >= edge && t0 - P + XW - 1 <= L - 1 - edge;
         };
 
         // --- sweep 1: forward, checkpoint the state entering each chunk.  The
@@ -250,23 +270,34 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             const int cnt = min(Q, L - t0);
             wait_vmem();
             wave_lds_sync();
+            // widen before the next transfers go out: any wait on vector memory
+            // the compiler puts here then covers nothing in flight
+            use_buf(bi);
+            widen(cnt, false);
             if (c > 0) {
 #pragma unroll
                 for (int n = 0; n < NS; ++n) ws[((size_t)c * NS + n) * kWave + lane] = h[n];
             }
             if (c + 1 < p.nchk) issue(t0 + Q, min(Q, L - t0 - Q), false, 0, bi ^ 1);
-            use_buf(bi);
-            widen(cnt, false);
             wave_lds_sync();
-            for (int i = 0; i < cnt; ++i) {
-                float z, u, v, dt;
-                pre(t0, i, z, u, v, dt);
-                const float du_ = dt * u;
+            auto fwd = [&](auto fastc) __attribute__((always_inline)) {
+                constexpr bool FAST = decltype(fastc)::value;
+                for (int i = 0; i < (FAST ? Q : cnt); ++i) {
+                    float z, u, v, dt;
+                    pre(fastc, t0, i, z, u, v, dt);
+                    const float du_ = dt * u;
 #pragma unroll
-                for (int n = 0; n < NS; ++n) {
-                    const float bx = du_ * bs[i * NS + n];
-                    h[n] = (t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dt * kLog2e * A[n]), h[n], bx);
+                    for (int n = 0; n < NS; ++n) {
+                        const float bx = du_ * bs[i * NS + n];
+                        h[n] = (!FAST && t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dt * kLog2e * A[n]), h[n], bx);
+                    }
                 }
+            };
+            if constexpr (kInteriorPath) {
+                if (interior(t0, cnt)) fwd(std::true_type{});
+                else fwd(std::false_type{});
+            } else {
+                fwd(std::false_type{});
             }
             bi ^= 1;
         }
@@ -311,123 +342,133 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             const int cnt = min(Q, L - t0);
             wait_vmem();
             wave_lds_sync();
+            use_buf(bi);
+            widen(cnt, true);  // before any transfer goes out (as in the forward sweep)
             if (pend >= 0) {
                 use_buf(bi ^ 1);
                 write_out(pend);
             }
             if (c > 0) issue(t0 - Q, Q, true, c - 1, bi ^ 1);
             use_buf(bi);
-            widen(cnt, true);
             for (int e = lane; e < kWave * XW; e += kWave) dxs[e] = 0.0f;
             float hin[NS];
 #pragma unroll
             for (int n = 0; n < NS; ++n) hin[n] = c > 0 ? hinl[n * kWave + lane] : 0.0f;
             wave_lds_sync();
-            // re-run the chunk forward, keeping every state
-            float hs[Q][NS];
-            float zs[Q], us[Q], vs[Q], dts[Q];
+            auto chunk = [&](auto fastc) __attribute__((always_inline)) {
+                constexpr bool FAST = decltype(fastc)::value;
+                // re-run the chunk forward, keeping every state
+                float hs[Q][NS];
+                float zs[Q], us[Q], vs[Q], dts[Q];
 #pragma unroll
-            for (int i = 0; i < Q; ++i) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (i < cnt) {
-                    pre(t0, i, zs[i], us[i], vs[i], dts[i]);
-                    const float du_ = dts[i] * us[i];
-#pragma unroll
-                    for (int n = 0; n < NS; ++n) {
-                        const float hp = i > 0 ? hs[i - 1][n] : hin[n];
-                        const float bx = du_ * bs[i * NS + n];
-                        hs[i][n] = (t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dts[i] * kLog2e * A[n]), hp, bx);
-                    }
-                }
-            }
-            // backwards through the chunk, R positions per dB/dC transpose round
-#pragma unroll
-            for (int r0 = Q - R; r0 >= 0; r0 -= R) {
-#pragma unroll
-                for (int ii = R - 1; ii >= 0; --ii) {
-                    const int i = r0 + ii;
-                    // one position at a time: keeps the schedule (and register use) to one step
+                for (int i = 0; i < Q; ++i) {
                     __builtin_amdgcn_sched_barrier(0);
-                    float dBv[NS], dCv[NS];
-#pragma unroll
-                    for (int n = 0; n < NS; ++n) dBv[n] = dCv[n] = 0.0f;
-                    if (i < cnt) {
-                        const int t = t0 + i;
-                        const float gy = valid ? Io<IO>::of_bits(dys[lane * Q + i]) : 0.0f;
-                        const float u = us[i], dt = dts[i];
-                        float du_ = Dk * gy;
-                        float ddt = 0.0f;
-                        gD = __builtin_fmaf(gy, u, gD);
+                    if (FAST || i < cnt) {
+                        pre(fastc, t0, i, zs[i], us[i], vs[i], dts[i]);
+                        const float du_ = dts[i] * us[i];
 #pragma unroll
                         for (int n = 0; n < NS; ++n) {
-                            const float Bv = bs[i * NS + n], Cv = cs[i * NS + n];
-                            const float Gn = __builtin_fmaf(gy, Cv, G[n]);
-                            dCv[n] = gy * hs[i][n];
-                            dBv[n] = Gn * dt * u;
-                            du_ = __builtin_fmaf(Gn * dt, Bv, du_);
-                            ddt = __builtin_fmaf(Gn * Bv, u, ddt);
-                            if (t > 0) {
-                                const float hp = i > 0 ? hs[i - 1][n] : hin[n];
-                                const float a = exp2_fast(dt * kLog2e * A[n]);
-                                const float w = a * Gn;    // carried to position t - 1
-                                const float dat = w * hp;  // dLoss/da_t times a_t
-                                ddt = __builtin_fmaf(dat, A[n], ddt);
-                                gA[n] = __builtin_fmaf(dat, dt, gA[n]);
-                                G[n] = w;
+                            const float hp = i > 0 ? hs[i - 1][n] : hin[n];
+                            const float bx = du_ * bs[i * NS + n];
+                            hs[i][n] = (!FAST && t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dts[i] * kLog2e * A[n]), hp, bx);
+                        }
+                    }
+                }
+                // backwards through the chunk, R positions per dB/dC transpose round
+#pragma unroll
+                for (int r0 = Q - R; r0 >= 0; r0 -= R) {
+#pragma unroll
+                    for (int ii = R - 1; ii >= 0; --ii) {
+                        const int i = r0 + ii;
+                        // one position at a time: keeps the schedule (and register use) to one step
+                        __builtin_amdgcn_sched_barrier(0);
+                        float dBv[NS], dCv[NS];
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) dBv[n] = dCv[n] = 0.0f;
+                        if (FAST || i < cnt) {
+                            const int t = t0 + i;
+                            const float gy = (FAST || valid) ? Io<IO>::of_bits(dys[lane * Q + i]) : 0.0f;
+                            const float u = us[i], dt = dts[i];
+                            float du_ = Dk * gy;
+                            float ddt = 0.0f;
+                            gD = __builtin_fmaf(gy, u, gD);
+#pragma unroll
+                            for (int n = 0; n < NS; ++n) {
+                                const float Bv = bs[i * NS + n], Cv = cs[i * NS + n];
+                                const float Gn = __builtin_fmaf(gy, Cv, G[n]);
+                                dCv[n] = gy * hs[i][n];
+                                dBv[n] = Gn * dt * u;
+                                du_ = __builtin_fmaf(Gn * dt, Bv, du_);
+                                ddt = __builtin_fmaf(Gn * Bv, u, ddt);
+                                if (FAST || t > 0) {
+                                    const float hp = i > 0 ? hs[i - 1][n] : hin[n];
+                                    const float a = exp2_fast(dt * kLog2e * A[n]);
+                                    const float w = a * Gn;    // carried to position t - 1
+                                    const float dat = w * hp;  // dLoss/da_t times a_t
+                                    ddt = __builtin_fmaf(dat, A[n], ddt);
+                                    gA[n] = __builtin_fmaf(dat, dt, gA[n]);
+                                    G[n] = w;
+                                } else {
+                                    G[n] = 0.0f;  // reset: nothing reaches the previous sample
+                                }
+                            }
+                            float dv = ddt;
+                            if constexpr (SP) dv = vs[i] > 20.0f ? ddt : ddt * sigmoid_f(vs[i]);
+                            dls[lane * Q + i] = __float_as_uint(dv);
+                            gb += dv;
+                            float dz = du_;
+                            if constexpr (CONV && SILU) {
+                                const float s = sigmoid_f(zs[i]);
+                                dz = du_ * (s + zs[i] * s * (1.0f - s));
+                            }
+                            if constexpr (CONV) {
+                                gcb += dz;
+#pragma unroll
+                                for (int jj = 0; jj < KW; ++jj) {
+                                    gw[jj] = __builtin_fmaf(dz, xv(fastc, t0, i + jj), gw[jj]);
+                                    wdx[jj] = __builtin_fmaf(dz, cw[jj], wdx[jj]);
+                                }
+                                // padded position t + lag is complete: it gets no later contribution
+                                dxs[lane * XW + i + KW - 1] = wdx[KW - 1];
+#pragma unroll
+                                for (int jj = KW - 1; jj > 0; --jj) wdx[jj] = wdx[jj - 1];
+                                wdx[0] = 0.0f;
                             } else {
-                                G[n] = 0.0f;  // reset: nothing reaches the previous sample
+                                dxs[lane * XW + i + P] = dz;
                             }
                         }
-                        float dv = ddt;
-                        if constexpr (SP) dv = vs[i] > 20.0f ? ddt : ddt * sigmoid_f(vs[i]);
-                        dls[lane * Q + i] = __float_as_uint(dv);
-                        gb += dv;
-                        float dz = du_;
-                        if constexpr (CONV && SILU) {
-                            const float s = sigmoid_f(zs[i]);
-                            dz = du_ * (s + zs[i] * s * (1.0f - s));
-                        }
-                        if constexpr (CONV) {
-                            gcb += dz;
+                        // transpose buffer: row (ii, k), column lane
 #pragma unroll
-                            for (int jj = 0; jj < KW; ++jj) {
-                                gw[jj] = __builtin_fmaf(dz, xv(t0, i + jj), gw[jj]);
-                                wdx[jj] = __builtin_fmaf(dz, cw[jj], wdx[jj]);
-                            }
-                            // padded position t + lag is complete: it gets no later contribution
-                            dxs[lane * XW + i + KW - 1] = wdx[KW - 1];
-#pragma unroll
-                            for (int jj = KW - 1; jj > 0; --jj) wdx[jj] = wdx[jj - 1];
-                            wdx[0] = 0.0f;
-                        } else {
-                            dxs[lane * XW + i + P] = dz;
+                        for (int n = 0; n < NS; ++n) {
+                            red[(ii * 2 * NS + n) * kRedStride + lane] = dBv[n];
+                            red[(ii * 2 * NS + NS + n) * kRedStride + lane] = dCv[n];
                         }
                     }
-                    // transpose buffer: row (ii, k), column lane
+                    wave_lds_sync();
+                    {
+                        // lane l sums row l: position r0 + l / (2NS), state l % NS, B or C
+                        const int ii = lane / (2 * NS);
+                        const int k = lane - ii * 2 * NS;
+                        const int n = k % NS;
+                        const int t = t0 + r0 + ii;
+                        const float4* row = reinterpret_cast<const float4*>(red + lane * kRedStride);
+                        float s = 0.0f;
 #pragma unroll
-                    for (int n = 0; n < NS; ++n) {
-                        red[(ii * 2 * NS + n) * kRedStride + lane] = dBv[n];
-                        red[(ii * 2 * NS + NS + n) * kRedStride + lane] = dCv[n];
+                        for (int m = 0; m < kWave / 4; ++m) {
+                            const float4 v4 = row[m];
+                            s += (v4.x + v4.y) + (v4.z + v4.w);
+                        }
+                        if (lane < 2 * NS * R && r0 + ii < cnt)
+                            p.ws[p.pbc_off + (((size_t)tile * p.B1 * p.B2 + b) * L + t) * 2 * NS + k] = s;
                     }
+                    wave_lds_sync();
                 }
-                wave_lds_sync();
-                {
-                    // lane l sums row l: position r0 + l / (2NS), state l % NS, B or C
-                    const int ii = lane / (2 * NS);
-                    const int k = lane - ii * 2 * NS;
-                    const int n = k % NS;
-                    const int t = t0 + r0 + ii;
-                    const float4* row = reinterpret_cast<const float4*>(red + lane * kRedStride);
-                    float s = 0.0f;
-#pragma unroll
-                    for (int m = 0; m < kWave / 4; ++m) {
-                        const float4 v4 = row[m];
-                        s += (v4.x + v4.y) + (v4.z + v4.w);
-                    }
-                    if (lane < 2 * NS * R && r0 + ii < cnt)
-                        p.ws[p.pbc_off + (((size_t)tile * p.B1 * p.B2 + b) * L + t) * 2 * NS + k] = s;
-                }
-                wave_lds_sync();
+            };
+            if constexpr (kInteriorPath) {
+                if (interior(t0, cnt)) chunk(std::true_type{});
+                else chunk(std::false_type{});
+            } else {
+                chunk(std::false_type{});
             }
             if constexpr (CONV) {
                 // positions t0 - P .. t0 + lag - 1 are complete once the sample start is passed
