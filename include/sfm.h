@@ -192,8 +192,19 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  * Two kernels: when every [rows][length] block of a sample and 64-channel tile
  * is a whole number of 16-byte units on 16-byte boundaries and fits in LDS,
  * each sample is staged once; otherwise chunk by chunk (channel-first only).
- * Environment override (diagnostics): SFM_BWD_CHUNKED=1 forces the chunked
- * kernel for channel-first tensors.
+ * The chunked kernel splits rows along L when samples times tiles give fewer
+ * than 1024 waves: segments of at least 64 positions, one wave each, after a
+ * carry pass (per segment: the state reached from zero, the output gradient
+ * carried back from zero, the sum of the steps); each wave composes the carries
+ * of the other segments of its row (the exact linear composition, its decay
+ * product taken as exp2(A * summed steps)), and the conv-input gradient at the
+ * positions around a segment boundary that the conv windows of both segments
+ * reach is the sum of the two segments' partials.  The workspace then also holds the carries, the row
+ * means of SFM_FUSE_PAD and those partials.
+ * Environment overrides (diagnostics): SFM_BWD_CHUNKED=1 forces the chunked
+ * kernel for channel-first tensors; SFM_BWD_SEGMENTS=n asks the chunked kernel
+ * for n segments per row (at most 64; at least the conv window per segment).
+ * Both change the workspace size: query it with the same environment.
  * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN/UNSUPPORTED (nothing
  * launched), HIP.
  */

@@ -49,16 +49,25 @@ constexpr int kRedStride = 68;  // floats per row of the transpose buffer (16-by
 
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + exp2_fast(-v * kLog2e)); }
 
-template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q>
+// MODE 0: whole rows; 1: rows split into segments (after the carry pass); 2: the carry pass.
+template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q, int MODE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kernel(BwdParams p) {
+    constexpr bool SPLIT = MODE != 0;
+    constexpr bool CARRY = MODE == 2;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     constexpr int XW = Q + KW - 1;  // x window columns of a chunk
     constexpr int R = Q < 32 / NS ? Q : 32 / NS;  // positions per dB/dC transpose round (2*NS*R <= 64 rows)
     static_assert(Q % R == 0, "chunk must hold whole transpose rounds");
     const int lane = threadIdx.x;
+    // wave g = ((b1 * tiles) + tile) * seg + s: segment s of the sample row b1 in channel tile `tile`
+    const int S = SPLIT ? p.seg : 1;
     const int g = blockIdx.x;
-    const int b1 = g / p.tiles;
-    const int tile = g - b1 * p.tiles;
+    const int s = g % S;
+    const int rt = g / S;
+    const int b1 = rt / p.tiles;
+    const int tile = rt - b1 * p.tiles;
+    const int cbeg = s * p.cps;                  // the segment's chunks [cbeg, cend)
+    const int cend = SPLIT ? min(p.nchk, cbeg + p.cps) : p.nchk;
     const int d0 = tile * kWave;
     const int nrows = min(kWave, p.D - d0);
     const int d = d0 + lane;
@@ -108,7 +117,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         bs[e] = 0.0f;
         cs[e] = 0.0f;
     }
-    float* ws = p.ws + (size_t)g * p.nchk * NS * kWave;
+    float* ws = p.ws + (size_t)g * (SPLIT ? p.cps : p.nchk) * NS * kWave;  // checkpoints, chunk c at c - cbeg
+    // carries of the segment waves of this row and tile: [seg][2 NS + 2][64]
+    float* car = p.ws + p.car_off + (size_t)rt * S * (2 * NS + 2) * kWave + lane;
+    auto carv = [&](int sg, int k) __attribute__((always_inline)) -> float& {
+        return car[((size_t)sg * (2 * NS + 2) + k) * kWave];
+    };
 
     for (int j = 0; j < p.B2; ++j) {
         const int b = b1 * p.B2 + j;
@@ -137,9 +151,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 dma_at<EB, (k % kPer) * kWave * 4>(addr(r, e - r * COLS), tile + (k / kPer) * kPer * kWave);
             });
         };
-        // Transfers of chunk (t0, cnt) into staging buffer i; with ck > 0 also the
-        // state entering chunk ck (its checkpoint, [NS][64] floats contiguous in
-        // the workspace, one 4-byte transfer per state).  Nothing is waited for;
+        // Transfers of chunk (t0, cnt) into staging buffer i; with ck >= 0 also the
+        // state entering the segment's chunk ck (its checkpoint, [NS][64] floats
+        // contiguous in the workspace, one 4-byte transfer per state).  Nothing is waited for;
         // the buffer was last read by LDS instructions of this wave, which have
         // completed before a transfer can write it.
         auto issue = [&](int t0, int cnt, bool with_dy, int ck, int i) __attribute__((always_inline)) {
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                                     : dummy;
                 dma_at<EB, 0>(src, rb);
             }
-            if (ck > 0) {
+            if (ck >= (SPLIT ? 0 : 1)) {  // (a whole row starts from zero: no checkpoint 0)
                 const float* hsrc = ws + (size_t)ck * NS * kWave + ln;
                 char* hb = buf(p.hin_off, i);
                 static_for<NS>([&](auto nc) {
@@ -204,7 +218,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 
         // --- fused aux pad: this row's mean, float64 in index order (as the forward)
         float mean = 0.0f;
-        if (p.pad_in) {
+        if (p.pad_in && SPLIT && !CARRY) {
+            // split rows: the carry pass's first segment wave computed it
+            mean = valid ? p.ws[p.meanw_off + (size_t)b * p.D + d] : 0.0f;
+        } else if (p.pad_in && (!CARRY || s == 0)) {
             double acc = 0.0;
             for (int c0 = 0; c0 < XL; c0 += XW) {
                 const int cnt = min(XW, XL - c0);
@@ -218,6 +235,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 for (int c = 0; c < cnt; ++c) acc += (double)Io<IO>::of_bits(xs[lane * XW + c]);
             }
             mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+            if (CARRY && valid) p.ws[p.meanw_off + (size_t)b * p.D + d] = mean;
         }
         // conv/scan input at padded position q = t0 - P + c (column c of the staged window)
         // An interior chunk (full tile, all Q positions, the x window clear of
@@ -262,10 +280,23 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         float h[NS];
 #pragma unroll
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
-        wave_lds_sync();
+        if constexpr (!CARRY) {
+            // the state entering the segment: the earlier segments' carries composed
+            // in order, each the state its segment reaches from zero plus the product
+            // of its decays, exp2(A * sum of Delta*log2e), times the state before it
+            for (int sg = 0; sg < s; ++sg) {
+                const float sd = carv(sg, 2 * NS);
+#pragma unroll
+                for (int n = 0; n < NS; ++n) h[n] = __builtin_fmaf(exp2_fast(sd * A[n]), h[n], carv(sg, n));
+            }
+        }
+        float sdt = 0.0f;  // carry pass: sum of Delta*log2e over the segment
         int bi = 0;
-        issue(0, min(Q, L), false, 0, 0);
-        for (int c = 0; c < p.nchk; ++c) {
+        // (the carry pass needs the forward for every segment but the row's last)
+        const int cstop = (!CARRY || s < S - 1) ? cend : cbeg;
+        wave_lds_sync();
+        if (cbeg < cstop) issue(cbeg * Q, min(Q, L - cbeg * Q), false, -1, 0);
+        for (int c = cbeg; c < cstop; ++c) {
             const int t0 = c * Q;
             const int cnt = min(Q, L - t0);
             wait_vmem();
@@ -274,17 +305,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             // the compiler puts here then covers nothing in flight
             use_buf(bi);
             widen(cnt, false);
-            if (c > 0) {
+            if (!CARRY && (SPLIT || c > 0)) {
 #pragma unroll
-                for (int n = 0; n < NS; ++n) ws[((size_t)c * NS + n) * kWave + lane] = h[n];
+                for (int n = 0; n < NS; ++n) ws[((size_t)(c - cbeg) * NS + n) * kWave + lane] = h[n];
             }
-            if (c + 1 < p.nchk) issue(t0 + Q, min(Q, L - t0 - Q), false, 0, bi ^ 1);
+            if (c + 1 < cend) issue(t0 + Q, min(Q, L - t0 - Q), false, -1, bi ^ 1);
             wave_lds_sync();
             auto fwd = [&](auto fastc) __attribute__((always_inline)) {
                 constexpr bool FAST = decltype(fastc)::value;
                 for (int i = 0; i < (FAST ? Q : cnt); ++i) {
                     float z, u, v, dt;
                     pre(fastc, t0, i, z, u, v, dt);
+                    if constexpr (CARRY) sdt += dt * kLog2e;
                     const float du_ = dt * u;
 #pragma unroll
                     for (int n = 0; n < NS; ++n) {
@@ -301,6 +333,53 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             }
             bi ^= 1;
         }
+        if constexpr (CARRY) {
+            if (s < S - 1) {
+#pragma unroll
+                for (int n = 0; n < NS; ++n) carv(s, n) = h[n];
+                carv(s, 2 * NS) = sdt;
+            }
+        }
+
+        // --- carry pass: the carried output gradient the segment passes to its
+        // start, reached from zero at its end (no states needed: only the decays
+        // and C*dy), and the sum of Delta*log2e, for every segment but the row's first
+        if constexpr (CARRY) {
+            if (s > 0) {
+                float Gc[NS];
+#pragma unroll
+                for (int n = 0; n < NS; ++n) Gc[n] = 0.0f;
+                float sdr = 0.0f;
+                wait_vmem();
+                wave_lds_sync();
+                bi = 0;
+                issue((cend - 1) * Q, min(Q, L - (cend - 1) * Q), true, -1, 0);
+                for (int c = cend - 1; c >= cbeg; --c) {
+                    const int t0 = c * Q;
+                    const int cnt = min(Q, L - t0);
+                    wait_vmem();
+                    wave_lds_sync();
+                    use_buf(bi);
+                    widen(cnt, true);
+                    if (c > cbeg) issue(t0 - Q, Q, true, -1, bi ^ 1);
+                    wave_lds_sync();
+                    for (int i = cnt - 1; i >= 0; --i) {
+                        float z, u, v, dt;
+                        pre(std::false_type{}, t0, i, z, u, v, dt);
+                        const float dtl = dt * kLog2e;
+                        sdr += dtl;
+                        const float gy = valid ? Io<IO>::of_bits(dys[lane * Q + i]) : 0.0f;
+#pragma unroll
+                        for (int n = 0; n < NS; ++n)
+                            Gc[n] = exp2_fast(dtl * A[n]) * __builtin_fmaf(gy, cs[i * NS + n], Gc[n]);
+                    }
+                    bi ^= 1;
+                }
+#pragma unroll
+                for (int n = 0; n < NS; ++n) carv(s, NS + n) = Gc[n];
+                carv(s, 2 * NS + 1) = sdr;
+            }
+        } else {
 
         // --- sweep 2: chunks in reverse.  Chunk c-1's transfers (with its
         // entering state) go out once chunk c has landed; chunk c's ddelta (in
@@ -317,27 +396,46 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             }
             // dx columns finished in this chunk: padded positions [lo, hi)
             const int lag = CONV ? KW - 1 - P : 0;
-            const int lo = CONV ? (c == 0 ? 0 : t0 + lag) : t0;
+            const int lo = CONV ? (c == cbeg ? max(0, t0 - P) : t0 + lag) : t0;
             const int hi = CONV ? min(L, t0 + cnt + lag) : t0 + cnt;
+            // split rows: the kw - 1 positions around a segment boundary take
+            // contributions from both segments; each writes its partial to the
+            // workspace ([leading | trailing][kw - 1][64]) for the seam kernel
+            const int s0 = cbeg * Q, s1 = cend * Q;
+            float* seam = p.ws + p.seam_off + (size_t)g * 2 * (KW - 1) * kWave;
             for (int e = lane; e < kWave * XW; e += kWave) {
                 const int r = e / XW;
                 const int cc = e - r * XW;
                 const int q = t0 - P + cc;
-                if (r < nrows && q >= lo && q < hi) dug[(size_t)r * L + q] = from_f32<IO>(dxs[r * XW + cc]);
+                if (r < nrows && q >= lo && q < hi) {
+                    const float v = dxs[r * XW + cc];
+                    if (CONV && SPLIT && s > 0 && q < s0 + lag)
+                        seam[(size_t)(q - s0 + P) * kWave + r] = v;
+                    else if (CONV && SPLIT && s < S - 1 && q >= s1 - P)
+                        seam[(size_t)(KW - 1 + q - s1 + P) * kWave + r] = v;
+                    else
+                        dug[(size_t)r * L + q] = from_f32<IO>(v);
+                }
             }
         };
         float G[NS];  // a_{t+1} G_{t+1} carried to position t
 #pragma unroll
         for (int n = 0; n < NS; ++n) G[n] = 0.0f;
+        // entering the segment's end: the later segments' carries composed from the row's end
+        for (int sg = S - 1; sg > s; --sg) {
+            const float sd = carv(sg, 2 * NS + 1);
+#pragma unroll
+            for (int n = 0; n < NS; ++n) G[n] = __builtin_fmaf(exp2_fast(sd * A[n]), G[n], carv(sg, NS + n));
+        }
         float wdx[KW];  // dx of padded positions t - P + jj, still collecting contributions
 #pragma unroll
         for (int jj = 0; jj < KW; ++jj) wdx[jj] = 0.0f;
         wait_vmem();  // the checkpoints stored above have landed before they are read back
         wave_lds_sync();
         bi = 0;
-        issue((p.nchk - 1) * Q, L - (p.nchk - 1) * Q, true, p.nchk - 1, 0);
+        issue((cend - 1) * Q, min(Q, L - (cend - 1) * Q), true, cend - 1 - cbeg, 0);
         int pend = -1;  // chunk whose outputs wait in buffer bi ^ 1 and dxs
-        for (int c = p.nchk - 1; c >= 0; --c) {
+        for (int c = cend - 1; c >= cbeg; --c) {
             const int t0 = c * Q;
             const int cnt = min(Q, L - t0);
             wait_vmem();
@@ -348,12 +446,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 use_buf(bi ^ 1);
                 write_out(pend);
             }
-            if (c > 0) issue(t0 - Q, Q, true, c - 1, bi ^ 1);
+            if (c > cbeg) issue(t0 - Q, Q, true, c - 1 - cbeg, bi ^ 1);
             use_buf(bi);
             for (int e = lane; e < kWave * XW; e += kWave) dxs[e] = 0.0f;
             float hin[NS];
 #pragma unroll
-            for (int n = 0; n < NS; ++n) hin[n] = c > 0 ? hinl[n * kWave + lane] : 0.0f;
+            for (int n = 0; n < NS; ++n) hin[n] = (SPLIT || c > 0) ? hinl[n * kWave + lane] : 0.0f;
             wave_lds_sync();
             auto chunk = [&](auto fastc) __attribute__((always_inline)) {
                 constexpr bool FAST = decltype(fastc)::value;
@@ -471,8 +569,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 chunk(std::false_type{});
             }
             if constexpr (CONV) {
-                // positions t0 - P .. t0 + lag - 1 are complete once the sample start is passed
-                if (c == 0) {
+                // positions t0 - P .. t0 + lag - 1 are complete once the sample (or
+                // segment: a partial) start is passed
+                if (c == cbeg) {
                     // after the last shift wdx[m] holds padded position m - 1 - P,
                     // i.e. window column m - 1
 #pragma unroll
@@ -486,10 +585,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         use_buf(bi ^ 1);
         write_out(pend);
         wave_lds_sync();
+        }  // sweep 2
     }
-    if (valid) {
-        // this folded row's per-channel sums (rows dA[0..N), dD, dbias, dconv_b, dconv_w[0..K))
-        float* pc = p.ws + p.pch_off + (size_t)b1 * p.kc * p.D + d;
+    if (!CARRY && valid) {
+        // this row segment's per-channel sums (rows dA[0..N), dD, dbias, dconv_b, dconv_w[0..K))
+        float* pc = p.ws + p.pch_off + ((size_t)b1 * S + s) * p.kc * p.D + d;
 #pragma unroll
         for (int n = 0; n < NS; ++n)
             if (n < N) pc[(size_t)n * p.D] = gA[n];
@@ -964,8 +1064,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int nb_bc)
     const int row = live ? (int)(o / D) : 0;
     const int d = live ? (int)(o % D) : 0;
     float s = 0.0f;
-    if (live)
-        for (int b1 = k; b1 < p.B1; b1 += kRedOut) s += pch[((size_t)b1 * p.kc + row) * D + d];
+    if (live)  // rows: folded row b1 and segment s at b1 * seg + s
+        for (int b1 = k; b1 < p.B1 * p.seg; b1 += kRedOut) s += pch[((size_t)b1 * p.kc + row) * D + d];
     part[k][oo] = s;
     __syncthreads();
     if (k == 0 && live) {
@@ -979,6 +1079,30 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int nb_bc)
     }
 }
 
+// Split rows: the conv-input gradient at the kw - 1 positions around each
+// segment boundary, the trailing partial of the segment before it plus the
+// leading partial of the segment after it (in that order).
+template <typename IO>
+__global__ __launch_bounds__(256) void bwd_seam_kernel(BwdParams p) {
+    const int km = p.kw - 1, S = p.seg, D = p.D;
+    const size_t total = (size_t)p.B1 * (S - 1) * km * D;
+    const float* seam = p.ws + p.seam_off;
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+        const int d = (int)(idx % D);
+        size_t r = idx / D;
+        const int j = (int)(r % km);
+        r /= km;
+        const int s = 1 + (int)(r % (S - 1));
+        const size_t b = r / (S - 1);
+        const int tile = d / kWave, lane = d - tile * kWave;
+        const size_t g = (b * p.tiles + tile) * S + s;  // the segment after the boundary; g - 1 before it
+        const float v = seam[((g - 1) * 2 + 1) * km * kWave + (size_t)j * kWave + lane] +
+                        seam[(g * 2) * km * kWave + (size_t)j * kWave + lane];
+        const int q = s * p.cps * p.q - p.P + j;
+        static_cast<IO*>(p.du)[(b * D + d) * p.L + q] = from_f32<IO>(v);
+    }
+}
+
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU>
 hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
     constexpr int Q = kHist / NS;  // kHist states of history in registers
@@ -988,9 +1112,23 @@ hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
     else if (p.whole)
         hipLaunchKernelGGL((bwd_whole_kernel<IO, NS, KW, CONV, SP, SILU, Q, false>), dim3((unsigned)(p.B1 * p.tiles)),
                            dim3(kWave), (size_t)p.lds_bytes, s, p);
-    else
-        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q>), dim3((unsigned)(p.B1 * p.tiles)), dim3(kWave),
-                           (size_t)p.lds_bytes, s, p);
+    else {
+        const unsigned grid = (unsigned)(p.B1 * p.tiles * p.seg);
+        if (p.seg > 1) {
+            hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 2>), dim3(grid), dim3(kWave),
+                               (size_t)p.lds_bytes, s, p);
+            hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 1>), dim3(grid), dim3(kWave),
+                               (size_t)p.lds_bytes, s, p);
+        } else {
+            hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 0>), dim3(grid), dim3(kWave),
+                               (size_t)p.lds_bytes, s, p);
+        }
+        if (CONV && p.seg > 1 && p.kw > 1) {
+            const size_t total = (size_t)p.B1 * (p.seg - 1) * (p.kw - 1) * p.D;
+            hipLaunchKernelGGL(bwd_seam_kernel<IO>, dim3((unsigned)std::min<size_t>(1024, (total + 255) / 256)),
+                               dim3(256), 0, s, p);
+        }
+    }
     return hipGetLastError();
 }
 
@@ -1025,12 +1163,27 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     p.nchk = (p.L + p.q - 1) / p.q;
     p.kc = p.N + 2 + (p.conv_w ? 1 + p.K : 0);  // rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
     auto up64 = [](long long v) { return (v + 63) & ~63LL; };  // 256-byte aligned regions
-    const long long ck = (long long)p.B1 * p.tiles * p.nchk * p.ns * kWave;
-    const long long pbc = (long long)p.tiles * p.B1 * p.B2 * p.L * 2 * p.ns;
-    const long long pch = (long long)p.B1 * p.kc * p.D;
-    p.pbc_off = up64(ck);
-    p.pch_off = p.pbc_off + up64(pbc);
-    *ws_bytes = (size_t)(p.pch_off + up64(pch)) * sizeof(float);
+    p.seg = 1;
+    p.cps = p.nchk;
+    p.kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 1;
+    // workspace regions, each on 256 bytes: checkpoints [B1 * tiles * seg][cps][ns][64],
+    // dB/dC partials, per-channel partials [B1 * seg][kc][D]; split rows add the
+    // carries [B1 * tiles * seg][2 ns + 2][64], the row means [B1][D] and the
+    // boundary partials [B1 * tiles * seg][2][kw - 1][64]
+    auto layout = [&]() {
+        const long long waves = (long long)p.B1 * p.tiles * p.seg;
+        const long long ck = waves * p.cps * p.ns * kWave;
+        const long long pbc = (long long)p.tiles * p.B1 * p.B2 * p.L * 2 * p.ns;
+        const long long pch = (long long)p.B1 * p.seg * p.kc * p.D;
+        const bool split = p.seg > 1;
+        p.pbc_off = up64(ck);
+        p.pch_off = p.pbc_off + up64(pbc);
+        p.car_off = p.pch_off + up64(pch);
+        p.meanw_off = p.car_off + (split ? up64(waves * (2 * p.ns + 2) * kWave) : 0);
+        p.seam_off = p.meanw_off + (split ? up64((long long)p.B1 * p.D) : 0);
+        *ws_bytes = (size_t)(p.seam_off + (split ? up64(waves * 2 * (p.kw - 1) * kWave) : 0)) * sizeof(float);
+    };
+    layout();
     auto up16 = [](long long v) { return (int)((v + 15) & ~15LL); };
     // Whole-sample staging: every [rows][length] block (x, delta, dy, ddelta, du)
     // of every sample and tile must start on 16 bytes and span whole 16-byte
@@ -1088,6 +1241,30 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     p.mean_off = off;  // fp32 dx window
     off += up16(kWave * xw * 4);
     p.lds_bytes = off;
+    // Split rows along L when the rows and tiles alone give fewer waves than
+    // the GPU has SIMDs (about two waves per SIMD wanted): segments of at least
+    // 64 positions (kw at least, also the last one) cost a carry pass over the
+    // row and a composition of the carries per wave.  SFM_BWD_SEGMENTS=n asks
+    // for n segments (tests; the length floor is then kw).
+    {
+        const long long waves = (long long)p.B1 * p.tiles;
+        const char* fs = getenv("SFM_BWD_SEGMENTS");
+        const bool forced = fs && atoi(fs) > 0;
+        long long want = forced ? atoi(fs) : (waves < 1024 ? (2048 + waves - 1) / waves : 1);
+        want = std::min<long long>(want, 64);
+        if (want > 1) {
+            const int floor_pos = forced ? kw : std::max(kw, 64);
+            int cps = std::max((int)((p.nchk + want - 1) / want), (floor_pos + q - 1) / q);
+            // the last segment gets kw positions at least
+            while (cps < p.nchk && p.L - ((p.nchk + cps - 1) / cps - 1) * cps * q < kw) ++cps;
+            const int S = (p.nchk + cps - 1) / cps;
+            if (S > 1) {
+                p.seg = S;
+                p.cps = cps;
+            }
+        }
+    }
+    layout();
     return p.lds_bytes <= 64 * 1024;
 }
 

@@ -40,8 +40,18 @@ struct BwdParams {
     int cl;               // channel-last tensors: u, delta, dy, du, ddelta [B, L, D]; B, C, dB, dC [B, L, N]
     // partial sums in the workspace (offsets in floats), added up in a fixed order
     // by a second kernel: dB/dC per channel tile [tiles][B][L][2][ns] and the
-    // per-channel sums per folded row [B1][kc][D], rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
+    // per-channel sums per folded row and segment [B1][seg][kc][D], rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
     long long pbc_off, pch_off;
+    // chunked kernel split along L: each sample row is cut into `seg` segments of
+    // `cps` chunks, one wave each.  A carry pass writes per segment wave (car_off)
+    // the state reached from zero at its end [ns], the carried output gradient
+    // reached from zero at its start [ns], and the two step sums (forward,
+    // reverse) [2], each over 64 lanes; the fused pad's row means [B1][D]
+    // (meanw_off); the conv-input gradient at the kw - 1 positions around each
+    // segment boundary comes as two partials per segment wave [2][kw - 1][64]
+    // (seam_off: the segment's leading and trailing ones) added by a seam kernel.
+    int seg, cps, kw;
+    long long car_off, meanw_off, seam_off;
     int kc;
     int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, braw_off, lds_bytes;
     int hin_off;          // chunked kernel: a chunk's entering state [ns][64] f32, staged with the chunk

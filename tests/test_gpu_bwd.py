@@ -146,6 +146,32 @@ def test_bwd_stage4_bf16_chunked(monkeypatch):
     run_case(B=64, D=640, N=8, T=49, B2=2, K=4, P=1, act=0, softplus=True, flags=3, io="bf16", seed=12)
 
 
+@pytest.mark.parametrize("B,D,N,T,B2,K,P,act,sp,flags,segs,conv", [
+    (2, 70, 5, 60, 1, 4, 1, 1, True, 3, 3, True),    # pad and swap, partial tile, N padded to 8
+    (2, 24, 16, 45, 2, 4, 3, 0, True, 0, 4, True),   # causal conv (lag 0), N = 16, folded pairs
+    (1, 16, 4, 40, 1, 8, 2, 0, True, 3, 5, True),    # widest window: 7 boundary positions, lag 5
+    (2, 16, 8, 30, 1, 4, 0, 0, False, 0, 3, True),   # anti-causal side only (lag 3), no softplus
+    (2, 16, 4, 30, 1, 1, 0, 0, True, 0, 4, False),   # no conv: no boundary partials
+])
+def test_bwd_split_rows_f32(B, D, N, T, B2, K, P, act, sp, flags, segs, conv, monkeypatch):
+    """The chunked kernel with rows split along L (carry pass, composed carries,
+    boundary partials) against the oracle; the plan must really split."""
+    monkeypatch.setenv("SFM_BWD_CHUNKED", "1")
+    kk = K if conv else 0
+    whole = sfm.sfm_selective_scan_bwd_workspace_size(B // B2, B2, D, N, T + 2, kk, "f32", flags)
+    monkeypatch.setenv("SFM_BWD_SEGMENTS", str(segs))
+    split = sfm.sfm_selective_scan_bwd_workspace_size(B // B2, B2, D, N, T + 2, kk, "f32", flags)
+    assert split > whole
+    run_case(B=B, D=D, N=N, T=T, B2=B2, K=K, P=P, act=act, softplus=sp, flags=flags, io="f32", seed=B * 11 + T,
+             use_conv=conv)
+
+
+def test_bwd_split_rows_stage3_bf16():
+    """The default plan splits rows when samples x tiles give few waves: stage-3
+    rows (L = 198) for 4 samples and 320 channels, bfloat16, pad and swap."""
+    run_case(B=4, D=320, N=8, T=196, B2=1, K=4, P=1, act=0, softplus=True, flags=3, io="bf16", seed=41)
+
+
 def test_bwd_no_conv_f32():
     run_case(B=3, D=16, N=4, T=10, B2=1, K=1, P=0, act=0, softplus=True, flags=0, io="f32", seed=5,
              use_conv=False)
