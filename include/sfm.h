@@ -199,8 +199,9 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  * of the other segments of its row (the exact linear composition, its decay
  * product taken as exp2(A * summed steps)), and the conv-input gradient at the
  * positions around a segment boundary that the conv windows of both segments
- * reach is the sum of the two segments' partials.  The workspace then also holds the carries, the row
- * means of SFM_FUSE_PAD and those partials.
+ * reach is the sum of the two segments' partials.  The workspace then also
+ * holds the carries, float64 token sums per segment (the row mean of
+ * SFM_FUSE_PAD, added in segment order) and those partials.
  * Environment overrides (diagnostics): SFM_BWD_CHUNKED=1 forces the chunked
  * kernel for channel-first tensors; SFM_BWD_SEGMENTS=n asks the chunked kernel
  * for n segments per row (at most 64; at least the conv window per segment).

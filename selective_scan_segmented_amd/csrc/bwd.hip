@@ -216,12 +216,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             }
         };
 
-        // --- fused aux pad: this row's mean, float64 in index order (as the forward)
+        // --- fused aux pad: this row's mean, float64 in index order (as the forward).
+        // Split rows: a first kernel adds each segment's tokens in float64 and the
+        // partials are added here in segment order (the same value whenever the
+        // float64 sums are exact, as for bfloat16 rows of moderate range); the
+        // carry pass needs it in the first segment only.
+        const double* xpart = reinterpret_cast<const double*>(p.ws + p.meanw_off) + (size_t)rt * S * kWave + lane;
         float mean = 0.0f;
-        if (p.pad_in && SPLIT && !CARRY) {
-            // split rows: the carry pass's first segment wave computed it
-            mean = valid ? p.ws[p.meanw_off + (size_t)b * p.D + d] : 0.0f;
-        } else if (p.pad_in && (!CARRY || s == 0)) {
+        if (p.pad_in && SPLIT && (!CARRY || s == 0)) {
+            double acc = 0.0;
+            for (int sg = 0; sg < S; ++sg) acc += xpart[(size_t)sg * kWave];
+            mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
+        } else if (p.pad_in && !CARRY) {
             double acc = 0.0;
             for (int c0 = 0; c0 < XL; c0 += XW) {
                 const int cnt = min(XW, XL - c0);
@@ -235,7 +241,6 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 for (int c = 0; c < cnt; ++c) acc += (double)Io<IO>::of_bits(xs[lane * XW + c]);
             }
             mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
-            if (CARRY && valid) p.ws[p.meanw_off + (size_t)b * p.D + d] = mean;
         }
         // conv/scan input at padded position q = t0 - P + c (column c of the staged window)
         // An interior chunk (full tile, all Q positions, the x window clear of
@@ -1079,6 +1084,34 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int nb_bc)
     }
 }
 
+// Split rows with the fused pad: each segment's tokens of the unpadded row
+// (padded positions 1 .. L-2 inside the segment) added in float64 in index
+// order, per channel, for the row mean.
+template <typename IO>
+__global__ __launch_bounds__(kWave) void bwd_tokens_kernel(BwdParams p) {
+    const int lane = threadIdx.x;
+    const int S = p.seg, g = blockIdx.x, s = g % S, rt = g / S;
+    const int b = rt / p.tiles, tile = rt - b * p.tiles;
+    const int d0 = tile * kWave, nrows = min(kWave, p.D - d0);
+    const int L = p.L, XL = p.xrow;
+    const int s0 = s * p.cps * p.q, s1 = min(L, s0 + p.cps * p.q);
+    const int lo = max(s0, 1) - 1, hi = min(s1, L - 1) - 1;  // tokens [lo, hi)
+    double acc = 0.0;
+    if (lane < nrows) {
+        const IO* x = static_cast<const IO*>(p.u) + ((size_t)b * p.D + d0 + lane) * XL;
+        int k = lo;
+        for (; k + 8 <= hi; k += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = to_f32(x[k + j]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += (double)v[j];
+        }
+        for (; k < hi; ++k) acc += (double)to_f32(x[k]);
+    }
+    reinterpret_cast<double*>(p.ws + p.meanw_off)[(size_t)g * kWave + lane] = acc;
+}
+
 // Split rows: the conv-input gradient at the kw - 1 positions around each
 // segment boundary, the trailing partial of the segment before it plus the
 // leading partial of the segment after it (in that order).
@@ -1115,6 +1148,7 @@ hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
     else {
         const unsigned grid = (unsigned)(p.B1 * p.tiles * p.seg);
         if (p.seg > 1) {
+            if (p.pad_in) hipLaunchKernelGGL(bwd_tokens_kernel<IO>, dim3(grid), dim3(kWave), 0, s, p);
             hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 2>), dim3(grid), dim3(kWave),
                                (size_t)p.lds_bytes, s, p);
             hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 1>), dim3(grid), dim3(kWave),
@@ -1168,7 +1202,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     p.kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 1;
     // workspace regions, each on 256 bytes: checkpoints [B1 * tiles * seg][cps][ns][64],
     // dB/dC partials, per-channel partials [B1 * seg][kc][D]; split rows add the
-    // carries [B1 * tiles * seg][2 ns + 2][64], the row means [B1][D] and the
+    // carries [B1 * tiles * seg][2 ns + 2][64], float64 token sums [B1 * tiles * seg][64] and the
     // boundary partials [B1 * tiles * seg][2][kw - 1][64]
     auto layout = [&]() {
         const long long waves = (long long)p.B1 * p.tiles * p.seg;
@@ -1180,7 +1214,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         p.pch_off = p.pbc_off + up64(pbc);
         p.car_off = p.pch_off + up64(pch);
         p.meanw_off = p.car_off + (split ? up64(waves * (2 * p.ns + 2) * kWave) : 0);
-        p.seam_off = p.meanw_off + (split ? up64((long long)p.B1 * p.D) : 0);
+        p.seam_off = p.meanw_off + (split ? up64(waves * kWave * 2) : 0);  // one float64 per lane
         *ws_bytes = (size_t)(p.seam_off + (split ? up64(waves * 2 * (p.kw - 1) * kWave) : 0)) * sizeof(float);
     };
     layout();
@@ -1242,7 +1276,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     off += up16(kWave * xw * 4);
     p.lds_bytes = off;
     // Split rows along L when the rows and tiles alone give fewer waves than
-    // the GPU has SIMDs (about two waves per SIMD wanted): segments of at least
+    // the GPU has SIMDs (about eight waves per SIMD wanted): segments of at least
     // 64 positions (kw at least, also the last one) cost a carry pass over the
     // row and a composition of the carries per wave.  SFM_BWD_SEGMENTS=n asks
     // for n segments (tests; the length floor is then kw).
@@ -1250,7 +1284,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         const long long waves = (long long)p.B1 * p.tiles;
         const char* fs = getenv("SFM_BWD_SEGMENTS");
         const bool forced = fs && atoi(fs) > 0;
-        long long want = forced ? atoi(fs) : (waves < 1024 ? (2048 + waves - 1) / waves : 1);
+        long long want = forced ? atoi(fs) : (waves < 1024 ? (8192 + waves - 1) / waves : 1);
         want = std::min<long long>(want, 64);
         if (want > 1) {
             const int floor_pos = forced ? kw : std::max(kw, 64);

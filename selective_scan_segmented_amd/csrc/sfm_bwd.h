@@ -46,8 +46,8 @@ struct BwdParams {
     // `cps` chunks, one wave each.  A carry pass writes per segment wave (car_off)
     // the state reached from zero at its end [ns], the carried output gradient
     // reached from zero at its start [ns], and the two step sums (forward,
-    // reverse) [2], each over 64 lanes; the fused pad's row means [B1][D]
-    // (meanw_off); the conv-input gradient at the kw - 1 positions around each
+    // reverse) [2], each over 64 lanes; the fused pad's float64 token sums per
+    // segment wave [64] (meanw_off); the conv-input gradient at the kw - 1 positions around each
     // segment boundary comes as two partials per segment wave [2][kw - 1][64]
     // (seam_off: the segment's leading and trailing ones) added by a seam kernel.
     int seg, cps, kw;

@@ -188,27 +188,37 @@ def ws_expect_split(B, D, N, L, K, segs, cps, kw):
     """Workspace floats with rows split into `segs` segments of `cps` chunks: the
     checkpoints per segment wave, the dB/dC partials, per-channel partials per
     (sample, segment), then the carries per segment wave (state, output gradient,
-    two step sums), the row means and the boundary partials [2][kw - 1][64]."""
+    two step sums), the float64 token sums per segment wave (for the fused pad's
+    row mean) and the boundary partials [2][kw - 1][64]."""
     ns = 4 if N <= 4 else (8 if N <= 8 else 16)
     tiles = (D + 63) // 64
     up = lambda v: (v + 63) // 64 * 64
     kc = N + 2 + (1 + K if K else 0)
     waves = B * tiles * segs
     return 4 * (up(waves * cps * ns * 64) + up(tiles * B * L * 2 * ns) + up(B * segs * kc * D) +
-                up(waves * (2 * ns + 2) * 64) + up(B * D) + up(waves * 2 * (kw - 1) * 64))
+                up(waves * (2 * ns + 2) * 64) + up(waves * 64 * 2) + up(waves * 2 * (kw - 1) * 64))
 
 
 def test_bwd_workspace_size_split_rows():
     """Few samples x tiles (here 1 x 1) on long rows: the chunked plan splits each
     row into segments of 64 positions or more; the reported size is that layout."""
-    # N = 16: chunks of 2 positions, 2001 chunks; about 2048 waves wanted, capped at
+    # N = 16: chunks of 2 positions, 2001 chunks; about 8192 waves wanted, capped at
     # 64 segments of 32 chunks -> 63 segments, the last of 34 positions
     assert sfm.sfm_selective_scan_bwd_workspace_size(1, 1, 64, 16, 4002, 4, "bf16", 3) == \
         ws_expect_split(1, 64, 16, 4002, 4, 63, 32, 4)
-    # 8 samples x 5 tiles = 40 waves: 52 segments wanted; 1001 chunks of 4 positions
-    # (N = 8), 20 chunks a segment would leave a last one of 2 positions, so 21 -> 48
+    # 8 samples x 5 tiles = 40 waves: 205 segments wanted, capped at 64; 1001 chunks of
+    # 4 positions (N = 8), 16 a segment (the 64-position floor) -> 63, the last of 34
     assert sfm.sfm_selective_scan_bwd_workspace_size(8, 1, 320, 8, 4002, 0, "bf16", 0) == \
-        ws_expect_split(8, 320, 8, 4002, 0, 48, 21, 1)
+        ws_expect_split(8, 320, 8, 4002, 0, 63, 16, 1)
+    # 2 samples x 1 tile, 1001 chunks: 20 chunks for 52 wanted segments would leave a
+    # last segment of 2 positions (under the window of 4), so 21 chunks -> 48
+    import os
+    os.environ["SFM_BWD_SEGMENTS"] = "52"
+    try:
+        got = sfm.sfm_selective_scan_bwd_workspace_size(2, 1, 64, 8, 4002, 4, "bf16", 0)
+    finally:
+        del os.environ["SFM_BWD_SEGMENTS"]
+    assert got == ws_expect_split(2, 64, 8, 4002, 4, 48, 21, 4)
 
 
 def test_aux_pad_bwd_validation(lib):
