@@ -228,17 +228,20 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int sg = 0; sg < S; ++sg) acc += xpart[(size_t)sg * kWave];
             mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
         } else if (p.pad_in && !CARRY) {
+            // windows of MW tokens of all 64 rows (4-byte slots, rows MW slots apart,
+            // MW odd for conflict-free row reads) fill both staging buffers: one
+            // direct transfer per row, lanes = tokens, then one wait per window
+            const int MW = (min(kWave, 2 * p.stage_bytes / (kWave * 4)) - 1) | 1;
+            uint32_t* mwin = reinterpret_cast<uint32_t*>(smem + p.xs_off);
             double acc = 0.0;
-            for (int c0 = 0; c0 < XL; c0 += XW) {
-                const int cnt = min(XW, XL - c0);
+            for (int c0 = 0; c0 < XL; c0 += MW) {
+                const int cnt = min(MW, XL - c0);
+                wave_lds_sync();  // the previous window's reads are done
+                if (lane < cnt)
+                    for (int r = 0; r < nrows; ++r) dma_at<EB, 0>(xg + (size_t)r * XL + c0 + lane, mwin + r * MW);
+                wait_vmem();
                 wave_lds_sync();
-                for (int e = lane; e < kWave * XW; e += kWave) {
-                    const int r = e / XW;
-                    const int c = e - r * XW;
-                    xs[r * XW + c] = (r < nrows && c < cnt) ? Io<IO>::bits(xg[(size_t)r * XL + c0 + c]) : 0u;
-                }
-                wave_lds_sync();
-                for (int c = 0; c < cnt; ++c) acc += (double)Io<IO>::of_bits(xs[lane * XW + c]);
+                for (int c = 0; c < cnt; ++c) acc += (double)Io<IO>::of_bits(mwin[lane * MW + c]);
             }
             mean = to_f32(Io<IO>::from_f64(acc / (double)XL));
         }
