@@ -49,6 +49,72 @@ constexpr int kRedStride = 68;  // floats per row of the transpose buffer (16-by
 
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + exp2_fast(-v * kLog2e)); }
 
+// Sums over the 64 lanes of v[0 .. V) (V = 8, 16 or 32), without LDS: a butterfly
+// whose exchanges halve the values each lane carries (lanes l and l^32, then
+// l^16, by lane swaps; then l^15 and l^7, the mirrors inside 16- and 8-lane
+// rows, and l^2 by DPP), followed by plain pairwise sums once one value is
+// left.  The exchange masks are independent bits, so every lane's result
+// covers all 64 lanes; value j ends in the lanes with lane >> (6 - log2 V) == j.
+template <int V>
+__device__ __forceinline__ float wave_sum_values(const float (&v)[V], int lane) {
+    static_assert(V == 8 || V == 16 || V == 32, "8, 16 or 32 values");
+    auto dpp = [](float x, auto ctrlc) __attribute__((always_inline)) {
+        constexpr int C = decltype(ctrlc)::value;
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), C, 0xF, 0xF, false));
+    };
+    using Mirror = std::integral_constant<int, 0x140>;      // lane 15 - i of its 16-lane row
+    using HalfMirror = std::integral_constant<int, 0x141>;  // lane 7 - i of its 8-lane half row
+    using Xor2 = std::integral_constant<int, 0x4E>;         // quad permute [2, 3, 0, 1]
+    using Xor1 = std::integral_constant<int, 0xB1>;         // quad permute [1, 0, 3, 2]
+    float a[V / 2];
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+        // lanes 0-31 keep value j, lanes 32-63 value j + V/2
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j + V / 2]), false,
+                                                        false);
+        a[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    float b[V / 4];
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+        // even 16-lane rows keep value j, odd rows j + V/4
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[j]), __float_as_uint(a[j + V / 4]), false,
+                                                        false);
+        b[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // a halving step by DPP: lanes with the bit clear keep the lower half
+    auto halve = [&](auto& in, auto& out, bool upper, auto ctrlc) __attribute__((always_inline)) {
+        constexpr int H = sizeof(out) / sizeof(float);
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            const float keep = upper ? in[j + H] : in[j];
+            const float send = upper ? in[j] : in[j + H];
+            out[j] = keep + dpp(send, ctrlc);
+        }
+    };
+    float x;
+    if constexpr (V == 32) {
+        float c[4], d[2], e[1];
+        halve(b, c, (lane & 8) != 0, Mirror{});
+        halve(c, d, (lane & 4) != 0, HalfMirror{});
+        halve(d, e, (lane & 2) != 0, Xor2{});
+        x = e[0];
+    } else if constexpr (V == 16) {
+        float c[2], d[1];
+        halve(b, c, (lane & 8) != 0, Mirror{});
+        halve(c, d, (lane & 4) != 0, HalfMirror{});
+        x = d[0];
+        x += dpp(x, Xor2{});
+    } else {
+        float c[1];
+        halve(b, c, (lane & 8) != 0, Mirror{});
+        x = c[0];
+        x += dpp(x, HalfMirror{});
+        x += dpp(x, Xor2{});
+    }
+    return x + dpp(x, Xor1{});
+}
+
 // MODE 0: whole rows; 1: rows split into segments (after the carry pass); 2: the carry pass.
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q, int MODE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kernel(BwdParams p) {
@@ -620,8 +686,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 // (position q is complete only after dy at q was read; the two dy values at the
 // sample ends are read up front because swap_dy moves them).  Both blocks leave
 // with 16-byte stores once the sample is done.  B and C of the sample are
-// widened to float32 once.  The dB/dC transpose uses 32 rows; two lanes sum
-// the two halves of a row.
+// widened to float32 once.  dB/dC of each position are summed over the
+// channels in registers (wave_sum_values), so the kernel's LDS is the three
+// blocks and B/C only: seven workgroups fit a compute unit at stage-4 sizes.
 // Channel-last staging: `rows` position rows of this tile (units_per_row 16-byte
 // units each, rows `stride` elements apart from `base`) into LDS back to back,
 // unit u at l + 16 u.  Four transfers share one LDS base; nothing is waited for.
@@ -649,7 +716,7 @@ __device__ __forceinline__ void dma_rows(const IO* base, int rows, int stride, i
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q, bool CL>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_whole_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    constexpr int R = 16 / NS;  // positions per dB/dC transpose round (2 * NS * R = 32 rows)
+    constexpr int R = 16 / NS;  // positions per round of the reverse walk
     static_assert(Q % R == 0, "chunk must hold whole transpose rounds");
     constexpr int EB = (int)sizeof(IO);
     const int lane = threadIdx.x;
@@ -672,7 +739,6 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     IO* ys = reinterpret_cast<IO*>(smem + p.dys_off);       // dy, then dx
     float* bs = reinterpret_cast<float*>(smem + p.bc_off);  // [L][NS]
     float* cs = bs + L * NS;                                // [L][NS]
-    float* red = reinterpret_cast<float*>(smem + p.red_off);  // [32][kRedStride]
     const int col = valid ? lane : 0;  // lanes past the tile read channel 0 and mask the value
     const int xrow = col * XL;
     const int row = col * L;
@@ -961,33 +1027,20 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                             if (valid) ys[ti(t)] = from_f32<IO>(dz);
                         }
                     }
-                    // transpose buffer: row (ii, k), column lane
+                    // dB/dC of this position summed over the channels (lanes) in registers:
+                    // value k (dB_n for k = n, dC_n for k = NS + n) in lanes k * 64 / (2 NS) ..
+                    float dv2[2 * NS];
 #pragma unroll
                     for (int n = 0; n < NS; ++n) {
-                        red[(ii * 2 * NS + n) * kRedStride + lane] = dBv[n];
-                        red[(ii * 2 * NS + NS + n) * kRedStride + lane] = dCv[n];
+                        dv2[n] = dBv[n];
+                        dv2[NS + n] = dCv[n];
                     }
+                    const float sum = wave_sum_values<2 * NS>(dv2, lane);
+                    constexpr int kShift = NS == 16 ? 1 : (NS == 8 ? 2 : 3);
+                    if ((lane & ((1 << kShift) - 1)) == 0 && i < cnt)
+                        p.ws[p.pbc_off + (((size_t)tile * p.B1 * p.B2 + b) * L + t0 + i) * 2 * NS + (lane >> kShift)] =
+                            sum;
                 }
-                wave_lds_sync();
-                {
-                    // lanes l and l + 32 sum the two halves of row l % 32:
-                    // position r0 + row / (2NS), state row % NS, B or C
-                    const int rr = lane & 31;
-                    const int ii = rr / (2 * NS);
-                    const int k = rr - ii * 2 * NS;
-                    const int n = k % NS;
-                    const float4* rp = reinterpret_cast<const float4*>(red + rr * kRedStride + (lane >> 5) * 32);
-                    float s = 0.0f;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        const float4 v4 = rp[m];
-                        s += (v4.x + v4.y) + (v4.z + v4.w);
-                    }
-                    s += __shfl_xor(s, 32);
-                    if (lane < 32 && r0 + ii < cnt)
-                        p.ws[p.pbc_off + (((size_t)tile * p.B1 * p.B2 + b) * L + t0 + r0 + ii) * 2 * NS + k] = s;
-                }
-                wave_lds_sync();
             }
         }
         if constexpr (CONV) {
@@ -1241,8 +1294,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         off += up16(kWave * L * eb);
         p.bc_off = off;
         off += up16(2 * L * p.ns * 4);
-        p.red_off = off;
-        off += 32 * kRedStride * 4;
+        p.red_off = off;  // (the dB/dC sums over channels stay in registers)
         const char* force = getenv("SFM_BWD_CHUNKED");  // diagnostics: force the chunked kernel
         if (ok && L <= 4096 && off <= 64 * 1024 && (p.cl || !(force && atoi(force) > 0))) {
             p.whole = 1;
