@@ -229,8 +229,9 @@ def run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io):
         "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}", "B2": b2,
                    "mode": "bwd", "input_sets": len(sets), "workspace_bytes": need,
                    "layout": "channel-last [B, L, D]" if cl else "channel-first [B, D, L]",
-                   "step": "one backward launch + the fixed-order reduce launch of the float32 sums "
-                           "(pad and swap fused)"},
+                   "step": "sfm_selective_scan_bwd: the backward launch (with rows split along L: "
+                           "token sums, carry pass, main pass and seam launches) + the fixed-order "
+                           "reduce launch of the float32 sums (pad and swap fused)"},
         "roofline": {"bound": "alu" if alu / VALU_PEAK_TSLOT >= hbm / HBM_PEAK_GBPS else "hbm",
                      "alu_achieved": round(alu, 3), "alu_peak": round(VALU_PEAK_TSLOT, 3),
                      "alu_frac": round(alu / VALU_PEAK_TSLOT, 4), "hbm_GBps": round(hbm, 1),
