@@ -463,17 +463,19 @@ struct ScanWave {
     }
 
     // Fused aux pad: float64 index-order sum of this lane's whole unpadded row
-    // of sample b, streamed in pieces of ch positions through two LDS areas
-    // (the x areas of both stages, or the x and delta areas of the one stage):
-    // the transfer of piece k+1 is in flight while piece k is summed.  The
-    // areas must be free.
+    // of sample b, streamed in windows through the two halves of the stage
+    // region (every stage's x, delta and raw B/C areas, all free here; each
+    // half a whole number of KB, rows an odd number of words apart): the
+    // transfer of window k+1 is in flight while window k is summed.
     __device__ __forceinline__ void mean1(int b) {
         constexpr int ew = 4 / (int)sizeof(IO);
-        const int XL = p.xrow, step = p.ch;
+        const int XL = p.xrow;
         const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * p.D + d0) * XL;
-        const bool two = p.stages == 2;
-        auto area = [&](int i) __attribute__((always_inline)) { return i ? (two ? xs_of(1) : ds_of(0)) : xs_of(0); };
-        auto stride = [&](int i) __attribute__((always_inline)) { return (i && !two) ? p.drs : p.xrs; };
+        const int half = (p.stages * sb1 / 2) & ~1023;
+        const int rs = (((half / (kWave * 4)) - 1) | 1) * ew;  // row pitch, elements
+        const int step = rs - 2 * (ew - 1);                    // window, with room for word alignment
+        auto area = [&](int i) __attribute__((always_inline)) { return reinterpret_cast<IO*>(own1 + i * half); };
+        auto stride = [&](int) __attribute__((always_inline)) { return rs; };
         auto issue = [&](int c0, int i) __attribute__((always_inline)) {
             const int lo = c0 / ew * ew;
             const int hi = min((c0 + min(step, XL - c0) + ew - 1) / ew * ew, XL);
