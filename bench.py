@@ -307,6 +307,9 @@ def main():
                          "copy: a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (pad, conv+scan, swap) instead of one")
+    ap.add_argument("--fwd-ws", action="store_true",
+                    help="run the fused step through sfm_selective_scan_fwd_ws (rows split along L across the "
+                         "GPU, with a device workspace, where the plan splits them)")
     ap.add_argument("--layout", choices=["bdl", "bld"], default="bdl",
                     help="bdl: channel-first [B, D, L] (default); bld: channel-last [B, L, D] activations and "
                          "[B, L, N] B/C (fused step only)")
@@ -400,6 +403,12 @@ def main():
         swap_args = (vp(s["y"]), vp(s["y"]), w.B, w.D, w.L - 2, 1, io, sp)
         calls.append((pad_args, scan_args, swap_args))
     b1_out = ctypes.c_int64()
+    ws_t = None
+    if a.fwd_ws:
+        if not fused or cl:
+            raise SystemExit("--fwd-ws times the fused channel-first step")
+        need = sfm.sfm_selective_scan_fwd_ws_size(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, 3)
+        ws_t = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def step(i, ev=None):
         pad_args, scan_args, swap_args = calls[i % nsets]
@@ -411,7 +420,10 @@ def main():
                 raise RuntimeError(f"pad failed: {lib.sfm_last_error().decode()}")
         if ev is not None:
             hip.record(ev[0], sp)
-        rc = lib.sfm_selective_scan_fwd_ex(*scan_args)
+        if ws_t is not None:
+            rc = lib.sfm_selective_scan_fwd_ws(*scan_args[:-1], vp(ws_t), ws_t.numel(), sp)
+        else:
+            rc = lib.sfm_selective_scan_fwd_ex(*scan_args)
         if ev is not None:
             hip.record(ev[1], sp)
         if rc:
@@ -499,7 +511,9 @@ def main():
         "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}",
                    "B2": b2, "B1": w.B // b2, "mode": a.mode, "input_sets": nsets,
                    "layout": "channel-last [B, L, D]" if cl else "channel-first [B, D, L]",
-                   "step": ("pick_b1 + one launch of pad/conv/scan/swap" if fused else
+                   "step": ("pick_b1 + sfm_selective_scan_fwd_ws (token sums, carry pass, output pass where "
+                            "rows are split)" if ws_t is not None else
+                            "pick_b1 + one launch of pad/conv/scan/swap" if fused else
                             "pick_b1 + pad + conv/scan + swap (3 launches)") if a.mode == "step" else "scan only"},
         "roofline": roof,
         "hbm": {"scan_alg_GBps": round(hbm_gbps, 1), "frac_of_8TBps": round(hbm_frac, 4)},

@@ -145,6 +145,40 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
                                      void* stream);
 
 /*
+ * sfm_selective_scan_fwd_ws -- sfm_selective_scan_fwd_ex (same arguments, flags
+ * and results within the parity tolerance) with a caller-owned device
+ * workspace, for rows too long for the in-LDS carries: when samples times
+ * 64-channel tiles give fewer than 1024 waves (channel-first only), each sample
+ * row is split along L into segments of at least 64 positions, one wave each,
+ * in three launches -- the fused pad's float64 token sums per segment, a carry
+ * pass (each segment's state reached from zero and the sum of its steps), and
+ * the output pass (each segment composes the earlier segments' carries, the
+ * recurrence being linear in its entering state with the segment's decay
+ * product taken as exp2(A * summed steps), then writes its y).  Every other
+ * shape, and any call whose workspace size below is 0, runs
+ * sfm_selective_scan_fwd_ex itself (workspace unused, may be NULL).
+ * workspace: device memory of at least sfm_selective_scan_fwd_ws_size() bytes
+ *   (same sizes, conv_k -- 0 without conv --, io_dtype, flags), owned by the
+ *   caller, not overlapping any tensor; it holds the carries [rows x tiles x
+ *   segments][2 Np + 2][64] f32 and the token sums for the call's duration.
+ * SFM_BWD_SEGMENTS=n (diagnostics) asks for n segments here too.
+ * Returns SFM_OK, or NULL/SHAPE/DTYPE/ALIAS/ALIGN/UNSUPPORTED (nothing
+ * launched), HIP.
+ */
+sfm_status sfm_selective_scan_fwd_ws(const void* u, const void* delta, const float* A, const void* Bm,
+                                     const void* Cm, const float* Dskip, const float* delta_bias,
+                                     int delta_softplus, const float* conv_w, const float* conv_b,
+                                     int conv_k, int conv_pad_left, int conv_act, void* y, int64_t B1,
+                                     int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype, int flags,
+                                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes sfm_selective_scan_fwd_ws needs for these sizes (host only;
+ * conv_k = 0 for no conv); 0 when the call runs the regular forward.
+ * Returns SFM_OK or NULL/SHAPE/DTYPE. */
+sfm_status sfm_selective_scan_fwd_ws_size(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
+                                          int conv_k, int io_dtype, int flags, int64_t* bytes);
+
+/*
  * sfm_dwconv1d_fold -- boundary-masked depthwise conv1d over folded rows
  * ([TL] "第二个模块", conv-boundary part; [SBW] 8.1 item 5):
  *   out[b,d,t] = act(bias[d] + sum_{j<K} w[d,j] * x[b,d,t+j-pad_left]),

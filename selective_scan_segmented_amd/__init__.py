@@ -15,7 +15,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_selective_scan_bwd",
+__all__ = ["sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_selective_scan_fwd_ws",
+           "sfm_selective_scan_fwd_ws_size", "sfm_selective_scan_bwd",
            "sfm_selective_scan_bwd_workspace_size", "sfm_dwconv1d_fold", "sfm_aux_pad_swap", "sfm_aux_pad_bwd",
            "sfm_aux_pad_bwd_ex",
            "sfm_pick_b1", "sfm_scan_plan_string", "sfm_version", "library_path", "load_library", "SFMError"]
@@ -51,6 +52,10 @@ def load_library():
                                            i64, i64, i64, i64, i64, ci, vp]
     lib.sfm_selective_scan_fwd_ex.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
                                               i64, i64, i64, i64, i64, ci, ci, vp]
+    lib.sfm_selective_scan_fwd_ws.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
+                                              i64, i64, i64, i64, i64, ci, ci, vp, i64, vp]
+    lib.sfm_selective_scan_fwd_ws_size.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci,
+                                                   ctypes.POINTER(ctypes.c_int64)]
     lib.sfm_dwconv1d_fold.argtypes = [vp, fp, fp, vp, i64, i64, i64, i64, ci, ci, ci, ci, vp]
     lib.sfm_selective_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
                                            vp, vp, fp, fp, fp, fp, fp, fp, fp,
@@ -62,7 +67,8 @@ def load_library():
     lib.sfm_aux_pad_swap.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
     lib.sfm_pick_b1.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.sfm_scan_plan_string.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci, ctypes.c_char_p, i64]
-    for f in ("sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_dwconv1d_fold", "sfm_aux_pad_swap",
+    for f in ("sfm_selective_scan_fwd", "sfm_selective_scan_fwd_ex", "sfm_selective_scan_fwd_ws",
+              "sfm_selective_scan_fwd_ws_size", "sfm_dwconv1d_fold", "sfm_aux_pad_swap",
               "sfm_pick_b1", "sfm_version", "sfm_scan_plan_string", "sfm_selective_scan_bwd",
               "sfm_selective_scan_bwd_workspace_size", "sfm_aux_pad_bwd", "sfm_aux_pad_bwd_ex"):
         getattr(lib, f).restype = ctypes.c_int
@@ -146,6 +152,14 @@ def sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, 
     [B, D, L-2] stage input) and/or the aux swap of y (flags & SFM_FUSE_SWAP) fused in.
     flags & SFM_LAYOUT_BLD: channel-last tensors, u/delta/y [B, L, D] (u [B, L-2, D] with
     the pad), Bm/Cm [B, L, N]."""
+    return _fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b, conv_pad_left,
+                   conv_act, y, B2, flags, stream, False)
+
+
+def _fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b, conv_pad_left, conv_act, y,
+            B2, flags, stream, workspace):
+    """Argument marshalling of the two fused forward entry points (workspace False:
+    sfm_selective_scan_fwd_ex; else sfm_selective_scan_fwd_ws)."""
     torch = _torch()
     io = _io_code(u)
     cl = bool(flags & SFM_LAYOUT_BLD)
@@ -175,12 +189,43 @@ def sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, 
     if y is None:
         y = torch.empty(tl(D, L), dtype=u.dtype, device=u.device)
     _dev(y, "y", u.dtype, tl(D, L))
-    rc = load_library().sfm_selective_scan_fwd_ex(
-        _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(delta_bias), int(bool(delta_softplus)),
-        _ptr(conv_w), _ptr(conv_b), K, int(conv_pad_left), _ACT[conv_act], _ptr(y),
-        B // B2, B2, D, N, L, io, int(flags), _stream(stream))
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(conv_w), _ptr(conv_b), K, int(conv_pad_left), _ACT[conv_act], _ptr(y),
+            B // B2, B2, D, N, L, io, int(flags))
+    if workspace is False:
+        rc = load_library().sfm_selective_scan_fwd_ex(*args, _stream(stream))
+    else:
+        need = sfm_selective_scan_fwd_ws_size(B // B2, B2, D, N, L, K, "bf16" if io == SFM_BF16 else "f32",
+                                              int(flags))
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=u.device)
+        _dev(workspace, "workspace")
+        rc = load_library().sfm_selective_scan_fwd_ws(*args, _ptr(workspace),
+                                                      workspace.numel() * workspace.element_size(),
+                                                      _stream(stream))
     _check(rc, "sfm_selective_scan_fwd")
     return y
+
+
+def sfm_selective_scan_fwd_ws(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, delta_softplus=True,
+                              conv_w=None, conv_b=None, conv_pad_left=1, conv_act=None, y=None, B2=1,
+                              flags=0, workspace=None, stream=None):
+    """sfm_selective_scan_fwd_ex with a device workspace (a uint8 GPU tensor of at least
+    sfm_selective_scan_fwd_ws_size() bytes; allocated here when None): rows too long
+    for the in-LDS carries are split along L across the whole GPU."""
+    return _fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b, conv_pad_left,
+                   conv_act, y, B2, flags, stream, workspace)
+
+
+def sfm_selective_scan_fwd_ws_size(B1: int, B2: int, D: int, N: int, L: int, conv_k: int = 4,
+                                   io: str = "bf16", flags: int = 0) -> int:
+    """Workspace bytes sfm_selective_scan_fwd_ws needs (host only; 0: the regular forward runs)."""
+    out = ctypes.c_int64(0)
+    _check(load_library().sfm_selective_scan_fwd_ws_size(B1, B2, D, N, L, conv_k,
+                                                         SFM_BF16 if io == "bf16" else SFM_F32, flags,
+                                                         ctypes.byref(out)),
+           "sfm_selective_scan_fwd_ws_size")
+    return int(out.value)
 
 
 def sfm_selective_scan_bwd_workspace_size(B1: int, B2: int, D: int, N: int, L: int, conv_k: int = 4,

@@ -115,11 +115,13 @@ __device__ __forceinline__ float wave_sum_values(const float (&v)[V], int lane) 
     return x + dpp(x, Xor1{});
 }
 
-// MODE 0: whole rows; 1: rows split into segments (after the carry pass); 2: the carry pass.
+// MODE 0: whole rows; 1: rows split into segments (after the carry pass); 2: the carry
+// pass; 3: the forward output of split rows (after the carry pass's forward half).
 template <typename IO, int NS, int KW, bool CONV, bool SP, bool SILU, int Q, int MODE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kernel(BwdParams p) {
     constexpr bool SPLIT = MODE != 0;
     constexpr bool CARRY = MODE == 2;
+    constexpr bool FWD = MODE == 3;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     constexpr int XW = Q + KW - 1;  // x window columns of a chunk
     constexpr int R = Q < 32 / NS ? Q : 32 / NS;  // positions per dB/dC transpose round (2*NS*R <= 64 rows)
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         // contiguous in the workspace, one 4-byte transfer per state).  Nothing is waited for;
         // the buffer was last read by LDS instructions of this wave, which have
         // completed before a transfer can write it.
-        auto issue = [&](int t0, int cnt, bool with_dy, int ck, int i) __attribute__((always_inline)) {
+        auto issue = [&](int t0, int cnt, bool with_dy, bool with_c, int ck, int i) __attribute__((always_inline)) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             // An opaque copy of the lane index: the per-lane transfer addresses are
             // recomputed here instead of being hoisted out of the chunk loop, where
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 const int e2 = e < half ? e : e - half;
                 const int n = e2 / Q;
                 const int c = e2 - n * Q;
-                const IO* src = (e < 2 * half && c < cnt && (e < half || with_dy))
+                const IO* src = (e < 2 * half && c < cnt && (e < half || with_c))
                                     ? (e < half ? bgl : cgl) + (size_t)n * L + t0 + c
                                     : dummy;
                 dma_at<EB, 0>(src, rb);
@@ -272,13 +274,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         };
         // After the chunk in the current buffer has landed: widen B/C to float32
         // [c][n]; states n >= N and positions past the sample are zero.
-        auto widen = [&](int cnt, bool with_dy) __attribute__((always_inline)) {
+        auto widen = [&](int cnt, bool with_c) __attribute__((always_inline)) {
             if (lane < Q * NS) {
                 const int c = lane / NS;
                 const int n = lane - c * NS;
                 const bool in = n < N && c < cnt;
                 bs[lane] = in ? Io<IO>::of_bits(braw[n * Q + c]) : 0.0f;
-                cs[lane] = (in && with_dy) ? Io<IO>::of_bits(braw[N * Q + n * Q + c]) : 0.0f;
+                cs[lane] = (in && with_c) ? Io<IO>::of_bits(braw[N * Q + n * Q + c]) : 0.0f;
             }
         };
 
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         // (the carry pass needs the forward for every segment but the row's last)
         const int cstop = (!CARRY || s < S - 1) ? cend : cbeg;
         wave_lds_sync();
-        if (cbeg < cstop) issue(cbeg * Q, min(Q, L - cbeg * Q), false, -1, 0);
+        if (cbeg < cstop) issue(cbeg * Q, min(Q, L - cbeg * Q), false, FWD, -1, 0);
         for (int c = cbeg; c < cstop; ++c) {
             const int t0 = c * Q;
             const int cnt = min(Q, L - t0);
@@ -378,12 +380,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             // widen before the next transfers go out: any wait on vector memory
             // the compiler puts here then covers nothing in flight
             use_buf(bi);
-            widen(cnt, false);
-            if (!CARRY && (SPLIT || c > 0)) {
+            widen(cnt, FWD);
+            if (!CARRY && !FWD && (SPLIT || c > 0)) {
 #pragma unroll
                 for (int n = 0; n < NS; ++n) ws[((size_t)(c - cbeg) * NS + n) * kWave + lane] = h[n];
             }
-            if (c + 1 < cend) issue(t0 + Q, min(Q, L - t0 - Q), false, -1, bi ^ 1);
+            if (c + 1 < cend) issue(t0 + Q, min(Q, L - t0 - Q), false, FWD, -1, bi ^ 1);
             wave_lds_sync();
             auto fwd = [&](auto fastc) __attribute__((always_inline)) {
                 constexpr bool FAST = decltype(fastc)::value;
@@ -397,6 +399,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                         const float bx = du_ * bs[i * NS + n];
                         h[n] = (!FAST && t0 + i == 0) ? bx : __builtin_fmaf(exp2_fast(dt * kLog2e * A[n]), h[n], bx);
                     }
+                    if constexpr (FWD) {
+                        // y = C.h + D u, in place of this position's delta (already read)
+                        float yv = Dk * u;
+#pragma unroll
+                        for (int n = 0; n < NS; ++n) yv = __builtin_fmaf(cs[i * NS + n], h[n], yv);
+                        dls[lane * Q + i] = __float_as_uint(yv);
+                    }
                 }
             };
             if constexpr (kInteriorPath) {
@@ -404,6 +413,20 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 else fwd(std::false_type{});
             } else {
                 fwd(std::false_type{});
+            }
+            if constexpr (FWD) {
+                // this chunk's y, coalesced (the fused swap exchanges the sample's ends)
+                wave_lds_sync();
+                IO* yo = static_cast<IO*>(p.y) + ((size_t)b * p.D + d0) * L;
+                for (int e = lane; e < kWave * Q; e += kWave) {
+                    const int r = e / Q;
+                    const int cc = e - r * Q;
+                    if (r < nrows && cc < cnt) {
+                        int t = t0 + cc;
+                        if (p.swap_out && L > 1) t = t == 0 ? L - 1 : (t == L - 1 ? 0 : t);
+                        yo[(size_t)r * L + t] = from_f32<IO>(__uint_as_float(dls[r * Q + cc]));
+                    }
+                }
             }
             bi ^= 1;
         }
@@ -419,7 +442,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         // start, reached from zero at its end (no states needed: only the decays
         // and C*dy), and the sum of Delta*log2e, for every segment but the row's first
         if constexpr (CARRY) {
-            if (s > 0) {
+            if (s > 0 && !p.fwd) {
                 float Gc[NS];
 #pragma unroll
                 for (int n = 0; n < NS; ++n) Gc[n] = 0.0f;
@@ -427,7 +450,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 wait_vmem();
                 wave_lds_sync();
                 bi = 0;
-                issue((cend - 1) * Q, min(Q, L - (cend - 1) * Q), true, -1, 0);
+                issue((cend - 1) * Q, min(Q, L - (cend - 1) * Q), true, true, -1, 0);
                 for (int c = cend - 1; c >= cbeg; --c) {
                     const int t0 = c * Q;
                     const int cnt = min(Q, L - t0);
@@ -435,7 +458,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                     wave_lds_sync();
                     use_buf(bi);
                     widen(cnt, true);
-                    if (c > cbeg) issue(t0 - Q, Q, true, -1, bi ^ 1);
+                    if (c > cbeg) issue(t0 - Q, Q, true, true, -1, bi ^ 1);
                     wave_lds_sync();
                     for (int i = cnt - 1; i >= 0; --i) {
                         float z, u, v, dt;
@@ -453,7 +476,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 for (int n = 0; n < NS; ++n) carv(s, NS + n) = Gc[n];
                 carv(s, 2 * NS + 1) = sdr;
             }
-        } else {
+        } else if constexpr (!FWD) {
 
         // --- sweep 2: chunks in reverse.  Chunk c-1's transfers (with its
         // entering state) go out once chunk c has landed; chunk c's ddelta (in
@@ -507,7 +530,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         wait_vmem();  // the checkpoints stored above have landed before they are read back
         wave_lds_sync();
         bi = 0;
-        issue((cend - 1) * Q, min(Q, L - (cend - 1) * Q), true, cend - 1 - cbeg, 0);
+        issue((cend - 1) * Q, min(Q, L - (cend - 1) * Q), true, true, cend - 1 - cbeg, 0);
         int pend = -1;  // chunk whose outputs wait in buffer bi ^ 1 and dxs
         for (int c = cend - 1; c >= cbeg; --c) {
             const int t0 = c * Q;
@@ -520,7 +543,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
                 use_buf(bi ^ 1);
                 write_out(pend);
             }
-            if (c > cbeg) issue(t0 - Q, Q, true, c - 1 - cbeg, bi ^ 1);
+            if (c > cbeg) issue(t0 - Q, Q, true, true, c - 1 - cbeg, bi ^ 1);
             use_buf(bi);
             for (int e = lane; e < kWave * XW; e += kWave) dxs[e] = 0.0f;
             float hin[NS];
@@ -661,7 +684,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         wave_lds_sync();
         }  // sweep 2
     }
-    if (!CARRY && valid) {
+    if (!CARRY && !FWD && valid) {
         // this row segment's per-channel sums (rows dA[0..N), dD, dbias, dconv_b, dconv_w[0..K))
         float* pc = p.ws + p.pch_off + ((size_t)b1 * S + s) * p.kc * p.D + d;
 #pragma unroll
@@ -1201,7 +1224,14 @@ hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
     else if (p.whole)
         hipLaunchKernelGGL((bwd_whole_kernel<IO, NS, KW, CONV, SP, SILU, Q, false>), dim3((unsigned)(p.B1 * p.tiles)),
                            dim3(kWave), (size_t)p.lds_bytes, s, p);
-    else {
+    else if (p.fwd) {  // split-row forward: token sums, the carry pass's forward half, the output pass
+        const unsigned grid = (unsigned)(p.B1 * p.tiles * p.seg);
+        if (p.pad_in) hipLaunchKernelGGL(bwd_tokens_kernel<IO>, dim3(grid), dim3(kWave), 0, s, p);
+        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 2>), dim3(grid), dim3(kWave),
+                           (size_t)p.lds_bytes, s, p);
+        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 3>), dim3(grid), dim3(kWave),
+                           (size_t)p.lds_bytes, s, p);
+    } else {
         const unsigned grid = (unsigned)(p.B1 * p.tiles * p.seg);
         if (p.seg > 1) {
             if (p.pad_in) hipLaunchKernelGGL(bwd_tokens_kernel<IO>, dim3(grid), dim3(kWave), 0, s, p);
@@ -1262,16 +1292,16 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     // boundary partials [B1 * tiles * seg][2][kw - 1][64]
     auto layout = [&]() {
         const long long waves = (long long)p.B1 * p.tiles * p.seg;
-        const long long ck = waves * p.cps * p.ns * kWave;
-        const long long pbc = (long long)p.tiles * p.B1 * p.B2 * p.L * 2 * p.ns;
-        const long long pch = (long long)p.B1 * p.seg * p.kc * p.D;
+        const long long ck = p.fwd ? 0 : waves * p.cps * p.ns * kWave;  // (the forward keeps only the carries)
+        const long long pbc = p.fwd ? 0 : (long long)p.tiles * p.B1 * p.B2 * p.L * 2 * p.ns;
+        const long long pch = p.fwd ? 0 : (long long)p.B1 * p.seg * p.kc * p.D;
         const bool split = p.seg > 1;
         p.pbc_off = up64(ck);
         p.pch_off = p.pbc_off + up64(pbc);
         p.car_off = p.pch_off + up64(pch);
         p.meanw_off = p.car_off + (split ? up64(waves * (2 * p.ns + 2) * kWave) : 0);
         p.seam_off = p.meanw_off + (split ? up64(waves * kWave * 2) : 0);  // one float64 per lane
-        *ws_bytes = (size_t)(p.seam_off + (split ? up64(waves * 2 * (p.kw - 1) * kWave) : 0)) * sizeof(float);
+        *ws_bytes = (size_t)(p.seam_off + (split && !p.fwd ? up64(waves * 2 * (p.kw - 1) * kWave) : 0)) * sizeof(float);
     };
     layout();
     auto up16 = [](long long v) { return (int)((v + 15) & ~15LL); };
@@ -1296,7 +1326,7 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         off += up16(2 * L * p.ns * 4);
         p.red_off = off;  // (the dB/dC sums over channels stay in registers)
         const char* force = getenv("SFM_BWD_CHUNKED");  // diagnostics: force the chunked kernel
-        if (ok && L <= 4096 && off <= 64 * 1024 && (p.cl || !(force && atoi(force) > 0))) {
+        if (!p.fwd && ok && L <= 4096 && off <= 64 * 1024 && (p.cl || !(force && atoi(force) > 0))) {
             p.whole = 1;
             p.mean_off = p.braw_off = p.hin_off = p.stage_bytes = 0;
             p.lds_bytes = off;
@@ -1355,6 +1385,10 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     }
     layout();
     return p.lds_bytes <= 64 * 1024;
+}
+
+hipError_t launch_fwd_split(const BwdParams& p, int io_dtype, hipStream_t s) {
+    return io_dtype == 0 ? launch_bio<float>(p, s) : launch_bio<__bf16>(p, s);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t s) {

@@ -92,11 +92,11 @@ sfm_status sfm_selective_scan_fwd(const void* u, const void* delta, const float*
                                      conv_pad_left, conv_act, y, B1, B2, D, N, L, io_dtype, 0, stream);
 }
 
-sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* Bm,
-                                     const void* Cm, const float* Dskip, const float* delta_bias,
-                                     int delta_softplus, const float* conv_w, const float* conv_b, int conv_k,
-                                     int conv_pad_left, int conv_act, void* y, int64_t B1, int64_t B2, int64_t D,
-                                     int64_t N, int64_t L, int io_dtype, int flags, void* stream) {
+// Argument checks shared by the forward entry points (nothing launched on failure).
+static sfm_status fwd_check(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                            int delta_softplus, const float* conv_w, int conv_k, int conv_pad_left, int conv_act,
+                            void* y, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype,
+                            int flags) {
     if (!u || !delta || !A || !Bm || !Cm || !y)
         return fail(SFM_ERR_NULL, "sfm_selective_scan_fwd: u, delta, A, Bm, Cm and y are required");
     if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP | SFM_LAYOUT_BLD))
@@ -137,6 +137,21 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
                          rng("A", A, D * N * 4)};
     for (const Range& r : ins)
         if (overlap(ry, r)) return fail(SFM_ERR_ALIAS, "sfm_selective_scan_fwd: y overlaps %s", r.name);
+
+    return SFM_OK;
+}
+
+sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* Bm,
+                                     const void* Cm, const float* Dskip, const float* delta_bias,
+                                     int delta_softplus, const float* conv_w, const float* conv_b, int conv_k,
+                                     int conv_pad_left, int conv_act, void* y, int64_t B1, int64_t B2, int64_t D,
+                                     int64_t N, int64_t L, int io_dtype, int flags, void* stream) {
+    const sfm_status st = fwd_check(u, delta, A, Bm, Cm, delta_softplus, conv_w, conv_k, conv_pad_left, conv_act, y,
+                                    B1, B2, D, N, L, io_dtype, flags);
+    if (st != SFM_OK) return st;
+    const bool pad_in = (flags & SFM_FUSE_PAD) != 0;
+    const int eb = io_bytes(io_dtype);
+    const int64_t XL = pad_in ? L - 2 : L;
 
     if (flags & SFM_LAYOUT_BLD) {
         sfm::ClParams c{};
@@ -509,6 +524,81 @@ extern "C" sfm_status sfm_selective_scan_bwd(
     p.dconv_b = dconv_b;
     p.ws = static_cast<float*>(workspace);
     return hip_status(sfm::launch_bwd(p, io_dtype, static_cast<hipStream_t>(stream)), who);
+}
+
+// Split-row forward plan (p.seg > 1) or none: channel-last rows, rows that the
+// chunked planner does not split, or no plan -> the regular forward.
+static bool fwd_split_plan(sfm::BwdParams& p, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
+                           const float* conv_w, int conv_k, int conv_pad_left, int conv_act, int delta_softplus,
+                           int flags, int eb, size_t* need) {
+    if (flags & SFM_LAYOUT_BLD) return false;
+    fill_bwd(p, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, flags);
+    p.fwd = 1;
+    p.swap_out = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+    *need = 0;
+    return sfm::plan_bwd(p, eb, need) && p.seg > 1;
+}
+
+extern "C" sfm_status sfm_selective_scan_fwd_ws_size(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
+                                                     int conv_k, int io_dtype, int flags, int64_t* bytes) {
+    const char* who = "sfm_selective_scan_fwd_ws_size";
+    if (!bytes) return fail(SFM_ERR_NULL, "%s: bytes is required", who);
+    if (io_dtype != SFM_F32 && io_dtype != SFM_BF16) return fail(SFM_ERR_DTYPE, "%s: io_dtype %d", who, io_dtype);
+    if (flags & ~(SFM_FUSE_PAD | SFM_FUSE_SWAP | SFM_LAYOUT_BLD))
+        return fail(SFM_ERR_SHAPE, "%s: unknown flags 0x%x", who, flags);
+    if (!sane(B1, 1 << 24) || !sane(B2, 1 << 16) || !sane(D, 1 << 20) || !sane(L, 1 << 24) || N < 1 ||
+        N > SFM_MAX_N || ((flags & SFM_FUSE_PAD) && L < 3) || conv_k < 0 || conv_k > SFM_MAX_K)
+        return fail(SFM_ERR_SHAPE, "%s: B1=%lld B2=%lld D=%lld N=%lld L=%lld conv_k=%d out of range", who,
+                    (long long)B1, (long long)B2, (long long)D, (long long)N, (long long)L, conv_k);
+    static const float dummy = 0.0f;
+    sfm::BwdParams p{};
+    size_t need = 0;
+    *bytes = fwd_split_plan(p, B1, B2, D, N, L, conv_k ? &dummy : nullptr, conv_k ? conv_k : 1, 0, 0, 1, flags,
+                            io_bytes(io_dtype), &need)
+                 ? (int64_t)need
+                 : 0;
+    return ok();
+}
+
+extern "C" sfm_status sfm_selective_scan_fwd_ws(const void* u, const void* delta, const float* A, const void* Bm,
+                                                const void* Cm, const float* Dskip, const float* delta_bias,
+                                                int delta_softplus, const float* conv_w, const float* conv_b,
+                                                int conv_k, int conv_pad_left, int conv_act, void* y, int64_t B1,
+                                                int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype, int flags,
+                                                void* workspace, int64_t workspace_bytes, void* stream) {
+    const char* who = "sfm_selective_scan_fwd_ws";
+    const sfm_status st = fwd_check(u, delta, A, Bm, Cm, delta_softplus, conv_w, conv_k, conv_pad_left, conv_act, y,
+                                    B1, B2, D, N, L, io_dtype, flags);
+    if (st != SFM_OK) return st;
+    const int eb = io_bytes(io_dtype);
+    sfm::BwdParams p{};
+    size_t need = 0;
+    if (!fwd_split_plan(p, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, flags, eb,
+                        &need))
+        return sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b,
+                                         conv_k, conv_pad_left, conv_act, y, B1, B2, D, N, L, io_dtype, flags,
+                                         stream);
+    if (!workspace || workspace_bytes < (int64_t)need)
+        return fail(SFM_ERR_SHAPE, "%s: workspace of %lld bytes needed (see sfm_selective_scan_fwd_ws_size)", who,
+                    (long long)need);
+    const int64_t B = B1 * B2, XL = (flags & SFM_FUSE_PAD) ? L - 2 : L;
+    const Range rw = rng("workspace", workspace, workspace_bytes);
+    const Range others[] = {rng("u", u, B * D * XL * eb), rng("delta", delta, B * D * L * eb),
+                            rng("Bm", Bm, B * N * L * eb), rng("Cm", Cm, B * N * L * eb), rng("A", A, D * N * 4),
+                            rng("y", y, B * D * L * eb)};
+    for (const Range& r : others)
+        if (overlap(rw, r)) return fail(SFM_ERR_ALIAS, "%s: workspace overlaps %s", who, r.name);
+    p.u = u;
+    p.delta = delta;
+    p.A = A;
+    p.Bm = Bm;
+    p.Cm = Cm;
+    p.Dskip = Dskip;
+    p.dbias = delta_bias;
+    p.conv_b = conv_w ? conv_b : nullptr;
+    p.y = y;
+    p.ws = static_cast<float*>(workspace);
+    return hip_status(sfm::launch_fwd_split(p, io_dtype, static_cast<hipStream_t>(stream)), who);
 }
 
 extern "C" sfm_status sfm_aux_pad_bwd_ex(const void* gpad, void* gx, int64_t B, int64_t D, int64_t T, int io_dtype,

@@ -52,6 +52,12 @@ struct BwdParams {
     // (seam_off: the segment's leading and trailing ones) added by a seam kernel.
     int seg, cps, kw;
     long long car_off, meanw_off, seam_off;
+    // forward through the split-row machinery (sfm_selective_scan_fwd_ws): the
+    // carry pass's forward half, then a pass that writes y [B, D, L] io (ends
+    // exchanged with swap_out); fwd = 1 drops the backward's outputs and regions
+    int fwd;
+    void* y;
+    int swap_out;
     int kc;
     int xs_off, ds_off, dys_off, bc_off, red_off, mean_off, braw_off, lds_bytes;
     int hin_off;          // chunked kernel: a chunk's entering state [ns][64] f32, staged with the chunk
@@ -61,6 +67,8 @@ struct BwdParams {
 // Backward planning; returns false when no plan fits.  ws_bytes: workspace size.
 bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes);
 hipError_t launch_bwd(const BwdParams& p, int io_dtype, hipStream_t stream);
+// The split-row forward (p.fwd = 1, planned with p.seg > 1): y only, no reduce.
+hipError_t launch_fwd_split(const BwdParams& p, int io_dtype, hipStream_t stream);
 
 // Gradient of the aux pad: channel-first rows [rows][T+2] -> [rows][T], or
 // channel-last (channels > 0) [B][T+2][channels] -> [B][T][channels] with rows = B.

@@ -248,3 +248,16 @@ def test_build_scratch_guard_parses_resource_remarks():
     assert b.scratch_users(ok) == []
     assert b.scratch_users(ok + bad) == ["k_bad (512 bytes/lane)", "k_dyn (dynamic stack)"]
     assert "bwd.hip" in b.SPILL_OK and "scan_bf16_n8.hip" not in b.SPILL_OK
+
+
+def test_fwd_ws_size():
+    """The workspace-taking forward: zero (the regular forward runs) where rows are not
+    split or are channel-last; on the long workload's shape the backward's split (63
+    segments of 64 positions for 16 samples x 5 tiles) with only the carries
+    [waves][2 Np + 2][64] f32 and the float64 token sums [waves][64]."""
+    assert sfm.sfm_selective_scan_fwd_ws_size(256, 1, 640, 8, 51, 4, "bf16", 3) == 0
+    up = lambda v: (v + 63) // 64 * 64
+    waves = 16 * 5 * 63
+    assert sfm.sfm_selective_scan_fwd_ws_size(16, 1, 320, 16, 4002, 4, "bf16", 3) == \
+        4 * (up(waves * 34 * 64) + up(waves * 64 * 2))
+    assert sfm.sfm_selective_scan_fwd_ws_size(16, 1, 320, 16, 4002, 4, "bf16", 3 | sfm.SFM_LAYOUT_BLD) == 0
