@@ -45,6 +45,7 @@ namespace {
 #define SFM_BWD_HIST 32
 #endif
 constexpr int kHist = SFM_BWD_HIST;  // states of history per chunk held in registers
+constexpr int kFwdQ = 16;            // chunk of the split-row forward (no history kept)
 constexpr int kRedStride = 68;  // floats per row of the transpose buffer (16-byte rows, no 16-lane bank clash)
 
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.0f / (1.0f + exp2_fast(-v * kLog2e)); }
@@ -253,15 +254,19 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
             }
             {
                 // raw B then C: element e < N*Q is B[n = e / Q][t0 + e % Q], the next N*Q are C
-                const int e = ln;
+                // (one 64-element transfer while 2 NS Q <= 64, as with the register history)
                 const int half = N * Q;
-                const int e2 = e < half ? e : e - half;
-                const int n = e2 / Q;
-                const int c = e2 - n * Q;
-                const IO* src = (e < 2 * half && c < cnt && (e < half || with_c))
-                                    ? (e < half ? bgl : cgl) + (size_t)n * L + t0 + c
-                                    : dummy;
-                dma_at<EB, 0>(src, rb);
+                static_for<(2 * NS * Q + kWave - 1) / kWave>([&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    const int e = k * kWave + ln;
+                    const int e2 = e < half ? e : e - half;
+                    const int n = e2 / Q;
+                    const int c = e2 - n * Q;
+                    const IO* src = (e < 2 * half && c < cnt && (e < half || with_c))
+                                        ? (e < half ? bgl : cgl) + (size_t)n * L + t0 + c
+                                        : dummy;
+                    dma_at<EB, (k % kPer) * kWave * 4>(src, rb + (k / kPer) * kPer * kWave);
+                });
             }
             if (ck >= (SPLIT ? 0 : 1)) {  // (a whole row starts from zero: no checkpoint 0)
                 const float* hsrc = ws + (size_t)ck * NS * kWave + ln;
@@ -275,12 +280,12 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
         // After the chunk in the current buffer has landed: widen B/C to float32
         // [c][n]; states n >= N and positions past the sample are zero.
         auto widen = [&](int cnt, bool with_c) __attribute__((always_inline)) {
-            if (lane < Q * NS) {
-                const int c = lane / NS;
-                const int n = lane - c * NS;
+            for (int e = lane; e < Q * NS; e += kWave) {
+                const int c = e / NS;
+                const int n = e - c * NS;
                 const bool in = n < N && c < cnt;
-                bs[lane] = in ? Io<IO>::of_bits(braw[n * Q + c]) : 0.0f;
-                cs[lane] = (in && with_c) ? Io<IO>::of_bits(braw[N * Q + n * Q + c]) : 0.0f;
+                bs[e] = in ? Io<IO>::of_bits(braw[n * Q + c]) : 0.0f;
+                cs[e] = (in && with_c) ? Io<IO>::of_bits(braw[N * Q + n * Q + c]) : 0.0f;
             }
         };
 
@@ -1227,9 +1232,9 @@ hipError_t launch_bt(const BwdParams& p, hipStream_t s) {
     else if (p.fwd) {  // split-row forward: token sums, the carry pass's forward half, the output pass
         const unsigned grid = (unsigned)(p.B1 * p.tiles * p.seg);
         if (p.pad_in) hipLaunchKernelGGL(bwd_tokens_kernel<IO>, dim3(grid), dim3(kWave), 0, s, p);
-        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 2>), dim3(grid), dim3(kWave),
+        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, kFwdQ, 2>), dim3(grid), dim3(kWave),
                            (size_t)p.lds_bytes, s, p);
-        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, Q, 3>), dim3(grid), dim3(kWave),
+        hipLaunchKernelGGL((bwd_kernel<IO, NS, KW, CONV, SP, SILU, kFwdQ, 3>), dim3(grid), dim3(kWave),
                            (size_t)p.lds_bytes, s, p);
     } else {
         const unsigned grid = (unsigned)(p.B1 * p.tiles * p.seg);
@@ -1279,7 +1284,7 @@ hipError_t launch_bio(const BwdParams& p, hipStream_t s) {
 bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     p.ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
     p.tiles = (p.D + kWave - 1) / kWave;
-    p.q = kHist / p.ns;
+    p.q = p.fwd ? kFwdQ : kHist / p.ns;
     p.nchk = (p.L + p.q - 1) / p.q;
     p.kc = p.N + 2 + (p.conv_w ? 1 + p.K : 0);  // rows dA (N), dD, dbias [, dconv_b, dconv_w (K)]
     auto up64 = [](long long v) { return (v + 63) & ~63LL; };  // 256-byte aligned regions
@@ -1343,22 +1348,25 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
     int off = 0;
     p.xs_off = off;
     off += up16(kWave * xw * 4);  // staged io elements take 4-byte slots
+    // (the split-row forward stages no dy or entering state and needs no
+    // transpose or dx window)
+    const bool bw = !p.fwd;
     p.ds_off = off;
     off += up16(kWave * q * 4);
     p.dys_off = off;
-    off += up16(kWave * q * 4);
-    p.braw_off = off;  // raw B/C of a chunk: one 64-element transfer
-    off += up16(kWave * 4);
+    off += bw ? up16(kWave * q * 4) : 0;
+    p.braw_off = off;  // raw B/C of a chunk: 64-element transfers
+    off += ((2 * p.ns * q + kWave - 1) / kWave) * kWave * 4;
     p.hin_off = off;
-    off += p.ns * kWave * 4;
+    off += bw ? p.ns * kWave * 4 : 0;
     p.stage_bytes = off;
     off *= 2;
     p.bc_off = off;
     off += up16(2 * q * p.ns * 4);
     p.red_off = off;
-    off += kWave * kRedStride * 4;
+    off += bw ? kWave * kRedStride * 4 : 0;
     p.mean_off = off;  // fp32 dx window
-    off += up16(kWave * xw * 4);
+    off += bw ? up16(kWave * xw * 4) : 0;
     p.lds_bytes = off;
     // Split rows along L when the rows and tiles alone give fewer waves than
     // the GPU has SIMDs (about eight waves per SIMD wanted): segments of at least
