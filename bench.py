@@ -319,7 +319,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the hot path shards by sample "
+        print(json.dumps({"error": "bench.py runs on one GPU only; the hot path shards by sample "
                                    "(no collectives), so N GPUs would run N independent copies of this "
                                    "bench -- run it with --gpus 1"}))
         sys.exit(2)

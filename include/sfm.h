@@ -47,7 +47,7 @@ typedef enum {
     SFM_ERR_NULL = 1,         /* a required pointer is NULL                        */
     SFM_ERR_SHAPE = 2,        /* a size is out of range or inconsistent            */
     SFM_ERR_DTYPE = 3,        /* io_dtype not one of sfm_dtype                     */
-    SFM_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement       */
+    SFM_ERR_UNSUPPORTED = 4,  /* valid request the library does not implement     */
     SFM_ERR_HIP = 5,          /* the HIP runtime reported an error at launch       */
     SFM_ERR_ALIAS = 6,        /* an output overlaps an input it must not overlap   */
     SFM_ERR_ALIGN = 7         /* an io base pointer is not 16-byte aligned         */
