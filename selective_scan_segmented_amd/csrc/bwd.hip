@@ -1378,6 +1378,12 @@ bool plan_bwd(BwdParams& p, int io_bytes, size_t* ws_bytes) {
         const char* fs = getenv("SFM_BWD_SEGMENTS");
         const bool forced = fs && atoi(fs) > 0;
         long long want = forced ? atoi(fs) : (waves < 1024 ? (8192 + waves - 1) / waves : 1);
+        if (p.fwd && !forced && waves < 1024) {
+            // the forward's segments are cheap: as many as the GPU holds at once, one
+            // round of resident waves (several rounds measured slower on the long rows)
+            const int per_cu = std::max(1, std::min(8, 160 * 1024 / std::max(1, p.lds_bytes)));
+            want = std::max(1LL, (long long)device_cus() * per_cu / waves);
+        }
         want = std::min<long long>(want, 64);
         if (want > 1) {
             const int floor_pos = forced ? kw : std::max(kw, 64);

@@ -20,7 +20,7 @@ int odd_word_stride(int elems, int elem_bytes) {
 
 
 // Compute units of the current device (256 when no device can be queried).
-static int device_cus() {
+int device_cus() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {

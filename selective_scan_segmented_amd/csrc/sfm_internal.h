@@ -54,6 +54,8 @@ struct ScanParams {
 // > 0 sets the delay per dispatch round in 10 ns ticks.
 // stages_hint (mode 1): 1 or 2 forces the LDS stages per wave, else automatic.
 bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint = -1, int stages_hint = 0);
+// Compute units of the current device (256 when no device can be queried).
+int device_cus();
 hipError_t launch_scan(const ScanParams& p, int io_dtype, hipStream_t stream);
 // per-(io type, state count) kernel sets, one translation unit each
 hipError_t launch_scan_f32_n4(const ScanParams& p, hipStream_t s);

@@ -252,12 +252,13 @@ def test_build_scratch_guard_parses_resource_remarks():
 
 def test_fwd_ws_size():
     """The workspace-taking forward: zero (the regular forward runs) where rows are not
-    split or are channel-last; on the long workload's shape the backward's split (63
-    segments of 64 positions for 16 samples x 5 tiles) with only the carries
-    [waves][2 Np + 2][64] f32 and the float64 token sums [waves][64]."""
+    split or are channel-last; on the long workload's shape one round of resident
+    waves (256 CUs x 6 workgroups of 24 KB LDS = 1536 for 16 samples x 5 tiles: 19
+    segments wanted, 251 chunks of 16 -> 14 chunks a segment, 18 segments) with only
+    the carries [waves][2 Np + 2][64] f32 and the float64 token sums [waves][64]."""
     assert sfm.sfm_selective_scan_fwd_ws_size(256, 1, 640, 8, 51, 4, "bf16", 3) == 0
     up = lambda v: (v + 63) // 64 * 64
-    waves = 16 * 5 * 63
+    waves = 16 * 5 * 18
     assert sfm.sfm_selective_scan_fwd_ws_size(16, 1, 320, 16, 4002, 4, "bf16", 3) == \
         4 * (up(waves * 34 * 64) + up(waves * 64 * 2))
     assert sfm.sfm_selective_scan_fwd_ws_size(16, 1, 320, 16, 4002, 4, "bf16", 3 | sfm.SFM_LAYOUT_BLD) == 0
