@@ -24,7 +24,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run(B, D, N, T, K, P, act, flags, io, seed, conv=True, samples=None):
+def run(B, D, N, T, K, P, act, flags, io, seed, conv=True, samples=None, B2=1):
     import torch
     w = synth.Workload("fws", B=B, D=D, N=N, T=T, io=io, B2_list=(1,), K=max(K, 1))
     li = synth.make_layer(w, seed=seed)
@@ -37,14 +37,14 @@ def run(B, D, N, T, K, P, act, flags, io, seed, conv=True, samples=None):
         xr = rng.standard_normal((B, D, L)).astype(np.float32)
         x = synth.f32_to_bf16_bits(xr) if io == "bf16" else xr
     cw = li.conv_w[:, :K] if conv else None
-    need = sfm.sfm_selective_scan_fwd_ws_size(B, 1, D, N, L, K if conv else 0, io, flags)
+    need = sfm.sfm_selective_scan_fwd_ws_size(B // B2, B2, D, N, L, K if conv else 0, io, flags)
     say(f"fwd_ws B={B} D={D} N={N} T={T} K={K} P={P} act={act} flags={flags} io={io} workspace={need}")
     assert need > 0, "the plan must split the rows"
     got = sfm.sfm_selective_scan_fwd_ws(to_dev(x), to_dev(li.delta), torch.from_numpy(li.A).cuda(),
                                         to_dev(li.Bm), to_dev(li.Cm), torch.from_numpy(li.Dskip).cuda(),
                                         torch.from_numpy(li.delta_bias).cuda(),
                                         conv_w=torch.from_numpy(np.ascontiguousarray(cw)).cuda() if conv else None,
-                                        conv_pad_left=P, conv_act="silu" if act else None, flags=flags)
+                                        conv_pad_left=P, conv_act="silu" if act else None, B2=B2, flags=flags)
     torch.cuda.synchronize()
     sel = slice(None) if samples is None else samples
     xo = f64(x)
@@ -73,6 +73,13 @@ def run(B, D, N, T, K, P, act, flags, io, seed, conv=True, samples=None):
 def test_fwd_ws_forced_segments_f32(B, D, N, T, K, P, act, flags, segs, conv, monkeypatch):
     monkeypatch.setenv("SFM_BWD_SEGMENTS", str(segs))
     run(B, D, N, T, K, P, act, flags, "f32", seed=B * 13 + T, conv=conv)
+
+
+def test_fwd_ws_folded_rows_f32(monkeypatch):
+    """Folded rows (B2 = 2): the split path runs every sample as its own row, as the
+    reset makes them independent."""
+    monkeypatch.setenv("SFM_BWD_SEGMENTS", "3")
+    run(4, 40, 8, 70, 4, 1, 0, 3, "f32", seed=23, B2=2)
 
 
 def test_fwd_ws_long_rows_bf16():
