@@ -10,10 +10,13 @@ enough independent input sets (>= 2 GiB) that no set is still in the 256 MB
 Infinity Cache when it comes round again.
 
 Prints ONE JSON line.  `value` is token*channels per second (token*channels =
-B * D * (T + 2), aux tokens included).  The `roofline` object is for the scan
-kernel, timed live with HIP events around each of its launches on the stream
-it runs on; the `hbm` object gives the same kernel's algorithmic bytes against
-the HBM peak; `cpu_baseline` times the CPU oracle on the same workload.
+B * D * (T + 2), aux tokens included) of the stage-4 step (L = 51).  The same
+line carries the stage-3 step (L = 198, `stage3`), a plain 1 GiB copy timed in
+the same process (the achievable HBM rate, `hbm.copy_GBps`) with each step's
+fraction of it, the folding speed-up t(B2 = 1) / t(B2) of both stages
+(`fold`), the `roofline` object of the scan kernel (timed live with HIP events
+on the stream it runs on) and `cpu_baseline`, the CPU oracle on one core and on
+all cores of the host.
 
     python bench.py [--steps K] [--warmup W] [--workload stage4] [--b2 B2]
     python bench.py --mode copy    # plain 1 GiB copy, used to calibrate HBM counters
@@ -35,9 +38,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-# fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 32 lanes/clock x 2.4 GHz
-VALU_PEAK_TSLOT = 256 * 4 * 32 * 2.4e9 / 1e12
-TRANS_SLOTS = 4  # v_exp_f32 / v_log_f32 issue at a quarter of the fp32 rate
+# Unpacked fp32 VALU rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes/clock x 2.4 GHz
+# = 39.3 T lane-operations/s (78.6 TFLOP/s counting an FMA as two; the published
+# 157.3 TFLOP/s vector figure counts packed FP32, which this build does not
+# emit).  Measured on the chip: a wave64 fp32 add/mul/fma occupies a SIMD for
+# about 4.2 cycles with four or more waves resident, v_exp_f32 about 8.3.
+VALU_PEAK_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12
+TRANS_SLOTS = 2  # v_exp_f32 / v_log_f32 occupy about twice the issue time of an fp32 fma
 
 
 class Hip:
@@ -79,13 +86,13 @@ class Hip:
         return float(out.value)
 
 
-def scan_source_hash() -> str:
-    """Hash of the code (comments and whitespace removed) of the files that
-    define the channel-first scan kernel: counters taken on one version of that
-    code stay valid across comment-only edits and no longer apply after any
-    other change."""
+def kernel_source_hash() -> str:
+    """Hash of the device code (comments and whitespace removed) of the forward
+    scan kernels: counters taken on one version of that code stay valid across
+    comment-only and host-only edits and no longer apply after any other change.
+    The launch plan string is compared separately."""
     h = hashlib.sha256()
-    for f in ("scan.hip", "scan_kernel.h", "sfm_device.h", "sfm_internal.h"):
+    for f in ("scan_kernel.h", "scan_split.h", "sfm_device.h"):
         with open(os.path.join(ROOT, "selective_scan_segmented_amd", "csrc", f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -94,17 +101,18 @@ def scan_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, b2: int):
+def read_traffic(workload: str, b2: int, plan: str):
     """HBM bytes per scan launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current scan source and the same launch."""
+    only if it was taken on the current kernel code and the same launch plan."""
     path = os.path.join(ROOT, "profiles", f"scan_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = {k: re.search(rf"^{k}:\s*(\S+)", text, re.M) for k in ("source_hash", "b2", "bytes_per_launch")}
+    m = {k: re.search(rf"^{k}:\s*(.+)$", text, re.M) for k in ("kernel_hash", "b2", "plan", "bytes_per_launch")}
     if not all(m.values()):
         return None
-    if m["source_hash"].group(1) != scan_source_hash() or int(m["b2"].group(1)) != b2:
+    if (m["kernel_hash"].group(1).strip() != kernel_source_hash() or int(m["b2"].group(1)) != b2
+            or m["plan"].group(1).strip() != plan):
         return None
     return float(m["bytes_per_launch"].group(1))
 
@@ -126,34 +134,58 @@ def alg_scan_slots(w) -> int:
     return w.B * w.D * w.L * per_tc
 
 
-def cpu_baseline(w, li, seconds: float):
-    import numpy as np
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": avail, "os_cpu_count": os.cpu_count()}
 
+
+def _oracle_rate(w, li, seconds: float, threads: int):
     import oracle
-    threads = oracle.threads(max(1, min(16, os.cpu_count() or 1)))
+    used = oracle.threads(threads)
     x = li.as_f64("x")
-    args = [li.as_f64(k) for k in ("delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "conv_w")]
-    # bounded sample: whole samples taken from the front of the batch, sized so
-    # one pass of the oracle chain takes on the order of a second or two
-    nb = max(1, min(w.B, int(round(w.B * 0.25))))
-    xs = x[:nb]
-    d, A, Bm, Cm, Dk, bias, cw = args
-    d, Bm, Cm = d[:nb], Bm[:nb], Cm[:nb]
+    d, A, Bm, Cm, Dk, bias, cw = [li.as_f64(k) for k in ("delta", "A", "Bm", "Cm", "Dskip", "delta_bias", "conv_w")]
+    # bounded sample: whole samples from the front of the batch, about a
+    # second or two of CPU work per pass of the oracle chain
+    nb = max(1, min(w.B, int(round(w.B * (0.25 if threads > 1 else 0.03125)))))
+    xs, d, Bm, Cm = x[:nb], d[:nb], Bm[:nb], Cm[:nb]
     t0 = time.perf_counter()
     passes = 0
     while True:
         xp = oracle.aux_pad(xs, w.io)
-        y = oracle.layer(xp, d, A, Bm, Cm, Dk, bias, cw, pad_left=1, nthreads=threads)
+        y = oracle.layer(xp, d, A, Bm, Cm, Dk, bias, cw, pad_left=1, nthreads=used)
         oracle.aux_swap(oracle.round_io(y, w.io))
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds or passes >= 1000:
             break
-    tcs = passes * nb * w.D * w.L / el
-    del np
-    return {"value": tcs, "unit": "token*channels/s", "cores": threads, "kind": "oracle",
+    return used, nb, passes, el, passes * nb * w.D * w.L / el
+
+
+def cpu_baseline(w, li, seconds: float):
+    """The oracle chain (pad -> conv -> scan -> swap, float64) on the host: on
+    all available cores (OpenMP over samples and channels) and on one core."""
+    info = host_info()
+    allc = max(1, info["nproc"] or 1)
+    used, nb, passes, el, rate = _oracle_rate(w, li, seconds, allc)
+    u1, nb1, p1, el1, rate1 = _oracle_rate(w, li, seconds, 1)
+    return {"value": rate, "unit": "token*channels/s", "cores": used, "kind": "oracle",
             "sample": f"{nb} of {w.B} samples (all {w.D} channels, L={w.L}) x {passes} passes of the fp64 oracle "
-                      f"chain pad->conv->scan->swap, {el:.1f} s wall on {threads} threads"}
+                      f"chain pad->conv->scan->swap, {el:.1f} s wall on {used} threads",
+            "one_core": {"value": rate1, "cores": u1,
+                         "sample": f"{nb1} of {w.B} samples x {p1} passes, {el1:.1f} s wall on 1 thread"},
+            "host": info}
 
 
 def alg_bwd_slots(w) -> int:
@@ -310,6 +342,8 @@ def main():
     ap.add_argument("--fwd-ws", action="store_true",
                     help="run the fused step through sfm_selective_scan_fwd_ws (rows split along L across the "
                          "GPU, with a device workspace, where the plan splits them)")
+    ap.add_argument("--full", action="store_true",
+                    help="add the stage-3 step, the copy rate and the fold sweeps to a non-default run")
     ap.add_argument("--layout", choices=["bdl", "bld"], default="bdl",
                     help="bdl: channel-first [B, D, L] (default); bld: channel-last [B, L, D] activations and "
                          "[B, L, N] B/C (fused step only)")
@@ -324,10 +358,8 @@ def main():
                                    "bench -- run it with --gpus 1"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import selective_scan_segmented_amd as sfm
     from selective_scan_segmented_amd import synth
 
     if not torch.cuda.is_available():
@@ -358,171 +390,267 @@ def main():
     if a.mode == "block":
         run_block(a, w, hip, sp, dev)
         return
-    io_bytes = 4 if w.io == "f32" else 2
-    B1 = sfm.sfm_pick_b1(w.B, w.L, w.D, w.N)
-    b2 = a.b2 if a.b2 > 0 else w.B // B1
-    if w.B % b2:
-        raise SystemExit(f"B2={b2} must divide B={w.B}")
-    li = synth.make_layer(w, seed=synth.WORKLOAD_ORDER.index(a.workload))
-
-    def dev_io(arr):
-        if arr.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
-
-    base = {"x": dev_io(li.x), "delta": dev_io(li.delta), "Bm": dev_io(li.Bm), "Cm": dev_io(li.Cm)}
-    cl = a.layout == "bld"
-    if cl:  # channel-last copies of the same values (outside the timed region)
-        base = {k: v.transpose(1, 2).contiguous() for k, v in base.items()}
-    prm = {k: torch.from_numpy(getattr(li, k)).to(dev) for k in ("A", "Dskip", "delta_bias", "conv_w")}
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + 2 * w.B * w.D * w.L * io_bytes
-    nsets = a.sets if a.sets > 0 else max(2, math.ceil((2 << 30) / set_bytes))
-    sets = []
-    for _ in range(nsets):
-        s = {k: v.clone() for k, v in base.items()}
-        s["xp"] = torch.empty((w.B, w.L, w.D) if cl else (w.B, w.D, w.L), dtype=base["x"].dtype, device=dev)
-        s["y"] = torch.empty_like(s["xp"])
-        sets.append(s)
-    torch.cuda.synchronize()
-
-    lib = sfm.load_library()
-    io = 0 if w.io == "f32" else 1
-    vp = lambda t: ctypes.c_void_p(t.data_ptr())
     if a.mode == "bwd":
-        run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io)
+        ctx = Workload(a, w, hip, sp, dev)
+        run_bwd(a, w, ctx.li, ctx.sets, ctx.prm, ctx.lib, ctx.io, ctx.io_bytes, ctx.b2(a.b2), hip, sp, dev,
+                ctx.dev_io)
         return
-    # fused (default): one launch does pad + conv + scan + swap from the unpadded x
-    fused = a.mode == "step" and not a.unfused
-    calls = []
-    for s in sets:
-        pad_args = (vp(s["x"]), vp(s["xp"]), w.B, w.D, w.T, 0, io, sp)
-        scan_in = s["x"] if fused else s["xp"]
-        scan_args = (vp(scan_in), vp(s["delta"]), vp(prm["A"]), vp(s["Bm"]), vp(s["Cm"]), vp(prm["Dskip"]),
-                     vp(prm["delta_bias"]), 1, vp(prm["conv_w"]), None, w.K, 1, 0, vp(s["y"]),
-                     w.B // b2, b2, w.D, w.N, w.L, io, (3 | (4 if cl else 0)) if fused else 0, sp)
-        swap_args = (vp(s["y"]), vp(s["y"]), w.B, w.D, w.L - 2, 1, io, sp)
-        calls.append((pad_args, scan_args, swap_args))
-    b1_out = ctypes.c_int64()
-    ws_t = None
-    if a.fwd_ws:
-        if not fused or cl:
-            raise SystemExit("--fwd-ws times the fused channel-first step")
-        need = sfm.sfm_selective_scan_fwd_ws_size(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, 3)
-        ws_t = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-
-    def step(i, ev=None):
-        pad_args, scan_args, swap_args = calls[i % nsets]
-        if a.mode == "step":
-            lib.sfm_pick_b1(w.B, w.L, w.D, w.N, ctypes.byref(b1_out))
-        if a.mode == "step" and not fused:
-            rc = lib.sfm_aux_pad_swap(*pad_args)
-            if rc:
-                raise RuntimeError(f"pad failed: {lib.sfm_last_error().decode()}")
-        if ev is not None:
-            hip.record(ev[0], sp)
-        if ws_t is not None:
-            rc = lib.sfm_selective_scan_fwd_ws(*scan_args[:-1], vp(ws_t), ws_t.numel(), sp)
-        else:
-            rc = lib.sfm_selective_scan_fwd_ex(*scan_args)
-        if ev is not None:
-            hip.record(ev[1], sp)
-        if rc:
-            raise RuntimeError(f"scan failed: {lib.sfm_last_error().decode()}")
-        if a.mode == "step" and not fused:
-            rc = lib.sfm_aux_pad_swap(*swap_args)
-            if rc:
-                raise RuntimeError(f"swap failed: {lib.sfm_last_error().decode()}")
-
-    if a.mode == "scan":  # inputs of the scan must exist
-        for s in sets:
-            sfm.sfm_aux_pad_swap(s["x"], out=s["xp"], mode="pad")
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    K = a.steps
-    # A step with one launch (the fused step, scan only) is timed by the two
-    # events around the K back-to-back launches, which also give the kernel's
-    # average duration (gaps between launches included); an event pair around
-    # every launch would add markers to the stream and stretch each step (by
-    # about 7 us at stage-4).  Steps with several launches (pad, scan, swap)
-    # bracket the scan launch with its own events.
-    single = fused or a.mode == "scan"
-    kev = None if single else [(hip.event(), hip.event()) for _ in range(K)]
-    t_start, t_end = hip.event(), hip.event()
-    torch.cuda.synchronize()
-    hip.record(t_start, sp)
-    h0 = time.perf_counter()
-    for i in range(K):
-        step(a.warmup + i, None if single else kev[i])
-    host_s = time.perf_counter() - h0
-    hip.record(t_end, sp)
-    torch.cuda.synchronize()
-    total_ms = hip.elapsed_ms(t_start, t_end)
-    if single:
-        scan_avg = scan_med = total_ms / K
-    else:
-        scan_ms = sorted(hip.elapsed_ms(e0, e1) for e0, e1 in kev)
-        scan_avg = sum(scan_ms) / K
-        scan_med = scan_ms[K // 2]
-
-    tc = w.B * w.D * w.L
-    ms_per_step = total_ms / K
-    value = tc / (ms_per_step * 1e-3)
-    sbytes = alg_scan_bytes(w, io_bytes, fused)
-    slots = alg_scan_slots(w)
-    hbm_gbps = sbytes / (scan_avg * 1e-3) / 1e9
-    alu = slots / (scan_avg * 1e-3) / 1e12
-    hbm_frac = hbm_gbps / HBM_PEAK_GBPS
-    alu_frac = alu / VALU_PEAK_TSLOT
-    traffic = read_traffic(a.workload, b2)
-    if alu_frac >= hbm_frac:
-        roof = {"bound": "alu", "achieved": round(alu, 3), "peak": round(VALU_PEAK_TSLOT, 3),
-                "unit": "T VALU-slot/s", "frac": round(alu_frac, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(hbm_frac, 4)}
-    roof["traffic"] = None if cl else traffic
-    roof["kernel"] = ("sfm scan_kernel (aux pad + boundary-masked conv + folded segmented scan + aux swap, "
-                      "one launch)" if fused else "sfm scan_kernel (conv + folded segmented scan)")
-    if cl:
-        roof["kernel"] = "sfm scan_cl_kernel (channel-last; aux pad + conv + folded segmented scan + aux swap)"
-    roof["plan"] = sfm.sfm_scan_plan_string(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io,
-                                            (3 | (4 if cl else 0)) if fused else 0)
-    roof["kernel_ms_avg"] = round(scan_avg, 5)
-    roof["kernel_ms_median"] = None if single else round(scan_med, 5)
-    roof["kernel_timing"] = ("HIP events around the K back-to-back launches (one launch per step)" if single else
-                             "HIP events around each scan launch")
-    roof["alg_bytes_per_launch"] = sbytes
-    roof["alg_valu_slots_per_launch"] = slots
+    ctx = Workload(a, w, hip, sp, dev)
+    b2 = ctx.b2(a.b2)
+    rec = ctx.time_step(b2, a.mode, a.steps, a.warmup, unfused=a.unfused, fwd_ws=a.fwd_ws)
+    headline_default = (a.mode == "step" and not a.unfused and not a.fwd_ws and a.layout == "bdl"
+                        and a.workload == "stage4" and a.b2 == 0)
     out = {
-        "metric": "folded selective-scan token*channels/s (T+2 aux tokens counted), % HBM peak",
-        "value": value,
+        "metric": "folded selective-scan token*channels/s (T+2 aux tokens counted), % HBM peak, at T+2 = 51 "
+                  "(value) and 198 (stage3)",
+        "value": rec["value"],
         "unit": "token*channels/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.io,
         "data": "synthetic (seeded SplitMix64 + Box-Muller, stage-shaped)",
-        "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}",
-                   "B2": b2, "B1": w.B // b2, "mode": a.mode, "input_sets": nsets,
-                   "layout": "channel-last [B, L, D]" if cl else "channel-first [B, D, L]",
-                   "step": ("pick_b1 + sfm_selective_scan_fwd_ws (token sums, carry pass, output pass where "
-                            "rows are split)" if ws_t is not None else
-                            "pick_b1 + one launch of pad/conv/scan/swap" if fused else
-                            "pick_b1 + pad + conv/scan + swap (3 launches)") if a.mode == "step" else "scan only"},
-        "roofline": roof,
-        "hbm": {"scan_alg_GBps": round(hbm_gbps, 1), "frac_of_8TBps": round(hbm_frac, 4)},
-        "token_channels_T_only_per_s": w.B * w.D * w.T / (ms_per_step * 1e-3),
-        "host_ms_per_step": host_s * 1e3 / K,
+        "config": rec["config"],
+        "roofline": rec["roofline"],
+        "hbm": rec["hbm"],
+        "token_channels_T_only_per_s": w.B * w.D * w.T / (rec["ms_per_step"] * 1e-3),
+        "host_ms_per_step": rec["host_ms_per_step"],
     }
+    if headline_default or a.full:
+        copy = copy_rate(hip, sp, dev)
+        out["hbm"]["copy_GBps"] = round(copy, 1)
+        out["hbm"]["frac_of_achievable"] = round(out["hbm"]["scan_alg_GBps"] / copy, 4)
+        # the other half of the metric: the stage-3 step (L = 198)
+        ctx3 = Workload(a, synth.WORKLOADS["stage3"], hip, sp, dev)
+        r3 = ctx3.time_step(ctx3.b2(0), "step", a.steps, a.warmup)
+        r3["hbm"]["copy_GBps"] = round(copy, 1)
+        r3["hbm"]["frac_of_achievable"] = round(r3["hbm"]["scan_alg_GBps"] / copy, 4)
+        out["stage3"] = {k: r3[k] for k in ("value", "ms_per_step", "config", "roofline", "hbm")}
+        # folding: t(B2 = 1) / t(B2) on the same inputs, fused step
+        ks = max(20, a.steps // 2)
+        out["fold"] = {"stage4": ctx.fold_sweep([1, 2, 4, 8, 16, 32], ks, a.warmup, b2, rec["ms_per_step"]),
+                       "stage3": ctx3.fold_sweep([1, 2, 4, 8], ks, a.warmup, ctx3.b2(0), r3["ms_per_step"]),
+                       "note": "t(B2=1)/t(B2) per fold ratio of the fused step, same inputs, same process; "
+                               "'chosen' is the adaptive-B1 table's pick"}
+        del ctx3
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, li, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, ctx.li, a.cpu_seconds)
     print(json.dumps(out))
+
+
+def copy_rate(hip, sp, dev, reps: int = 10) -> float:
+    """GB/s of a plain 1 GiB bf16 copy (1 GiB read + 1 GiB written): the achievable HBM rate."""
+    import torch
+    n = 1 << 29
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, sp)
+    for _ in range(reps):
+        dst.copy_(src)
+    hip.record(e1, sp)
+    ms = hip.elapsed_ms(e0, e1) / reps
+    del src, dst
+    return 4 * n / ms / 1e6
+
+
+class Workload:
+    """Seeded inputs of one workload on the GPU, rotated over enough input sets
+    (>= 2 GiB) that no set is still cached in the 256 MB Infinity Cache when it
+    comes round again, and the timing of the step on them."""
+
+    def __init__(self, a, w, hip, sp, dev):
+        import numpy as np
+        import torch
+        import selective_scan_segmented_amd as sfm
+        from selective_scan_segmented_amd import synth
+        self.a, self.w, self.hip, self.sp, self.dev = a, w, hip, sp, dev
+        self.sfm = sfm
+        self.io_bytes = 4 if w.io == "f32" else 2
+        self.io = 0 if w.io == "f32" else 1
+        self.li = synth.make_layer(w, seed=synth.WORKLOAD_ORDER.index(w.name))
+        self.cl = a.layout == "bld"
+
+        def dev_io(arr):
+            if arr.dtype == np.uint16:
+                return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+        self.dev_io = dev_io
+        li = self.li
+        base = {"x": dev_io(li.x), "delta": dev_io(li.delta), "Bm": dev_io(li.Bm), "Cm": dev_io(li.Cm)}
+        if self.cl:  # channel-last copies of the same values (outside the timed region)
+            base = {k: v.transpose(1, 2).contiguous() for k, v in base.items()}
+        self.prm = {k: torch.from_numpy(getattr(li, k)).to(dev) for k in ("A", "Dskip", "delta_bias", "conv_w")}
+        set_bytes = sum(t.numel() * t.element_size() for t in base.values()) + 2 * w.B * w.D * w.L * self.io_bytes
+        self.nsets = a.sets if a.sets > 0 else max(2, math.ceil((2 << 30) / set_bytes))
+        self.sets = []
+        for _ in range(self.nsets):
+            st = {k: v.clone() for k, v in base.items()}
+            st["xp"] = torch.empty((w.B, w.L, w.D) if self.cl else (w.B, w.D, w.L), dtype=base["x"].dtype,
+                                   device=dev)
+            st["y"] = torch.empty_like(st["xp"])
+            self.sets.append(st)
+        torch.cuda.synchronize()
+        self.lib = sfm.load_library()
+        self.padded = False
+
+    def b2(self, arg: int) -> int:
+        w = self.w
+        b2 = arg if arg > 0 else w.B // self.sfm.sfm_pick_b1(w.B, w.L, w.D, w.N)
+        if w.B % b2:
+            raise SystemExit(f"B2={b2} must divide B={w.B}")
+        return b2
+
+    def _calls(self, b2, fused):
+        w, io, sp, cl, prm = self.w, self.io, self.sp, self.cl, self.prm
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        calls = []
+        for st in self.sets:
+            pad_args = (vp(st["x"]), vp(st["xp"]), w.B, w.D, w.T, 0, io, sp)
+            scan_in = st["x"] if fused else st["xp"]
+            scan_args = (vp(scan_in), vp(st["delta"]), vp(prm["A"]), vp(st["Bm"]), vp(st["Cm"]), vp(prm["Dskip"]),
+                         vp(prm["delta_bias"]), 1, vp(prm["conv_w"]), None, w.K, 1, 0, vp(st["y"]),
+                         w.B // b2, b2, w.D, w.N, w.L, io, (3 | (4 if cl else 0)) if fused else 0, sp)
+            swap_args = (vp(st["y"]), vp(st["y"]), w.B, w.D, w.L - 2, 1, io, sp)
+            calls.append((pad_args, scan_args, swap_args))
+        return calls
+
+    def time_step(self, b2, mode, K, W, unfused=False, fwd_ws=False):
+        """Time K steps (after W warm-up steps); returns this workload's record."""
+        import torch
+        w, lib, hip, sp, cl = self.w, self.lib, self.hip, self.sp, self.cl
+        fused = mode == "step" and not unfused
+        calls = self._calls(b2, fused)
+        b1_out = ctypes.c_int64()
+        ws_t = None
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        if fwd_ws:
+            if not fused or cl:
+                raise SystemExit("--fwd-ws times the fused channel-first step")
+            need = self.sfm.sfm_selective_scan_fwd_ws_size(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, 3)
+            ws_t = torch.empty(max(need, 16), dtype=torch.uint8, device=self.dev)
+        nsets = len(calls)
+
+        def step(i, ev=None):
+            pad_args, scan_args, swap_args = calls[i % nsets]
+            if mode == "step":
+                lib.sfm_pick_b1(w.B, w.L, w.D, w.N, ctypes.byref(b1_out))
+            if mode == "step" and not fused:
+                rc = lib.sfm_aux_pad_swap(*pad_args)
+                if rc:
+                    raise RuntimeError(f"pad failed: {lib.sfm_last_error().decode()}")
+            if ev is not None:
+                hip.record(ev[0], sp)
+            if ws_t is not None:
+                rc = lib.sfm_selective_scan_fwd_ws(*scan_args[:-1], vp(ws_t), ws_t.numel(), sp)
+            else:
+                rc = lib.sfm_selective_scan_fwd_ex(*scan_args)
+            if ev is not None:
+                hip.record(ev[1], sp)
+            if rc:
+                raise RuntimeError(f"scan failed: {lib.sfm_last_error().decode()}")
+            if mode == "step" and not fused:
+                rc = lib.sfm_aux_pad_swap(*swap_args)
+                if rc:
+                    raise RuntimeError(f"swap failed: {lib.sfm_last_error().decode()}")
+
+        if mode == "scan" and not self.padded:  # inputs of the scan must exist
+            for st in self.sets:
+                self.sfm.sfm_aux_pad_swap(st["x"], out=st["xp"], mode="pad")
+            self.padded = True
+        for i in range(W):
+            step(i)
+        torch.cuda.synchronize()
+        # A step with one launch (the fused step, scan only) is timed by the two
+        # events around the K back-to-back launches, which also give the kernel's
+        # average duration (gaps between launches included); an event pair around
+        # every launch would add markers to the stream and stretch each step (by
+        # about 7 us at stage-4).  Steps with several launches (pad, scan, swap)
+        # bracket the scan launch with its own events.
+        single = fused or mode == "scan"
+        kev = None if single else [(hip.event(), hip.event()) for _ in range(K)]
+        t_start, t_end = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(t_start, sp)
+        h0 = time.perf_counter()
+        for i in range(K):
+            step(W + i, None if single else kev[i])
+        host_s = time.perf_counter() - h0
+        hip.record(t_end, sp)
+        torch.cuda.synchronize()
+        total_ms = hip.elapsed_ms(t_start, t_end)
+        if single:
+            scan_avg = scan_med = total_ms / K
+        else:
+            scan_ms = sorted(hip.elapsed_ms(e0, e1) for e0, e1 in kev)
+            scan_avg = sum(scan_ms) / K
+            scan_med = scan_ms[K // 2]
+        tc = w.B * w.D * w.L
+        ms_per_step = total_ms / K
+        sbytes = alg_scan_bytes(w, self.io_bytes, fused)
+        slots = alg_scan_slots(w)
+        hbm_gbps = sbytes / (scan_avg * 1e-3) / 1e9
+        alu = slots / (scan_avg * 1e-3) / 1e12
+        hbm_frac = hbm_gbps / HBM_PEAK_GBPS
+        alu_frac = alu / VALU_PEAK_TSLOT
+        flags = (3 | (4 if cl else 0)) if fused else 0
+        plan = self.sfm.sfm_scan_plan_string(w.B // b2, b2, w.D, w.N, w.L, w.K, w.io, flags)
+        traffic = None if cl or fwd_ws or not fused else read_traffic(w.name, b2, plan)
+        if alu_frac >= hbm_frac:
+            roof = {"bound": "alu", "achieved": round(alu, 3), "peak": round(VALU_PEAK_TSLOT, 3),
+                    "unit": "T VALU-lane-op/s", "frac": round(alu_frac, 4)}
+        else:
+            roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(hbm_frac, 4)}
+        roof["traffic"] = traffic
+        roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roof["kernel"] = ("sfm scan kernel (aux pad + boundary-masked conv + folded segmented scan + aux swap, "
+                          "one launch)" if fused else "sfm scan kernel (conv + folded segmented scan)")
+        if cl:
+            roof["kernel"] = "sfm scan_cl_kernel (channel-last; aux pad + conv + folded segmented scan + aux swap)"
+        roof["plan"] = plan
+        roof["kernel_ms_avg"] = round(scan_avg, 5)
+        roof["kernel_ms_median"] = None if single else round(scan_med, 5)
+        roof["kernel_timing"] = ("HIP events around the K back-to-back launches (one launch per step)" if single
+                                 else "HIP events around each scan launch")
+        roof["alg_bytes_per_launch"] = sbytes
+        roof["alg_valu_lane_ops_per_launch"] = slots
+        roof["valu_roof_ms"] = round(slots / (VALU_PEAK_TSLOT * 1e12) * 1e3, 5)
+        roof["hbm_roof_ms"] = round(sbytes / (HBM_PEAK_GBPS * 1e9) * 1e3, 5)
+        step_desc = ("pick_b1 + sfm_selective_scan_fwd_ws (token sums, carry pass, output pass where rows are "
+                     "split)" if ws_t is not None else "pick_b1 + one launch of pad/conv/scan/swap" if fused else
+                     "pick_b1 + pad + conv/scan + swap (3 launches)") if mode == "step" else "scan only"
+        return {
+            "value": tc / (ms_per_step * 1e-3),
+            "ms_per_step": ms_per_step,
+            "config": {"workload": f"{w.name}: B={w.B} D={w.D} N={w.N} T={w.T} L={w.L} K={w.K}",
+                       "B2": b2, "B1": w.B // b2, "mode": mode, "input_sets": nsets,
+                       "layout": "channel-last [B, L, D]" if cl else "channel-first [B, D, L]", "step": step_desc},
+            "roofline": roof,
+            "hbm": {"scan_alg_GBps": round(hbm_gbps, 1), "frac_of_8TBps": round(hbm_frac, 4)},
+            "host_ms_per_step": host_s * 1e3 / K,
+        }
+
+    def fold_sweep(self, b2s, K, W, chosen, chosen_ms):
+        """Fused-step time per fold ratio; speed-up over B2 = 1."""
+        rows = {}
+        for b2 in b2s:
+            if self.w.B % b2:
+                continue
+            ms = chosen_ms if b2 == chosen else self.time_step(b2, "step", K, W)["ms_per_step"]
+            rows[b2] = ms
+        base = rows[1]
+        best = min(rows, key=rows.get)
+        return {"ms": {str(k): round(v, 5) for k, v in rows.items()},
+                "speedup_vs_B2_1": {str(k): round(base / v, 4) for k, v in rows.items()},
+                "chosen_B2": chosen, "best_B2": best,
+                "chosen_over_best_time": round(rows[chosen] / rows[best], 4)}
 
 
 if __name__ == "__main__":

@@ -2,6 +2,9 @@
 
     python -m selective_scan_segmented_amd.build      # or build() from Python
 
+Every call compiles every source; SFM_BUILD_INCREMENTAL=1 reuses objects that
+are newer than their source and all headers (development only).
+
 Objects go to selective_scan_segmented_amd/_build/ (not committed); the shared
 library lands next to this file as libsfm.so.
 """
@@ -20,7 +23,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsfm.so")
 SOURCES = ["scan.hip", "scan_cl.hip", "conv.hip", "aux.hip", "bwd.hip", "sfm_api.cpp"] + [
-    f"scan_{io}_n{n}.hip" for io in ("f32", "bf16") for n in (4, 8, 16)]
+    f"scan_{io}_n{n}.hip" for io in ("f32", "bf16") for n in (4, 8, 16)] + [
+    f"split_{io}_n{n}.hip" for io in ("f32", "bf16") for n in (4, 8, 16)]
 ARCH = os.environ.get("SFM_OFFLOAD_ARCH", "gfx950")
 SPILL_OK = {"bwd.hip"}  # sources whose kernels may use scratch (register spills)
 
@@ -55,8 +59,21 @@ def scratch_users(remarks: str):
     return bad
 
 
+def _up_to_date(src: str, obj: str) -> bool:
+    """Object newer than its source and every header (SFM_BUILD_INCREMENTAL=1 only)."""
+    if os.environ.get("SFM_BUILD_INCREMENTAL") != "1" or not os.path.exists(obj):
+        return False
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                                        if f.endswith((".h", ".inc"))]
+    deps += [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    t = os.path.getmtime(obj)
+    return all(os.path.getmtime(d) < t for d in deps)
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
+    if _up_to_date(src, obj):
+        return obj
     cmd = [_hipcc(), *_flags(), "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]

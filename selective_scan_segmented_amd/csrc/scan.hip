@@ -16,6 +16,98 @@ int odd_word_stride(int elems, int elem_bytes) {
     return s;
 }
 
+// Lane-split plan (scan_split.h): whole sample rows staged by 16-byte
+// transfers, G lanes per channel.  Returns false when the shape does not fit
+// (alignment, LDS), leaving the classic kernel to plan it.  G is the smallest
+// group that gives every SIMD of the device about four waves (a lone wave
+// issues a VALU instruction at most every five to six cycles, a SIMD with
+// four or more every four), else the largest; split_hint > 0 forces G.
+bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, int cus) {
+    const int L = p.L, XL = p.xrow, N = p.N, D = p.D;
+    const int ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
+    const long long dl = (long long)D * L * io_bytes, dx = (long long)D * XL * io_bytes;
+    if (dl % 16 || dx % 16 || ((long long)N * L * io_bytes) % 16 || L > 1024) return false;
+    int cands[2] = {2, 4};
+    int nc = ns == 4 ? 1 : 2;
+    if (split_hint > 0) {
+        if (split_hint != 2 && split_hint != 4) return false;
+        if (ns == 4 && split_hint != 2) return false;
+        cands[0] = split_hint;
+        nc = 1;
+    }
+    constexpr int kLdsCap = 160 * 1024;
+    constexpr int kLdsUnit = 1280;
+    int best_g = 0;
+    for (int ci = 0; ci < nc; ++ci) {
+        const int G = cands[ci];
+        const int cpw = kWave / G;
+        if (((long long)cpw * L * io_bytes) % 16 || ((long long)cpw * XL * io_bytes) % 16) continue;
+        best_g = G;
+        const long long waves = (long long)p.B1 * ((D + cpw - 1) / cpw);
+        if (waves >= 4LL * 4 * cus) break;  // about four waves per SIMD
+    }
+    if (!best_g) return false;
+    const int G = best_g, cpw = kWave / G;
+    const int tiles = (D + cpw - 1) / cpw;
+    const int bc = L * 2 * ns * (int)sizeof(float);
+    const int braw = (2 * N * L * io_bytes + 15) & ~15;
+    const int mean_bytes = 4 * 64 * (int)sizeof(float);  // row means of up to 256 channels (wpg <= 4)
+    const int xsb = (cpw * XL * io_bytes + 15) & ~15;
+    const int dsb = (cpw * L * io_bytes + 15) & ~15;
+    // waves per workgroup: four (one per SIMD) when two such groups fit in LDS
+    int wpg = 0;
+    for (int w = 4; w >= 1; w /= 2) {
+        if (w > tiles) continue;
+        const int tot = bc + braw + mean_bytes + w * (xsb + dsb);
+        if (2 * ((tot + kLdsUnit - 1) / kLdsUnit * kLdsUnit) <= kLdsCap) {
+            wpg = w;
+            break;
+        }
+    }
+    if (!wpg) return false;
+    // resident waves per CU that LDS allows (the kernels hold up to five per
+    // SIMD by registers): fewer than two per SIMD leaves the classic kernel ahead
+    const int per_wg = (bc + braw + mean_bytes + wpg * (xsb + dsb) + kLdsUnit - 1) / kLdsUnit * kLdsUnit;
+    if (split_hint <= 0 && kLdsCap / per_wg * wpg < 8) return false;
+    p.split = G;
+    p.wpg = wpg;
+    p.stiles = (tiles + wpg - 1) / wpg;
+    p.ns = ns;
+    p.bc_off = 0;
+    p.braw_off = bc;
+    p.mean_off = bc + braw;
+    p.slab_off = bc + braw + mean_bytes;
+    p.xs_bytes = xsb;
+    p.ds_bytes = dsb;
+    p.slab_bytes = xsb + dsb;
+    p.lds_bytes = bc + braw + mean_bytes + wpg * (xsb + dsb);
+    p.tiles = tiles;
+    p.mode = 0;
+    p.ch = L;
+    p.waves = 1;
+    p.piece = p.B2 * L;
+    p.need_carry = 0;
+    p.cw = wpg;
+    p.tgroups = p.stiles;
+    // Staggered start when the whole grid is resident at once: dispatch round
+    // r (one workgroup per CU) delays its loads by r times the time HBM needs
+    // for one round's inputs at about 6.5 TB/s (65000 bytes per 10 ns tick).
+    p.stagger_period = 0;
+    p.stagger_ticks = 0;
+    const long long grid = (long long)p.stiles * p.B1;
+    const int wg_per_cu = kLdsCap / per_wg;
+    if (stagger_hint != 0 && grid > cus && grid <= (long long)cus * (wg_per_cu < 5 ? wg_per_cu : 5)) {
+        const long long wg_bytes = (long long)wpg * cpw * (XL + L) * io_bytes + 2LL * N * L * io_bytes;
+        long long ticks = stagger_hint > 0 ? stagger_hint : (long long)cus * wg_bytes / 65000;
+        if (ticks > 500) ticks = 500;
+        if (ticks > 0) {
+            p.stagger_period = cus;
+            p.stagger_ticks = (int)ticks;
+        }
+    }
+    return true;
+}
+
 }  // namespace
 
 
@@ -30,9 +122,21 @@ int device_cus() {
     return cus;
 }
 
-bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint, int stages_hint) {
+bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint, int stages_hint,
+               int split_hint) {
     const int L = p.L, S = p.B2 * p.L;
     if (p.xrow <= 0) p.xrow = p.pad_in ? L - 2 : L;
+    p.split = 0;
+    // The lane-split kernel when asked for, or when one wave per (sample,
+    // 64-channel tile) would give the SIMDs fewer than two waves each (measured
+    // on MI355X: stage-3 shapes 80.7 vs 102.6 us; at stage-4, 2.5 waves per
+    // SIMD, the one-lane kernel keeps the edge, 31.2 vs 32.4 us, by issuing
+    // fewer VALU instructions per token).
+    const int cus = device_cus();
+    const long long lane_waves = (long long)p.B1 * p.B2 * ((p.D + kWave - 1) / kWave);
+    const bool want_split = split_hint > 0 || (split_hint < 0 && lane_waves < 2LL * 4 * cus);
+    if (want_split && waves_hint <= 0 && ch_hint <= 0 && plan_split(p, io_bytes, split_hint, stagger_hint, cus))
+        return true;
     const int XL = p.xrow;
     // The fused pad/swap keep each sample inside one wave, except with tile
     // staging (even row lengths), whose pieces take the row mean and write the
@@ -131,7 +235,6 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
         return per_wg * grp + agg;
     };
     const int vgpr_waves_per_cu = p.ns <= 8 ? 12 : 8;
-    const int cus = device_cus();
     int grp = 0;
     if (mode == 1 && ch_hint <= 0) {
         // Chunk length: every chunk costs a fixed set-up (waits, conv window,
@@ -244,6 +347,16 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
 }
 
 hipError_t launch_scan(const ScanParams& p, int io_dtype, hipStream_t stream) {
+    if (p.split) {
+        if (io_dtype == 0) {
+            if (p.ns == 4) return launch_split_f32_n4(p, stream);
+            if (p.ns == 8) return launch_split_f32_n8(p, stream);
+            return launch_split_f32_n16(p, stream);
+        }
+        if (p.ns == 4) return launch_split_bf16_n4(p, stream);
+        if (p.ns == 8) return launch_split_bf16_n8(p, stream);
+        return launch_split_bf16_n16(p, stream);
+    }
     if (io_dtype == 0) {
         if (p.ns == 4) return launch_scan_f32_n4(p, stream);
         if (p.ns == 8) return launch_scan_f32_n8(p, stream);

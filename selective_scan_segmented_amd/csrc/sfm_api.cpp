@@ -141,6 +141,13 @@ static sfm_status fwd_check(const void* u, const void* delta, const float* A, co
     return SFM_OK;
 }
 
+// SFM_SCAN_SPLIT (diagnostics): 0 keeps the one-lane-per-channel kernel, 2 or
+// 4 asks for that many lanes per channel, unset lets the planner choose.
+static int split_hint_env() {
+    if (const char* e = std::getenv("SFM_SCAN_SPLIT")) return std::atoi(e);
+    return -1;
+}
+
 sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* Bm,
                                      const void* Cm, const float* Dskip, const float* delta_bias,
                                      int delta_softplus, const float* conv_w, const float* conv_b, int conv_k,
@@ -214,7 +221,7 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
     int stagger_hint = -1, stages_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_STAGGER")) stagger_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_STAGES")) stages_hint = std::atoi(e);
-    if (!sfm::plan_scan(p, eb, waves_hint, ch_hint, stagger_hint, stages_hint))
+    if (!sfm::plan_scan(p, eb, waves_hint, ch_hint, stagger_hint, stages_hint, split_hint_env()))
         return fail(SFM_ERR_UNSUPPORTED, "sfm_selective_scan_fwd: no launch plan fits LDS for this shape");
     return hip_status(sfm::launch_scan(p, io_dtype, static_cast<hipStream_t>(stream)), "sfm_selective_scan_fwd");
 }
@@ -269,8 +276,13 @@ sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, in
     int stagger_hint = -1, stages_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_STAGGER")) stagger_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_STAGES")) stages_hint = std::atoi(e);
-    if (!sfm::plan_scan(p, io_bytes(io_dtype), waves_hint, ch_hint, stagger_hint, stages_hint))
+    if (!sfm::plan_scan(p, io_bytes(io_dtype), waves_hint, ch_hint, stagger_hint, stages_hint, split_hint_env()))
         return fail(SFM_ERR_UNSUPPORTED, "sfm_scan_plan_string: no launch plan fits LDS");
+    if (p.split) {
+        snprintf(buf, (size_t)cap, "split=%d ns=%d wpg=%d lds=%d grid=%lld block=%d stagger=%d/%d", p.split, p.ns,
+                 p.wpg, p.lds_bytes, (long long)p.stiles * p.B1, 64 * p.wpg, p.stagger_ticks, p.stagger_period);
+        return ok();
+    }
     snprintf(buf, (size_t)cap,
              "mode=%d ch=%d pieces=%d piece=%d carry=%d cw=%d ns=%d lds=%d grid=%lld block=%d stagger=%d/%d "
              "stages=%d",
@@ -583,9 +595,13 @@ extern "C" sfm_status sfm_selective_scan_fwd_ws(const void* u, const void* delta
                     (long long)need);
     const int64_t B = B1 * B2, XL = (flags & SFM_FUSE_PAD) ? L - 2 : L;
     const Range rw = rng("workspace", workspace, workspace_bytes);
+    // the kernels read every input after the workspace has been written
     const Range others[] = {rng("u", u, B * D * XL * eb), rng("delta", delta, B * D * L * eb),
                             rng("Bm", Bm, B * N * L * eb), rng("Cm", Cm, B * N * L * eb), rng("A", A, D * N * 4),
-                            rng("y", y, B * D * L * eb)};
+                            rng("y", y, B * D * L * eb), rng("Dskip", Dskip, Dskip ? D * 4 : 0),
+                            rng("delta_bias", delta_bias, delta_bias ? D * 4 : 0),
+                            rng("conv_w", conv_w, conv_w ? D * conv_k * 4 : 0),
+                            rng("conv_b", conv_b, conv_w && conv_b ? D * 4 : 0)};
     for (const Range& r : others)
         if (overlap(rw, r)) return fail(SFM_ERR_ALIAS, "%s: workspace overlaps %s", who, r.name);
     p.u = u;

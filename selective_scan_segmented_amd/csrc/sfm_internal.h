@@ -47,13 +47,20 @@ struct ScanParams {
     // workgroups of dispatch round r = blockIdx / stagger_period issue their
     // loads r * stagger_ticks (10 ns ticks) after they start.
     int stagger_period, stagger_ticks;
+    // Lane-split kernel (scan_split.h): split = G lanes per channel (0 = the
+    // kernel above), wpg waves of 64/G channels per workgroup sharing one B/C
+    // stage, stiles workgroups per folded row; LDS offsets of the float32
+    // B/C rows, the raw B/C area and the first wave's x/delta slabs.
+    int split, wpg, stiles;
+    int bc_off, braw_off, mean_off, slab_off, slab_bytes;
 };
 
 // Fills the plan fields; waves_hint / ch_hint <= 0 select automatically,
 // stagger_hint < 0 selects automatically, 0 turns the staggered start off and
 // > 0 sets the delay per dispatch round in 10 ns ticks.
 // stages_hint (mode 1): 1 or 2 forces the LDS stages per wave, else automatic.
-bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint = -1, int stages_hint = 0);
+bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint = -1, int stages_hint = 0,
+               int split_hint = -1);
 // Compute units of the current device (256 when no device can be queried).
 int device_cus();
 hipError_t launch_scan(const ScanParams& p, int io_dtype, hipStream_t stream);
@@ -64,6 +71,13 @@ hipError_t launch_scan_f32_n16(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan_bf16_n4(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan_bf16_n8(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan_bf16_n16(const ScanParams& p, hipStream_t s);
+// lane-split kernel sets (p.split = G), one translation unit each
+hipError_t launch_split_f32_n4(const ScanParams& p, hipStream_t s);
+hipError_t launch_split_f32_n8(const ScanParams& p, hipStream_t s);
+hipError_t launch_split_f32_n16(const ScanParams& p, hipStream_t s);
+hipError_t launch_split_bf16_n4(const ScanParams& p, hipStream_t s);
+hipError_t launch_split_bf16_n8(const ScanParams& p, hipStream_t s);
+hipError_t launch_split_bf16_n16(const ScanParams& p, hipStream_t s);
 
 hipError_t launch_dwconv1d(const void* x, const float* w, const float* bias, void* out, int64_t B1, int64_t B2,
                            int64_t D, int64_t L, int K, int pad_left, int act, int io_dtype, hipStream_t stream);

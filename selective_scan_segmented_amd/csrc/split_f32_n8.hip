@@ -1,0 +1,3 @@
+// Lane-split selective-scan kernels for f32 io and 8 compiled states.
+#include "scan_split.h"
+SFM_SPLIT_INSTANCE(float, f32, 8, 2, 4)

@@ -2,9 +2,11 @@
 
 The pages pick channel-first or channel-last per model, whichever runs faster;
 the layout is a permutation of the same values, so every case here checks the
-channel-last launch (a) bit for bit against the channel-first launch on the
-transposed tensors and (b) against the float64 oracle (computed channel-first
-and transposed) with the forward's tolerance.
+channel-last launch (a) bit for bit against the one-lane-per-channel
+channel-first kernel (SFM_SCAN_SPLIT=0; its per-position arithmetic is the one
+the channel-last kernel runs, while the lane-split kernel sums C.h in another
+order) on the transposed tensors and (b) against the float64 oracle (computed
+channel-first and transposed) with the forward's tolerance.
 """
 import os
 import sys
@@ -42,15 +44,17 @@ def run(x, delta, A, Bm, Cm, Dk, db, cw, P, act, softplus, B2, flags, io, oracle
     T_ = lambda a: torch.from_numpy(a).cuda() if a is not None else None
     xd, dd, Bd, Cd = map(to_dev, (x, delta, Bm, Cm))
     kw = dict(delta_softplus=softplus, conv_w=T_(cw), conv_pad_left=P, conv_act="silu" if act else None, B2=B2)
-    saved = os.environ.pop("SFM_SCAN_WAVES", None)
+    saved = {k: os.environ.pop(k, None) for k in ("SFM_SCAN_WAVES", "SFM_SCAN_SPLIT")}
     try:
+        os.environ["SFM_SCAN_SPLIT"] = "0"
         if cf_whole_samples:
             os.environ["SFM_SCAN_WAVES"] = "1"
         ref = sfm.sfm_selective_scan_fwd_ex(xd, dd, T_(A), Bd, Cd, T_(Dk), T_(db), flags=flags, **kw)
     finally:
-        os.environ.pop("SFM_SCAN_WAVES", None)
-        if saved is not None:
-            os.environ["SFM_SCAN_WAVES"] = saved
+        for k, v in saved.items():
+            os.environ.pop(k, None)
+            if v is not None:
+                os.environ[k] = v
     got = sfm.sfm_selective_scan_fwd_ex(tr(xd), tr(dd), T_(A), tr(Bd), tr(Cd), T_(Dk), T_(db), flags=flags | CL,
                                         **kw)
     torch.cuda.synchronize()
