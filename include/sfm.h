@@ -179,6 +179,31 @@ sfm_status sfm_selective_scan_fwd_ws_size(int64_t B1, int64_t B2, int64_t D, int
                                           int conv_k, int io_dtype, int flags, int64_t* bytes);
 
 /*
+ * sfm_selective_scan_fwd_noalloc -- sfm_selective_scan_fwd_ws (same arguments
+ * without the workspace, same kernels, bit-identical results) for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Where the split-row plan needs a
+ * workspace, the call uses a static device array of SFM_NOALLOC_SCRATCH_BYTES
+ * instead (one copy per GPU, held until the process ends); it calls no
+ * allocator.  Rows that need more (sfm_selective_scan_fwd_ws_size above the
+ * limit; the 16 x 320 x 4002-position long workload needs 12.7 MiB) return
+ * SFM_ERR_UNSUPPORTED with nothing launched.  Every call on one GPU shares that
+ * GPU's array: calls that may overlap in time on one GPU (different streams)
+ * race and must be serialised by the caller; nothing in it needs clearing
+ * between calls (each call writes what it reads).  The first call on a device
+ * resolves the array's device address (the runtime may load the library's
+ * code object then): make one call before capturing a graph.
+ * Returns as sfm_selective_scan_fwd_ws.
+ */
+#define SFM_NOALLOC_SCRATCH_BYTES (32LL << 20)
+sfm_status sfm_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* Bm,
+                                          const void* Cm, const float* Dskip, const float* delta_bias,
+                                          int delta_softplus, const float* conv_w, const float* conv_b,
+                                          int conv_k, int conv_pad_left, int conv_act, void* y, int64_t B1,
+                                          int64_t B2, int64_t D, int64_t N, int64_t L, int io_dtype, int flags,
+                                          void* stream);
+
+/*
  * sfm_dwconv1d_fold -- boundary-masked depthwise conv1d over folded rows
  * ([TL] "第二个模块", conv-boundary part; [SBW] 8.1 item 5):
  *   out[b,d,t] = act(bias[d] + sum_{j<K} w[d,j] * x[b,d,t+j-pad_left]),

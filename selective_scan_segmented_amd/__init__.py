@@ -54,6 +54,8 @@ def load_library():
                                               i64, i64, i64, i64, i64, ci, ci, vp]
     lib.sfm_selective_scan_fwd_ws.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
                                               i64, i64, i64, i64, i64, ci, ci, vp, i64, vp]
+    lib.sfm_selective_scan_fwd_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, fp, ci, fp, fp, ci, ci, ci, vp,
+                                                   i64, i64, i64, i64, i64, ci, ci, vp]
     lib.sfm_selective_scan_fwd_ws_size.argtypes = [i64, i64, i64, i64, i64, ci, ci, ci,
                                                    ctypes.POINTER(ctypes.c_int64)]
     lib.sfm_dwconv1d_fold.argtypes = [vp, fp, fp, vp, i64, i64, i64, i64, ci, ci, ci, ci, vp]
@@ -130,6 +132,7 @@ def _stream(stream):
 
 
 SFM_FUSE_PAD, SFM_FUSE_SWAP, SFM_LAYOUT_BLD = 1, 2, 4
+SFM_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of sfm_selective_scan_fwd_noalloc (include/sfm.h)
 
 
 def sfm_selective_scan_fwd(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, delta_softplus=True,
@@ -158,8 +161,9 @@ def sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, 
 
 def _fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b, conv_pad_left, conv_act, y,
             B2, flags, stream, workspace):
-    """Argument marshalling of the two fused forward entry points (workspace False:
-    sfm_selective_scan_fwd_ex; else sfm_selective_scan_fwd_ws)."""
+    """Argument marshalling of the fused forward entry points (workspace False:
+    sfm_selective_scan_fwd_ex; "noalloc": sfm_selective_scan_fwd_noalloc; else
+    sfm_selective_scan_fwd_ws)."""
     torch = _torch()
     io = _io_code(u)
     cl = bool(flags & SFM_LAYOUT_BLD)
@@ -194,6 +198,8 @@ def _fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv
             B // B2, B2, D, N, L, io, int(flags))
     if workspace is False:
         rc = load_library().sfm_selective_scan_fwd_ex(*args, _stream(stream))
+    elif isinstance(workspace, str) and workspace == "noalloc":
+        rc = load_library().sfm_selective_scan_fwd_noalloc(*args, _stream(stream))
     else:
         need = sfm_selective_scan_fwd_ws_size(B // B2, B2, D, N, L, K, "bf16" if io == SFM_BF16 else "f32",
                                               int(flags))
@@ -215,6 +221,16 @@ def sfm_selective_scan_fwd_ws(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, 
     for the in-LDS carries are split along L across the whole GPU."""
     return _fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b, conv_pad_left,
                    conv_act, y, B2, flags, stream, workspace)
+
+
+def sfm_selective_scan_fwd_noalloc(u, delta, A, Bm, Cm, Dskip=None, delta_bias=None, delta_softplus=True,
+                                   conv_w=None, conv_b=None, conv_pad_left=1, conv_act=None, y=None, B2=1,
+                                   flags=0, stream=None):
+    """sfm_selective_scan_fwd_ws without a workspace argument: the library's static
+    per-GPU scratch array stands in for it (see include/sfm.h for its limit).  ``y``
+    must be passed by callers that cannot allocate (else it is allocated here)."""
+    return _fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b, conv_pad_left,
+                   conv_act, y, B2, flags, stream, "noalloc")
 
 
 def sfm_selective_scan_fwd_ws_size(B1: int, B2: int, D: int, N: int, L: int, conv_k: int = 4,

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -614,6 +615,82 @@ extern "C" sfm_status sfm_selective_scan_fwd_ws(const void* u, const void* delta
     p.conv_b = conv_w ? conv_b : nullptr;
     p.y = y;
     p.ws = static_cast<float*>(workspace);
+    return hip_status(sfm::launch_fwd_split(p, io_dtype, static_cast<hipStream_t>(stream)), who);
+}
+
+// ------------------------------------------------------------ no allocation
+// Scratch of sfm_selective_scan_fwd_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address comes from hipGetSymbolAddress, resolved once per device (with that
+// device current) and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[SFM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+sfm_status scratch_of_current_device(const char* who, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SFM_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(SFM_ERR_UNSUPPORTED, "%s: device %d out of range", who, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(SFM_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+        }
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return SFM_OK;
+}
+}  // namespace
+
+extern "C" sfm_status sfm_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* Bm,
+                                                     const void* Cm, const float* Dskip, const float* delta_bias,
+                                                     int delta_softplus, const float* conv_w, const float* conv_b,
+                                                     int conv_k, int conv_pad_left, int conv_act, void* y,
+                                                     int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
+                                                     int io_dtype, int flags, void* stream) {
+    const char* who = "sfm_selective_scan_fwd_noalloc";
+    const sfm_status st = fwd_check(u, delta, A, Bm, Cm, delta_softplus, conv_w, conv_k, conv_pad_left, conv_act, y,
+                                    B1, B2, D, N, L, io_dtype, flags);
+    if (st != SFM_OK) return st;
+    sfm::BwdParams p{};
+    size_t need = 0;
+    if (!fwd_split_plan(p, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, flags,
+                        io_bytes(io_dtype), &need))
+        // rows the plan does not split: the regular forward, which uses no scratch
+        return sfm_selective_scan_fwd_ex(u, delta, A, Bm, Cm, Dskip, delta_bias, delta_softplus, conv_w, conv_b,
+                                         conv_k, conv_pad_left, conv_act, y, B1, B2, D, N, L, io_dtype, flags,
+                                         stream);
+    if ((long long)need > SFM_NOALLOC_SCRATCH_BYTES)
+        return fail(SFM_ERR_UNSUPPORTED, "%s: these rows need %lld bytes of scratch, the static array holds %lld",
+                    who, (long long)need, (long long)SFM_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const sfm_status sst = scratch_of_current_device(who, &ws);
+    if (sst != SFM_OK) return sst;
+    p.u = u;
+    p.delta = delta;
+    p.A = A;
+    p.Bm = Bm;
+    p.Cm = Cm;
+    p.Dskip = Dskip;
+    p.dbias = delta_bias;
+    p.conv_b = conv_w ? conv_b : nullptr;
+    p.y = y;
+    // every word of the scratch the kernels read is written earlier in the same
+    // call (token sums, then carries), so nothing needs clearing between calls
+    p.ws = static_cast<float*>(ws);
     return hip_status(sfm::launch_fwd_split(p, io_dtype, static_cast<hipStream_t>(stream)), who);
 }
 
