@@ -4,9 +4,13 @@
  * (gfx950).
  *
  * Plain C: extern "C", only pointers, integers and enums; no C++ exception and
- * no torch type crosses it.  Device pointers point to memory the CALLER owns
- * (the library never allocates, frees or keeps a reference to device memory,
- * and needs no workspace).  Every entry point that touches the GPU only
+ * no torch type crosses it.  Device pointers point to memory the CALLER owns:
+ * the library never allocates, frees or keeps a reference to device memory.
+ * The backward and the split-row forward (sfm_selective_scan_bwd,
+ * sfm_selective_scan_fwd_ws) take a caller-owned workspace;
+ * sfm_selective_scan_fwd_noalloc uses the library's static per-GPU scratch
+ * array instead; every other entry point needs no device memory beyond its
+ * inputs and outputs.  Every entry point that touches the GPU only
  * enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
  * returns without synchronising: device faults surface at the caller's next
  * synchronisation.  Arguments are validated BEFORE any launch; a violation

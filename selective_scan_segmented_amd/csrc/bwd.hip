@@ -21,12 +21,16 @@
 //    the state entering every chunk (fp32) to a caller-provided workspace;
 //  * sweep 2 visits the chunks in reverse: it re-runs the chunk forward from
 //    its checkpoint keeping the Q states in registers, then steps backwards.
-// Inputs of a chunk are staged through LDS with coalesced loads.  dB and dC
-// (sums over channels) go through an LDS transpose: each lane writes its terms
-// for R positions, then each lane sums one (position, state) row of 64 and adds
-// it to the output with a float32 atomic (one per channel tile).  Per-channel
-// sums (dA, dD, dbias, dconv) stay in registers over the wave's samples and are
-// added with atomics at the end.  All float32 outputs are zeroed first.
+// Inputs are staged through LDS by direct global->LDS transfers (whole sample
+// blocks in bwd_whole_kernel, chunk by chunk in bwd_kernel).  dB and dC (sums
+// over channels) are summed over the 64 lanes in registers (lane swaps and a
+// DPP butterfly; an LDS transpose in the chunked kernel) and stored as this
+// tile's partials; per-channel sums (dA, dD, dbias, dconv) are stored per
+// folded row.  bwd_reduce_kernel then adds the partials in a fixed order
+// (tiles ascending, folded rows in interleaved strands combined in order), so
+// every float32 output is bit-repeatable; nothing uses atomics.  Rows too long
+// for enough waves are split along L into segments (a token-sum launch, a carry
+// pass, the main pass and a seam launch), see plan_bwd.
 #include <stdlib.h>
 
 #include <algorithm>

@@ -2,6 +2,8 @@
 // (kernel: scan_kernel.h; instantiations: scan_<io>_n<N>.hip).
 #include "scan_kernel.h"
 
+#include <algorithm>
+
 namespace sfm {
 
 using scan_detail::kMaxWaves;
@@ -16,17 +18,29 @@ int odd_word_stride(int elems, int elem_bytes) {
     return s;
 }
 
-// Lane-split plan (scan_split.h): whole sample rows staged by 16-byte
-// transfers, G lanes per channel.  Returns false when the shape does not fit
-// (alignment, LDS), leaving the classic kernel to plan it.  G is the smallest
+// smallest odd number of 4-byte words >= w (rows that far apart in LDS put the
+// 64 lanes reading one column into distinct banks)
+int odd_words(int w) { return w | 1; }
+
+// Lane-split plan (scan_split.h), G lanes per channel.  G is the smallest
 // group that gives every SIMD of the device about four waves (a lone wave
 // issues a VALU instruction at most every five to six cycles, a SIMD with
 // four or more every four), else the largest; split_hint > 0 forces G.
-bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, int cus) {
+// Staging: whole sample rows (x, delta and raw B/C by 16-byte transfers), or,
+// when that leaves fewer waves resident per CU than the grid could use,
+// chunked (x whole rows; delta/y and raw B/C sq positions at a time by 4-byte
+// transfers).  chunk_hint: < 0 automatic, 0 whole rows only, > 0 forces sq.
+// Returns false when the shape does not fit (alignment, LDS), leaving the
+// classic kernel to plan it.
+bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, int chunk_hint, int cus) {
     const int L = p.L, XL = p.xrow, N = p.N, D = p.D;
     const int ns = p.N <= 4 ? 4 : (p.N <= 8 ? 8 : 16);
-    const long long dl = (long long)D * L * io_bytes, dx = (long long)D * XL * io_bytes;
-    if (dl % 16 || dx % 16 || ((long long)N * L * io_bytes) % 16 || L > 1024) return false;
+    const int ew = 4 / io_bytes;
+    if (((long long)D * XL * io_bytes) % 16) return false;  // x whole rows by 16-byte transfers
+    const bool whole_ok = ((long long)D * L * io_bytes) % 16 == 0 && ((long long)N * L * io_bytes) % 16 == 0 &&
+                          L <= 1024 && chunk_hint <= 0;
+    const bool chunk_ok = ((long long)L * io_bytes) % 4 == 0 && XL <= 2048 && chunk_hint != 0;
+    if (!whole_ok && !chunk_ok) return false;
     int cands[2] = {2, 4};
     int nc = ns == 4 ? 1 : 2;
     if (split_hint > 0) {
@@ -37,50 +51,78 @@ bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, i
     }
     constexpr int kLdsCap = 160 * 1024;
     constexpr int kLdsUnit = 1280;
-    int best_g = 0;
+    constexpr int kRegWavesPerCu = 20;  // five waves per SIMD by registers
+    auto units = [&](int b) { return (b + kLdsUnit - 1) / kLdsUnit * kLdsUnit; };
+    int G = 0;
     for (int ci = 0; ci < nc; ++ci) {
-        const int G = cands[ci];
-        const int cpw = kWave / G;
-        if (((long long)cpw * L * io_bytes) % 16 || ((long long)cpw * XL * io_bytes) % 16) continue;
-        best_g = G;
+        const int g = cands[ci];
+        const int cpw = kWave / g;
+        if (((long long)cpw * XL * io_bytes) % 16) continue;
+        if (whole_ok && !chunk_ok && ((long long)cpw * L * io_bytes) % 16) continue;
+        G = g;
         const long long waves = (long long)p.B1 * ((D + cpw - 1) / cpw);
         if (waves >= 4LL * 4 * cus) break;  // about four waves per SIMD
     }
-    if (!best_g) return false;
-    const int G = best_g, cpw = kWave / G;
+    if (!G) return false;
+    const int cpw = kWave / G;
     const int tiles = (D + cpw - 1) / cpw;
-    const int bc = L * 2 * ns * (int)sizeof(float);
-    const int braw = (2 * N * L * io_bytes + 15) & ~15;
-    const int mean_bytes = 4 * 64 * (int)sizeof(float);  // row means of up to 256 channels (wpg <= 4)
+    const int wpg = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
+    const int gch = wpg * cpw;
+    const int mean_bytes = (gch * (int)sizeof(float) + 15) & ~15;
     const int xsb = (cpw * XL * io_bytes + 15) & ~15;
-    const int dsb = (cpw * L * io_bytes + 15) & ~15;
-    // waves per workgroup: four (one per SIMD) when two such groups fit in LDS
-    int wpg = 0;
-    for (int w = 4; w >= 1; w /= 2) {
-        if (w > tiles) continue;
-        const int tot = bc + braw + mean_bytes + w * (xsb + dsb);
-        if (2 * ((tot + kLdsUnit - 1) / kLdsUnit * kLdsUnit) <= kLdsCap) {
-            wpg = w;
-            break;
-        }
+    const long long grid = (long long)((tiles + wpg - 1) / wpg) * p.B1;
+    auto resident = [&](int lds) { return std::min(kRegWavesPerCu, kLdsCap / units(lds) * wpg); };
+    // whole rows
+    int w_lds = 0, w_res = 0;
+    const int bc_w = L * 2 * ns * (int)sizeof(float);
+    const int braw_w = (2 * N * L * io_bytes + 15) & ~15;
+    const int dsb_w = (cpw * L * io_bytes + 15) & ~15;
+    if (whole_ok && ((long long)cpw * L * io_bytes) % 16 == 0) {
+        w_lds = bc_w + braw_w + mean_bytes + wpg * (xsb + dsb_w);
+        if (w_lds <= kLdsCap) w_res = resident(w_lds);
     }
-    if (!wpg) return false;
-    // resident waves per CU that LDS allows (the kernels hold up to five per
-    // SIMD by registers): fewer than two per SIMD leaves the classic kernel ahead
-    const int per_wg = (bc + braw + mean_bytes + wpg * (xsb + dsb) + kLdsUnit - 1) / kLdsUnit * kLdsUnit;
-    if (split_hint <= 0 && kLdsCap / per_wg * wpg < 8) return false;
+    // chunked: the largest chunk with the most resident waves
+    int c_q = 0, c_lds = 0, c_res = 0, c_dpw = 0, c_di = 0, c_bi = 0;
+    if (chunk_ok) {
+        const int step = std::max(G, ew);
+        for (int q : {64, 48, 32, 24, 16}) {
+            if (chunk_hint > 0 && q != chunk_hint) continue;
+            if (q % step || q < 2 * step) continue;
+            const int qq = std::min(q, (L + step - 1) / step * step);
+            const int pw = odd_words((qq + ew - 1) / ew);
+            const int di = (cpw * pw + kWave - 1) / kWave;  // transfers of one delta tile
+            const int bi = (N * pw + kWave - 1) / kWave;    // of one raw B or C tile
+            const int lds = qq * 2 * ns * (int)sizeof(float) + 2 * bi * 256 + mean_bytes + wpg * (xsb + di * 256);
+            if (lds > kLdsCap) continue;
+            const int r = resident(lds);
+            if (r > c_res) {
+                c_q = qq;
+                c_lds = lds;
+                c_res = r;
+                c_dpw = pw;
+                c_di = di;
+                c_bi = bi;
+            }
+            if (qq >= L) break;
+        }
+        if (chunk_hint > 0 && !c_q) return false;
+    }
+    // Whole rows whenever they keep two or more waves per SIMD resident: the
+    // chunked staging's per-chunk waits, barriers and B/C widening cost more
+    // than its extra residency gains (measured at stage-3 shapes: whole rows,
+    // 2 waves per SIMD, 76 us; 24-position chunks, 5 per SIMD, 81-83 us).
+    bool chunk;
+    if (chunk_hint > 0) chunk = true;
+    else if (w_res >= 8 || (w_res > 0 && w_res >= c_res)) chunk = false;
+    else chunk = c_res > 0;
+    const int res = chunk ? c_res : w_res;
+    if (res == 0) return false;
+    // fewer than two resident waves per SIMD leaves the classic kernel ahead
+    if (split_hint <= 0 && res < 8) return false;
     p.split = G;
     p.wpg = wpg;
     p.stiles = (tiles + wpg - 1) / wpg;
     p.ns = ns;
-    p.bc_off = 0;
-    p.braw_off = bc;
-    p.mean_off = bc + braw;
-    p.slab_off = bc + braw + mean_bytes;
-    p.xs_bytes = xsb;
-    p.ds_bytes = dsb;
-    p.slab_bytes = xsb + dsb;
-    p.lds_bytes = bc + braw + mean_bytes + wpg * (xsb + dsb);
     p.tiles = tiles;
     p.mode = 0;
     p.ch = L;
@@ -89,14 +131,37 @@ bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, i
     p.need_carry = 0;
     p.cw = wpg;
     p.tgroups = p.stiles;
-    // Staggered start when the whole grid is resident at once: dispatch round
-    // r (one workgroup per CU) delays its loads by r times the time HBM needs
-    // for one round's inputs at about 6.5 TB/s (65000 bytes per 10 ns tick).
+    p.xs_bytes = xsb;
+    if (chunk) {
+        p.sq = c_q;
+        p.dpw = c_dpw;
+        p.bpw = c_dpw;
+        p.dtile_insts = c_di;
+        p.btile_insts = c_bi;
+        p.bc_off = 0;
+        p.braw_off = c_q * 2 * ns * (int)sizeof(float);
+        p.mean_off = p.braw_off + 2 * c_bi * 256;
+        p.slab_off = p.mean_off + mean_bytes;
+        p.ds_bytes = c_di * 256;
+        p.lds_bytes = c_lds;
+    } else {
+        p.sq = 0;
+        p.bc_off = 0;
+        p.braw_off = bc_w;
+        p.mean_off = bc_w + braw_w;
+        p.slab_off = bc_w + braw_w + mean_bytes;
+        p.ds_bytes = dsb_w;
+        p.lds_bytes = w_lds;
+    }
+    p.slab_bytes = p.xs_bytes + p.ds_bytes;
+    // Staggered start (whole rows) when the whole grid is resident at once:
+    // dispatch round r (one workgroup per CU) delays its loads by r times the
+    // time HBM needs for one round's inputs at about 6.5 TB/s (65000 bytes per
+    // 10 ns tick).
     p.stagger_period = 0;
     p.stagger_ticks = 0;
-    const long long grid = (long long)p.stiles * p.B1;
-    const int wg_per_cu = kLdsCap / per_wg;
-    if (stagger_hint != 0 && grid > cus && grid <= (long long)cus * (wg_per_cu < 5 ? wg_per_cu : 5)) {
+    const int wg_per_cu = res / wpg;
+    if (!chunk && stagger_hint != 0 && grid > cus && grid <= (long long)cus * wg_per_cu) {
         const long long wg_bytes = (long long)wpg * cpw * (XL + L) * io_bytes + 2LL * N * L * io_bytes;
         long long ticks = stagger_hint > 0 ? stagger_hint : (long long)cus * wg_bytes / 65000;
         if (ticks > 500) ticks = 500;
@@ -123,7 +188,7 @@ int device_cus() {
 }
 
 bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint, int stages_hint,
-               int split_hint) {
+               int split_hint, int split_chunk_hint) {
     const int L = p.L, S = p.B2 * p.L;
     if (p.xrow <= 0) p.xrow = p.pad_in ? L - 2 : L;
     p.split = 0;
@@ -135,7 +200,8 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     const int cus = device_cus();
     const long long lane_waves = (long long)p.B1 * p.B2 * ((p.D + kWave - 1) / kWave);
     const bool want_split = split_hint > 0 || (split_hint < 0 && lane_waves < 2LL * 4 * cus);
-    if (want_split && waves_hint <= 0 && ch_hint <= 0 && plan_split(p, io_bytes, split_hint, stagger_hint, cus))
+    if (want_split && waves_hint <= 0 && ch_hint <= 0 &&
+        plan_split(p, io_bytes, split_hint, stagger_hint, split_chunk_hint, cus))
         return true;
     const int XL = p.xrow;
     // The fused pad/swap keep each sample inside one wave, except with tile

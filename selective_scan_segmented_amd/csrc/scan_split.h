@@ -72,6 +72,54 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// 4-byte direct global->LDS transfers of a tile: words [0, nw) of rows
+// [0, rows) of a region whose rows start rowb bytes apart at g, into LDS rows of
+// pw words at l.  LDS word e = 64 k + lane of instruction k holds word e % pw of
+// row e / pw; a slot past the valid rows or words re-reads the last valid word
+// (in bounds, never read back).  Instructions k0, k0 + kstep, ... of ninst (so
+// the waves of a group can share a tile), four per LDS base where four remain.
+__device__ __forceinline__ void dma_tile4(const char* g, uint32_t rowb, int rows, int nw, int pw, char* l, int lane,
+                                          int ninst, int k0 = 0, int kstep = 1) {
+    if (rows <= 0 || nw <= 0) return;
+    const float inv = 1.0f / (float)pw;
+    const uint32_t maxoff = (uint32_t)(rows - 1) * rowb + (uint32_t)(nw - 1) * 4u;
+    auto off_of = [&](int k) __attribute__((always_inline)) {
+        const int e = k * kWave + lane;
+        const int r = div_small(e, inv);
+        const int w = e - r * pw;
+        return min((uint32_t)r * rowb + (uint32_t)min(w, nw - 1) * 4u, maxoff);
+    };
+    int k = k0;
+    if (kstep == 1) {
+        for (; k + 4 <= ninst; k += 4) {
+            char* lk = l + k * 256;
+            dma_at<4, 0>(g + off_of(k), lk);
+            dma_at<4, 256>(g + off_of(k + 1), lk);
+            dma_at<4, 512>(g + off_of(k + 2), lk);
+            dma_at<4, 768>(g + off_of(k + 3), lk);
+        }
+    }
+    for (; k < ninst; k += kstep) dma_at<4, 0>(g + off_of(k), l + k * 256);
+}
+
+// Float64 sum of r[0 .. n) in index order (bit-identical to a sequential CPU
+// sum); the LDS reads go out eight at a time, so the additions wait on one
+// read latency per eight elements, not per element.
+template <typename IO>
+__device__ __forceinline__ double row_sum_f64(const IO* r, int n) {
+    double acc = 0.0;
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = to_f32(r[i + k]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += (double)v[k];
+    }
+    for (; i < n; ++i) acc += (double)to_f32(r[i]);
+    return acc;
+}
+
 template <typename IO, int NS, int G, int KW, bool CONV, bool SP, bool SILU>
 struct SplitWave {
     static constexpr int NPL = NS / G;   // states per lane
@@ -204,41 +252,63 @@ struct SplitWave {
         if (!CHECK || tau < L) dr[tau] = from_f32<IO>(yown);
     }
 
-    // Whole sample: positions [0, L) from the staged rows; y replaces delta.
-    __device__ __forceinline__ void sample(const IO* xr, IO* dr, const float* bc) {
+    // Blocks of a sample that need no checks, [kA, kB): every position < L and
+    // every newly read conv tap inside the interior [lo, L-1-lo] of padded
+    // positions (the taps kept from the previous block were read there already).
+    __device__ __forceinline__ void bounds(int& kA, int& kB, int& nblk) const {
         const int L = p.L;
-        float h[NPL];
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) h[i] = 0.0f;
-        float win[KW];
         const int P2 = p.P + KW - p.K;
-        // taps of the virtual position g - G (the block loop shifts by G first)
-#pragma unroll
-        for (int j = 0; j < KW; ++j) win[j] = CONV ? xq(xr, g - G - P2 + j) : 0.0f;
-        const int nblk = (L + G - 1) / G;
-        // Blocks that need no checks: every position < L and every newly read
-        // conv tap inside the staged interior [lo, L-1-lo] of padded positions
-        // (the taps kept from the previous block were read there already).
+        nblk = (L + G - 1) / G;
         const int lo = p.pad_in ? 1 : 0;
         constexpr int keep = CONV ? (KW > G ? KW - G : 0) : 0;
-        const int first_new = CONV ? keep - P2 : 0;           // tap offset of the oldest new tap
-        const int last_new = CONV ? KW - 1 - P2 : 0;          // tap offset of the newest tap
+        const int first_new = CONV ? keep - P2 : 0;   // tap offset of the oldest new tap
+        const int last_new = CONV ? KW - 1 - P2 : 0;  // tap offset of the newest tap
         // k*G + first_new >= lo  and  k*G + G-1 + last_new <= L-1-lo  and  k*G + G-1 <= L-1
-        int kA = lo - first_new;
+        kA = lo - first_new;
         kA = kA <= 0 ? 1 : max(1, (kA + G - 1) / G);
         const int hiA = min(L - 1 - lo - (G - 1) - last_new, L - G);
-        int kB = hiA >= 0 ? hiA / G + 1 : 0;
+        kB = hiA >= 0 ? hiA / G + 1 : 0;
         if (kB > nblk) kB = nblk;
         if (kB < kA) kB = kA;
-        block<true, true>(0, xr, dr, bc, h, win);
-        int k = 1;
-        for (; k < kA && k < nblk; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
-        for (; k + 1 < kB; k += 2) {  // two blocks per trip: LDS offsets become immediates
+    }
+
+    // State and conv window at the sample start: taps of the virtual position
+    // g - G (the block loop shifts the window by G first).
+    __device__ __forceinline__ void start(const IO* xr, float (&h)[NPL], float (&win)[KW]) const {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) h[i] = 0.0f;
+        const int P2 = p.P + KW - p.K;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) win[j] = CONV ? xq(xr, g - G - P2 + j) : 0.0f;
+    }
+
+    // Blocks [k0, k1) of the sample.  xr, dr and bc are addressed by absolute
+    // position (they may point before a staged chunk).
+    __device__ __forceinline__ void blocks(int k0, int k1, int kA, int kB, const IO* xr, IO* dr, const float* bc,
+                                           float (&h)[NPL], float (&win)[KW]) {
+        int k = k0;
+        if (k == 0 && k < k1) {
+            block<true, true>(0, xr, dr, bc, h, win);
+            k = 1;
+        }
+        for (; k < kA && k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
+        const int ke = min(kB, k1);
+        for (; k + 1 < ke; k += 2) {  // two blocks per trip: LDS offsets become immediates
             block<false, false>(k * G, xr, dr, bc, h, win);
             block<false, false>(k * G + G, xr, dr, bc, h, win);
         }
-        for (; k < kB; ++k) block<false, false>(k * G, xr, dr, bc, h, win);
-        for (; k < nblk; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
+        for (; k < ke; ++k) block<false, false>(k * G, xr, dr, bc, h, win);
+        for (; k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
+    }
+
+    // Whole sample: positions [0, L) from the staged rows; y replaces delta.
+    __device__ __forceinline__ void sample(const IO* xr, IO* dr, const float* bc) {
+        float h[NPL];
+        float win[KW];
+        int kA, kB, nblk;
+        bounds(kA, kB, nblk);
+        start(xr, h, win);
+        blocks(0, nblk, kA, kB, xr, dr, bc, h, win);
     }
 };
 
@@ -328,9 +398,7 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_kernel(ScanParams p) {
             if (r < gch && oc < orows) {
                 // float64, index order, one rounding: bit-identical to the aux pad
                 const IO* row = reinterpret_cast<const IO*>(smem + p.slab_off + (size_t)ow * p.slab_bytes) + oc * XL;
-                double acc = 0.0;
-                for (int t = 0; t < XL; ++t) acc += (double)to_f32(row[t]);
-                means[r] = to_f32(Io<IO>::from_f64(acc / (double)XL));
+                means[r] = to_f32(Io<IO>::from_f64(row_sum_f64(row, XL) / (double)XL));
             }
         }
         // (with a single wave per group it does both in turn)
@@ -371,15 +439,191 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_kernel(ScanParams p) {
     (void)NPL;
 }
 
+// Chunked variant for rows too long to stage delta whole: the conv input x
+// stays whole rows in LDS (it feeds the conv windows and the fused pad's row
+// mean), while delta/y and the raw B/C move sq positions at a time by 4-byte
+// transfers into odd-pitch LDS rows (conflict-free column reads), so about
+// five workgroups of four waves fit a CU at stage-3 row lengths.  Per chunk:
+// wait, workgroup barrier, B/C widened by all waves, barrier, the blocks of the
+// chunk (y over delta in the tile), y stored by 4-byte stores (with the fused
+// swap, the end tokens leave one by one), then the next chunk's transfers; the
+// next chunk's raw B/C go out as soon as the current one is widened.
+template <typename IO, int NS, int G, int KW, bool CONV, bool SP, bool SILU>
+__global__ __launch_bounds__(kWave * kMaxWpg) void split_chunk_kernel(ScanParams p) {
+    using W = SplitWave<IO, NS, G, KW, CONV, SP, SILU>;
+    constexpr int NPL = W::NPL;
+    constexpr int CPW = W::CPW;
+    constexpr int ew = 4 / (int)sizeof(IO);  // elements per 4-byte word
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    if (p.stagger_ticks) {
+        const unsigned long long r = blockIdx.x / p.stagger_period;
+        if (r) {
+            const unsigned long long until = __builtin_amdgcn_s_memrealtime() + r * p.stagger_ticks;
+            while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int NGRP = p.stiles * p.B1;
+    int gi = blockIdx.x;
+    if ((NGRP & 7) == 0) gi = (gi & 7) * (NGRP >> 3) + (gi >> 3);
+    const int b1 = gi / p.stiles;
+    const int tile = gi - b1 * p.stiles;
+    const int dw0 = (tile * p.wpg + wave) * CPW;
+    W w(p, lane, dw0);
+    const int L = p.L, XL = p.xrow, N = p.N, D = p.D, Q = p.sq;
+    const uint32_t rowb = (uint32_t)L * sizeof(IO);
+    float* bc = reinterpret_cast<float*>(smem + p.bc_off);        // [Q][G][B.., C..] float32
+    char* btile = smem + p.braw_off;                              // raw B rows [N][bpw words]
+    char* ctile = btile + p.btile_insts * 256;                    // raw C rows
+    float* means = reinterpret_cast<float*>(smem + p.mean_off);
+    char* slab = smem + p.slab_off + (size_t)wave * p.slab_bytes;
+    IO* xs = reinterpret_cast<IO*>(slab);                         // [CPW][XL] whole rows
+    char* dtile = slab + p.xs_bytes;                              // [CPW][dpw words]
+    const int rows = w.rows;
+    const int nthr = p.wpg * kWave;
+    const int tid = threadIdx.x;
+
+    auto issue_bc = [&](int b, int t0, int len) __attribute__((always_inline)) {
+        const int nw = (len + ew - 1) / ew;
+        const char* bg = reinterpret_cast<const char*>(static_cast<const IO*>(p.Bm) + ((size_t)b * N) * L + t0);
+        const char* cg = reinterpret_cast<const char*>(static_cast<const IO*>(p.Cm) + ((size_t)b * N) * L + t0);
+        dma_tile4(bg, rowb, N, nw, p.bpw, btile, lane, p.btile_insts, wave, p.wpg);
+        dma_tile4(cg, rowb, N, nw, p.bpw, ctile, lane, p.btile_insts, p.wpg - 1 - wave, p.wpg);
+    };
+    auto issue_d = [&](int b, int t0, int len) __attribute__((always_inline)) {
+        const int nw = (len + ew - 1) / ew;
+        const char* dg = reinterpret_cast<const char*>(static_cast<const IO*>(p.delta) + ((size_t)b * D + dw0) * L + t0);
+        dma_tile4(dg, rowb, rows, nw, p.dpw, dtile, lane, p.dtile_insts);
+    };
+    auto widen = [&](int len, int first_wave) __attribute__((always_inline)) {
+        const int wthr = (p.wpg - first_wave) * kWave;
+        const float inv = 1.0f / (float)len;
+        const IO* bt = reinterpret_cast<const IO*>(btile);
+        const IO* ct = reinterpret_cast<const IO*>(ctile);
+        for (int e = tid - first_wave * kWave; e < N * len; e += wthr) {
+            const int n = div_small(e, inv), q = e - n * len;
+            float* o = bc + (q * G + n / NPL) * (2 * NPL) + n % NPL;
+            o[0] = to_f32(bt[n * p.bpw * ew + q]);
+            o[NPL] = to_f32(ct[n * p.bpw * ew + q]);
+        }
+    };
+
+    w.load_params();
+    if (N < NS) {  // states n >= N: B = C = 0 for the whole launch (widening never writes them)
+        for (int e = tid; e < Q * NS; e += nthr) {
+            const int q = e / NS, n = e - q * NS;
+            if (n >= N) {
+                float* o = bc + (q * G + n / NPL) * (2 * NPL) + n % NPL;
+                o[0] = 0.0f;
+                o[NPL] = 0.0f;
+            }
+        }
+    }
+    const IO* xr = xs + w.c * XL;
+    IO* drow = reinterpret_cast<IO*>(dtile) + w.c * p.dpw * ew;  // this lane's delta/y tile row
+    const int nch = (L + Q - 1) / Q;
+    int kA, kB, nblk;
+    w.bounds(kA, kB, nblk);
+    for (int j = 0; j < p.B2; ++j) {
+        const int b = b1 * p.B2 + j;
+        const int len0 = min(Q, L);
+        if (rows > 0) {
+            const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + dw0) * XL;
+            dma_to_lds(xg, xs, rows * XL * (int)sizeof(IO), lane);
+        }
+        issue_bc(b, 0, len0);
+        if (rows > 0) issue_d(b, 0, len0);
+        IO* yg = static_cast<IO*>(p.y) + ((size_t)b * D + dw0) * L;
+        float h[NPL];
+        float win[KW];
+        IO y0 = Io<IO>::zero();  // fused swap: y at t = 0 of this lane's row, written last
+        for (int c = 0; c < nch; ++c) {
+            const int t0 = c * Q, len = min(Q, L - t0);
+            wait_vmem();
+            __syncthreads();  // this chunk's delta and raw B/C (and at c = 0 the x rows) have landed
+            if (c == 0) {
+                // the row means (first waves, one lane per channel of the group)
+                // and the first chunk's B/C (the others)
+                const int gch = p.wpg * CPW;
+                const int nmean = p.pad_in ? min(p.wpg, (gch + kWave - 1) / kWave) : 0;
+                if (wave < nmean) {
+                    const int r = wave * kWave + lane;
+                    const int ow = r / CPW, oc = r - ow * CPW;
+                    const int orows = max(0, min(CPW, D - (tile * p.wpg + ow) * CPW));
+                    if (r < gch && oc < orows) {
+                        const IO* row = reinterpret_cast<const IO*>(smem + p.slab_off + (size_t)ow * p.slab_bytes) +
+                                        oc * XL;
+                        // float64, index order, one rounding: bit-identical to the aux pad
+                        means[r] = to_f32(Io<IO>::from_f64(row_sum_f64(row, XL) / (double)XL));
+                    }
+                }
+                const int wb = nmean < p.wpg ? nmean : 0;
+                if (wave >= wb) widen(len, wb);
+            } else {
+                widen(len, 0);
+            }
+            __syncthreads();  // B/C of the chunk (and the row means) visible to the group
+            if (c + 1 < nch) issue_bc(b, t0 + Q, min(Q, L - t0 - Q));  // the raw B/C tiles are free again
+            if (c == 0) {
+                if (p.pad_in) w.mean = means[wave * CPW + w.c];
+                w.start(xr, h, win);
+            }
+            const int k0 = t0 / G;
+            const int k1 = c + 1 == nch ? nblk : (t0 + len) / G;
+            w.blocks(k0, k1, kA, kB, xr, drow - t0, bc - t0 * G * (2 * NPL), h, win);
+            wave_lds_sync();
+            if (rows > 0) {
+                // y of positions [t0, t0 + len) from the tile, 4-byte words; with the
+                // fused swap the words holding positions 0 and L-1 leave element-wise
+                const bool sw = p.swap_out && L > 1;
+                const int nw = (len + ew - 1) / ew;
+                const int wlo = (sw && t0 == 0) ? 1 : 0;
+                const int whi = (sw && t0 + len == L) ? nw - 1 : nw;
+                const float inv = 1.0f / (float)p.dpw;
+                const uint32_t* tw = reinterpret_cast<const uint32_t*>(dtile);
+                for (int k = 0; k < p.dtile_insts; ++k) {
+                    const int e = k * kWave + lane;
+                    const int r = div_small(e, inv), wd = e - r * p.dpw;
+                    if (r < rows && wd >= wlo && wd < whi)
+                        reinterpret_cast<uint32_t*>(yg + (size_t)r * L + t0)[wd] = tw[e];
+                }
+                if (sw && w.g == 0 && w.c < rows) {
+                    IO* yr = yg + (size_t)w.c * L;
+                    if (t0 == 0) {
+                        y0 = drow[0];
+                        for (int q = 1; q < min(ew, len); ++q) yr[q] = drow[q];
+                    }
+                    if (t0 + len == L) {
+                        const int lw = (nw - 1) * ew;  // first position of the last word, relative to t0
+                        for (int q = lw; q < len - 1; ++q) yr[t0 + q] = drow[q];
+                        yr[0] = drow[L - 1 - t0];
+                        yr[L - 1] = y0;
+                    }
+                }
+            }
+            if (c + 1 < nch) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile's reads are done
+                if (rows > 0) issue_d(b, t0 + Q, min(Q, L - t0 - Q));
+            }
+        }
+        if (j + 1 < p.B2) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();  // every wave is done with this sample's x rows and B/C
+        }
+    }
+    (void)NPL;
+}
+
 template <typename IO, int NS, int G, int KW, bool CONV, bool SP, bool SILU>
 hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
-    auto kern = split_kernel<IO, NS, G, KW, CONV, SP, SILU>;
-    static bool attr_set = false;
-    if (!attr_set && p.lds_bytes > 64 * 1024) {
+    auto kern = p.sq > 0 ? split_chunk_kernel<IO, NS, G, KW, CONV, SP, SILU> : split_kernel<IO, NS, G, KW, CONV, SP, SILU>;
+    static bool attr_set[2] = {false, false};
+    if (!attr_set[p.sq > 0] && p.lds_bytes > 64 * 1024) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 160 * 1024) != hipSuccess)
             (void)hipGetLastError();
-        attr_set = true;
+        attr_set[p.sq > 0] = true;
     }
     const unsigned grid = (unsigned)(p.stiles * p.B1);
     const unsigned block = (unsigned)(kWave * p.wpg);

@@ -148,6 +148,12 @@ static int split_hint_env() {
     if (const char* e = std::getenv("SFM_SCAN_SPLIT")) return std::atoi(e);
     return -1;
 }
+// SFM_SCAN_SPLIT_CHUNK (diagnostics): 0 keeps the lane-split kernel's whole-row
+// staging, q > 0 asks for its chunked staging with q positions per chunk.
+static int split_chunk_hint_env() {
+    if (const char* e = std::getenv("SFM_SCAN_SPLIT_CHUNK")) return std::atoi(e);
+    return -1;
+}
 
 sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* Bm,
                                      const void* Cm, const float* Dskip, const float* delta_bias,
@@ -222,7 +228,7 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
     int stagger_hint = -1, stages_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_STAGGER")) stagger_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_STAGES")) stages_hint = std::atoi(e);
-    if (!sfm::plan_scan(p, eb, waves_hint, ch_hint, stagger_hint, stages_hint, split_hint_env()))
+    if (!sfm::plan_scan(p, eb, waves_hint, ch_hint, stagger_hint, stages_hint, split_hint_env(), split_chunk_hint_env()))
         return fail(SFM_ERR_UNSUPPORTED, "sfm_selective_scan_fwd: no launch plan fits LDS for this shape");
     return hip_status(sfm::launch_scan(p, io_dtype, static_cast<hipStream_t>(stream)), "sfm_selective_scan_fwd");
 }
@@ -277,11 +283,12 @@ sfm_status sfm_scan_plan_string(int64_t B1, int64_t B2, int64_t D, int64_t N, in
     int stagger_hint = -1, stages_hint = 0;
     if (const char* e = std::getenv("SFM_SCAN_STAGGER")) stagger_hint = std::atoi(e);
     if (const char* e = std::getenv("SFM_SCAN_STAGES")) stages_hint = std::atoi(e);
-    if (!sfm::plan_scan(p, io_bytes(io_dtype), waves_hint, ch_hint, stagger_hint, stages_hint, split_hint_env()))
+    if (!sfm::plan_scan(p, io_bytes(io_dtype), waves_hint, ch_hint, stagger_hint, stages_hint, split_hint_env(), split_chunk_hint_env()))
         return fail(SFM_ERR_UNSUPPORTED, "sfm_scan_plan_string: no launch plan fits LDS");
     if (p.split) {
-        snprintf(buf, (size_t)cap, "split=%d ns=%d wpg=%d lds=%d grid=%lld block=%d stagger=%d/%d", p.split, p.ns,
-                 p.wpg, p.lds_bytes, (long long)p.stiles * p.B1, 64 * p.wpg, p.stagger_ticks, p.stagger_period);
+        snprintf(buf, (size_t)cap, "split=%d chunk=%d ns=%d wpg=%d lds=%d grid=%lld block=%d stagger=%d/%d", p.split,
+                 p.sq, p.ns, p.wpg, p.lds_bytes, (long long)p.stiles * p.B1, 64 * p.wpg, p.stagger_ticks,
+                 p.stagger_period);
         return ok();
     }
     snprintf(buf, (size_t)cap,

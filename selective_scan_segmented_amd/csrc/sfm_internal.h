@@ -53,6 +53,10 @@ struct ScanParams {
     // B/C rows, the raw B/C area and the first wave's x/delta slabs.
     int split, wpg, stiles;
     int bc_off, braw_off, mean_off, slab_off, slab_bytes;
+    // Chunked lane-split kernel (sq > 0): x stays whole rows, delta/y and the
+    // raw B/C of sq positions at a time by 4-byte transfers into LDS rows of
+    // dpw / bpw words (odd pitches), dtile_insts / btile_insts transfers each.
+    int sq, dpw, bpw, dtile_insts, btile_insts;
 };
 
 // Fills the plan fields; waves_hint / ch_hint <= 0 select automatically,
@@ -60,7 +64,7 @@ struct ScanParams {
 // > 0 sets the delay per dispatch round in 10 ns ticks.
 // stages_hint (mode 1): 1 or 2 forces the LDS stages per wave, else automatic.
 bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int stagger_hint = -1, int stages_hint = 0,
-               int split_hint = -1);
+               int split_hint = -1, int split_chunk_hint = -1);
 // Compute units of the current device (256 when no device can be queried).
 int device_cus();
 hipError_t launch_scan(const ScanParams& p, int io_dtype, hipStream_t stream);

@@ -1,8 +1,8 @@
 """Parity of the HIP backward (through the C ABI) against the float64 oracle backward.
 
 Tolerance (|g - r| <= rtol (|r| + rms r), the forward's rule): the backward
-runs the reverse recurrence and per-position sums in float32 and adds the
-per-channel / per-sample sums with float32 atomics in no fixed order, so its
+runs the reverse recurrence and the per-position sums in float32 and adds the
+per-tile / per-sample partial sums in a fixed order (a reduce launch), so its
 float32 bar is 1e-4 (ten times the forward's 1e-5).  Outputs stored in bfloat16
 (du, ddelta) keep the forward's 2e-2; float32 sums computed from bfloat16
 inputs use 1e-3.

@@ -214,3 +214,64 @@ def test_planner_picks_the_kernel_by_waves_per_simd():
     with env(SFM_SCAN_SPLIT=-1):
         assert "split=4" in sfm.sfm_scan_plan_string(256, 1, 320, 8, 198, 4, "bf16", 3)
         assert "mode=0" in sfm.sfm_scan_plan_string(256, 1, 640, 8, 51, 4, "bf16", 3)
+
+
+CHUNK_SHAPES = [
+    # B, D, N, T, B2, K, P, act, bias, io, G, chunk
+    (4, 64, 8, 196, 1, 4, 1, None, False, "bf16", 4, 24),    # stage-3 rows, ragged last chunk (6 positions)
+    (4, 64, 8, 196, 2, 4, 1, "silu", True, "bf16", 2, 32),   # two lanes per channel, folded rows
+    (3, 72, 16, 62, 3, 8, 3, None, True, "f32", 4, 16),      # partial wave, widest conv, 16 states
+    (2, 64, 5, 30, 2, 3, 0, None, False, "f32", 4, 16),      # two chunks, N padded to 8
+    (2, 64, 8, 1, 1, 4, 1, None, False, "f32", 4, 16),       # L = 3: one chunk shorter than the chunk size
+    (2, 128, 8, 46, 1, 4, 2, None, False, "bf16", 4, 48),    # one chunk holding both swapped ends
+    (2, 64, 8, 25, 1, 4, 1, None, False, "f32", 4, 16),      # odd L (f32 words are single elements)
+]
+
+
+@pytest.mark.parametrize("B,D,N,T,B2,K,P,act,bias,io,G,chunk", CHUNK_SHAPES)
+@pytest.mark.parametrize("flags", [0, 3])
+def test_split_chunked_against_oracle(B, D, N, T, B2, K, P, act, bias, io, G, chunk, flags):
+    """The chunked staging (x whole rows; delta/y and raw B/C in chunks)."""
+    import torch
+    say(f"split chunked B={B} D={D} N={N} T={T} B2={B2} K={K} io={io} G={G} chunk={chunk} flags={flags}")
+    L = T + 2
+    x, delta, Bm, Cm, A, Dk, db, cw, cb = make(B, D, N, T, K, io, seed=B * 5 + D + N + T + chunk, bias=bias)
+    Tt = lambda a: torch.from_numpy(a).cuda()
+    xd, dd, Bd, Cd = map(to_dev, (x, delta, Bm, Cm))
+    xp64 = oracle.aux_pad(up(x), io)
+    want = oracle.layer(xp64, up(delta), A, up(Bm), up(Cm), Dk, db, cw, cb, pad_left=P,
+                        act=1 if act == "silu" else 0)
+    with env(SFM_SCAN_SPLIT=G, SFM_SCAN_SPLIT_CHUNK=chunk):
+        plan = sfm.sfm_scan_plan_string(B // B2, B2, D, N, L, K, io, flags)
+        assert f"split={G} chunk={min(chunk, (L + 3) // 4 * 4)}" in plan, plan
+        u = xd if flags & 1 else sfm.sfm_aux_pad_swap(xd, mode="pad")
+        y = torch.full((B, D, L), float("nan"), dtype=xd.dtype, device="cuda")
+        sfm.sfm_selective_scan_fwd_ex(u, dd, Tt(A), Bd, Cd, Tt(Dk), Tt(db), conv_w=Tt(cw),
+                                      conv_b=None if cb is None else Tt(cb), conv_pad_left=P, conv_act=act,
+                                      y=y, B2=B2, flags=flags)
+        torch.cuda.synchronize()
+    got = from_dev(y)
+    if flags & 2:
+        want = oracle.aux_swap(want)
+    assert_close(got, want, io, f"split chunked G={G} chunk={chunk}")
+
+
+@pytest.mark.parametrize("G,N", [(2, 1), (4, 5)])
+def test_split_chunked_integer_scan(G, N):
+    """A = 0, Delta = 1, B = C = 1, D = 0, u = 1  =>  y = N (t + 1) exactly, chunk by chunk."""
+    import torch
+    B, D, L = 4, 64, 70
+    a = _int_inputs(B, D, L, N, 0.0)
+    with env(SFM_SCAN_SPLIT=G, SFM_SCAN_SPLIT_CHUNK=16):
+        assert f"split={G} chunk=16" in sfm.sfm_scan_plan_string(B, 1, D, N, L, 0, "f32", 0)
+        y = sfm.sfm_selective_scan_fwd(**a, delta_softplus=False, B2=2)
+        torch.cuda.synchronize()
+    want = np.broadcast_to(N * np.arange(1, L + 1, dtype=np.float64), (B, D, L))
+    assert np.array_equal(from_dev(y), want)
+
+
+def test_planner_keeps_whole_rows_where_they_fit():
+    """Stage-3 rows fit whole (two waves per SIMD resident); the chunked staging is
+    used only when asked for (or when whole rows would not keep two per SIMD)."""
+    with env(SFM_SCAN_SPLIT=-1):
+        assert "split=4 chunk=0" in sfm.sfm_scan_plan_string(256, 1, 320, 8, 198, 4, "bf16", 3)
