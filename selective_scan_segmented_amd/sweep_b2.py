@@ -90,18 +90,25 @@ def _time_scan(w, B2: int, steps: int, warmup: int, min_bytes: int = 2 << 30) ->
     return ms * 1000.0
 
 
-def sweep(names, steps=50, warmup=5):
+def sweep(names, steps=50, warmup=5, reps=3):
+    """Per workload, every candidate B2 timed `reps` times, the candidates
+    interleaved within each repetition (so drift of the clock or of the box hits
+    them alike); the median decides, the spread is kept beside it."""
     from selective_scan_segmented_amd import synth
     rows = []
     for name in names:
         w = synth.WORKLOADS[name]
         cands = [b for b in sorted(set(w.B2_list) | {1}) if w.B % b == 0]
-        times = {}
-        for b2 in cands:
-            times[b2] = _time_scan(w, b2, steps, warmup)
-            print(json.dumps({"workload": name, "B2": b2, "us": round(times[b2], 3)}), flush=True)
+        runs = {b2: [] for b2 in cands}
+        for rep in range(reps):
+            for b2 in cands:
+                runs[b2].append(_time_scan(w, b2, steps, warmup))
+                print(json.dumps({"workload": name, "rep": rep, "B2": b2, "us": round(runs[b2][-1], 3)}), flush=True)
+        times = {b2: sorted(v)[len(v) // 2] for b2, v in runs.items()}
+        spread = {b2: (max(v) - min(v)) / times[b2] for b2, v in runs.items()}
         best = min(times, key=times.get)
-        rows.append({"workload": name, "B": w.B, "L": w.L, "D": w.D, "N": w.N, "times_us": times, "best_B2": best,
+        rows.append({"workload": name, "B": w.B, "L": w.L, "D": w.D, "N": w.N, "times_us": times,
+                     "runs_us": runs, "rel_spread": spread, "best_B2": best,
                      "speedup_best_vs_B2_1": times[1] / times[best]})
     return rows
 
@@ -110,7 +117,8 @@ def write_table(rows, path=TABLE):
     lines = ["// b1_table.inc -- adaptive-B1 lookup table: key (B, L, D, N) -> fold ratio B2.",
              "// Written by selective_scan_segmented_amd/sweep_b2.py from timings of",
              "// sfm_selective_scan_fwd_ex (pad + conv + scan + swap, one launch) on MI355X;",
-             "// each entry keeps the fastest B2.  Timings (us per launch) per candidate B2:"]
+             "// each entry keeps the fastest B2 (median of the repetitions).  Timings (us",
+             "// per launch) per candidate B2:"]
     for r in rows:
         t = ", ".join(f"B2={b}: {v:.1f}" for b, v in sorted(r["times_us"].items()))
         lines.append(f"//   {r['workload']} (B={r['B']} L={r['L']} D={r['D']} N={r['N']}): {t}")
@@ -127,12 +135,13 @@ def main():
     ap.add_argument("--workloads", default="stage4,stage3,base_stage3,long")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--write-table", action="store_true")
     ap.add_argument("--json", default="")
     a = ap.parse_args()
-    rows = sweep(a.workloads.split(","), a.steps, a.warmup)
+    rows = sweep(a.workloads.split(","), a.steps, a.warmup, a.reps)
     for r in rows:
-        print(json.dumps({k: v for k, v in r.items() if k != "times_us"}), flush=True)
+        print(json.dumps({k: v for k, v in r.items() if k not in ("times_us", "runs_us")}), flush=True)
     if a.json:
         with open(a.json, "w") as f:
             json.dump(rows, f, indent=1)
