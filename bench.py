@@ -128,8 +128,9 @@ def alg_scan_bytes(w, io_bytes: int, fused_pad: bool) -> int:
 
 def alg_scan_slots(w) -> int:
     """Algorithmic VALU work of the fused conv+scan, in fp32 issue slots:
-    per (token, channel) N exp (quarter rate) and 4N mul/fma for the N states,
-    softplus (exp + log, 6 fp32 ops), K conv FMAs, bias add, Delta*u, D*u."""
+    per (token, channel) N exp (TRANS_SLOTS each) and 4N mul/fma for the N
+    states, softplus (exp + log, TRANS_SLOTS each, and 6 fp32 ops), K conv FMAs,
+    bias add, Delta*u, D*u."""
     per_tc = w.N * (TRANS_SLOTS + 4) + 2 * TRANS_SLOTS + 6 + w.K + 3
     return w.B * w.D * w.L * per_tc
 
@@ -192,8 +193,8 @@ def alg_bwd_slots(w) -> int:
     """Algorithmic VALU work of the backward of the fused conv+scan, in fp32 issue
     slots: one forward (alg_scan_slots) plus the reverse step -- per state the
     gradient carry, dC, dB, du, dDelta and dA terms (10 fp32 ops) and the decay
-    exp (4 slots) -- and per position the softplus and conv derivatives (~20)."""
-    return alg_scan_slots(w) + w.B * w.D * w.L * (w.N * (10 + 4) + 20)
+    exp (TRANS_SLOTS) -- and per position the softplus and conv derivatives (~20)."""
+    return alg_scan_slots(w) + w.B * w.D * w.L * (w.N * (10 + TRANS_SLOTS) + 20)
 
 
 def alg_bwd_bytes(w, io_bytes: int) -> int:
