@@ -63,13 +63,27 @@ def scratch_users(remarks: str):
     return bad
 
 
+def _local_includes(path: str, seen: set) -> None:
+    """Files reached from path through #include "..." (csrc/ and include/), transitively."""
+    if path in seen or not os.path.exists(path):
+        return
+    seen.add(path)
+    with open(path) as f:
+        for m in re.finditer(r'^\s*#\s*include\s+"([^"]+)"', f.read(), re.M):
+            for d in (os.path.dirname(path), CSRC, os.path.join(ROOT, "include")):
+                cand = os.path.join(d, m.group(1))
+                if os.path.exists(cand):
+                    _local_includes(cand, seen)
+                    break
+
+
 def _up_to_date(src: str, obj: str) -> bool:
-    """Object newer than its source and every header (SFM_BUILD_INCREMENTAL=1 only)."""
+    """Object newer than its source and every local header it includes
+    (SFM_BUILD_INCREMENTAL=1 only)."""
     if os.environ.get("SFM_BUILD_INCREMENTAL") != "1" or not os.path.exists(obj):
         return False
-    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                                        if f.endswith((".h", ".inc"))]
-    deps += [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    deps: set = set()
+    _local_includes(os.path.join(CSRC, src), deps)
     t = os.path.getmtime(obj)
     return all(os.path.getmtime(d) < t for d in deps)
 

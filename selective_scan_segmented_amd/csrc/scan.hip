@@ -3,6 +3,7 @@
 #include "scan_kernel.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace sfm {
 
@@ -173,6 +174,102 @@ bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, i
     return true;
 }
 
+// Streaming lane-split plan (split_stream_kernel): one state per lane, 16
+// lanes per channel, four channels per wave, for 9 to 16 states.  Every
+// (sample, channel) row stays on one wave -- no carries -- and nothing is
+// staged whole: x, delta/y and raw B/C move sq positions at a time,
+// double-buffered, so the LDS a workgroup needs does not grow with L.  Each
+// chunk costs a fixed ~2 us (two workgroup barriers, the wait, widening,
+// stores: measured on the long rows as the slope of step time over chunk
+// count), so the chunk is the longest that keeps every workgroup resident in
+// one round and the kernel's precomputed-transfer path (at most 8 transfers
+// per tile and wave); wpg = 4 or 8 waves share one B/C stage.  chunk_hint > 0
+// forces a chunk length (a multiple of 16 up to 256); SFM_SCAN_SPLIT_WPG
+// (diagnostics) forces the waves per workgroup.  Needs rows of whole 4-byte
+// words.
+bool plan_stream(ScanParams& p, int io_bytes, int chunk_hint, int cus) {
+    if (p.N <= 8) return false;
+    const int L = p.L, XL = p.xrow, N = p.N, D = p.D;
+    const int ew = 4 / io_bytes;
+    if (((long long)L * io_bytes) % 4 || ((long long)XL * io_bytes) % 4) return false;
+    if (chunk_hint > 0 && (chunk_hint % 16 || chunk_hint > 256)) return false;
+    constexpr int G = 16, cpw = kWave / G;
+    constexpr int kLdsCap = 160 * 1024, kLdsUnit = 1280, kWavesPerCu = 8;  // two waves per SIMD by registers
+    constexpr int kFast = 8;                                                // see split_stream_kernel
+    const int kw = p.conv_w ? (p.K <= 4 ? 4 : 8) : 4;  // compiled conv window
+    const int tiles = (D + cpw - 1) / cpw;
+    int wpg_hint = 0;
+    if (const char* e = std::getenv("SFM_SCAN_SPLIT_WPG")) wpg_hint = std::atoi(e);
+    struct Cand { int q, wpg, lds, xi, di, bi, xpw, dpw; };
+    auto layout = [&](int q, int wpg, Cand& c) {
+        c.q = q;
+        c.wpg = wpg;
+        c.xpw = odd_words((q + kw - 1) / ew + 2);  // the chunk's taps plus word alignment
+        c.dpw = odd_words((q + ew - 1) / ew);
+        c.xi = (cpw * c.xpw + kWave - 1) / kWave;
+        c.di = (cpw * c.dpw + kWave - 1) / kWave;
+        c.bi = (N * c.dpw + kWave - 1) / kWave;
+        c.lds = q * G * 2 * (int)sizeof(float) + 2 * 2 * c.bi * 256 + wpg * kWave * (int)sizeof(double) +
+                wpg * 2 * (c.xi + c.di) * 256;
+    };
+    Cand best{};
+    long long best_score = -1;
+    const int qmax = (L + G - 1) / G * G;
+    for (int wpg : {4, 8}) {
+        if (wpg_hint > 0 && wpg != wpg_hint) continue;
+        const int w = tiles >= wpg ? wpg : (tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1));
+        const long long grid = (long long)((tiles + w - 1) / w) * p.B1;
+        for (int q = 256; q >= G; q -= G) {
+            if (chunk_hint > 0 && q != chunk_hint) continue;
+            Cand c;
+            layout(std::min(q, qmax), w, c);
+            if (c.lds > kLdsCap) continue;
+            const int per_cu = std::min(kLdsCap / ((c.lds + kLdsUnit - 1) / kLdsUnit * kLdsUnit), kWavesPerCu / w);
+            if (per_cu < 1) continue;
+            const long long rounds = (grid + (long long)cus * per_cu - 1) / ((long long)cus * per_cu);
+            const bool fast = c.xi <= kFast && c.di <= kFast && (c.bi + w - 1) / w <= kFast;
+            // fewest rounds, then the precomputed path, then the longest chunk, then fewer waves per group
+            const long long score = (1000 - std::min(rounds, 999LL)) * 1000000LL + (fast ? 100000 : 0) + c.q * 10 +
+                                    (w == 4 ? 1 : 0);
+            if (score > best_score) {
+                best_score = score;
+                best = c;
+            }
+        }
+    }
+    if (best_score < 0) return false;
+    p.split = G;
+    p.wpg = best.wpg;
+    p.stiles = (tiles + best.wpg - 1) / best.wpg;
+    p.ns = 16;
+    p.tiles = tiles;
+    p.mode = 0;
+    p.ch = best.q;
+    p.waves = 1;
+    p.piece = p.B2 * L;
+    p.need_carry = 0;
+    p.cw = best.wpg;
+    p.tgroups = p.stiles;
+    p.sq = best.q;
+    p.xpw = best.xpw;
+    p.dpw = best.dpw;
+    p.bpw = best.dpw;
+    p.xtile_insts = best.xi;
+    p.dtile_insts = best.di;
+    p.btile_insts = best.bi;
+    p.bc_off = 0;
+    p.braw_off = best.q * G * 2 * (int)sizeof(float);
+    p.mean_off = p.braw_off + 2 * 2 * best.bi * 256;
+    p.slab_off = p.mean_off + best.wpg * kWave * (int)sizeof(double);
+    p.slab_bytes = 2 * (best.xi + best.di) * 256;
+    p.xs_bytes = best.xi * 256;
+    p.ds_bytes = best.di * 256;
+    p.lds_bytes = best.lds;
+    p.stagger_period = 0;
+    p.stagger_ticks = 0;
+    return true;
+}
+
 }  // namespace
 
 
@@ -200,9 +297,12 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     const int cus = device_cus();
     const long long lane_waves = (long long)p.B1 * p.B2 * ((p.D + kWave - 1) / kWave);
     const bool want_split = split_hint > 0 || (split_hint < 0 && lane_waves < 2LL * 4 * cus);
-    if (want_split && waves_hint <= 0 && ch_hint <= 0 &&
-        plan_split(p, io_bytes, split_hint, stagger_hint, split_chunk_hint, cus))
-        return true;
+    if (want_split && waves_hint <= 0 && ch_hint <= 0) {
+        // G = 2 or 4 first (fewer instructions per token); the streaming
+        // kernel where those cannot stage the rows (long rows) or when asked for
+        if (split_hint != 16 && plan_split(p, io_bytes, split_hint, stagger_hint, split_chunk_hint, cus)) return true;
+        if ((split_hint < 0 || split_hint == 16) && plan_stream(p, io_bytes, split_chunk_hint, cus)) return true;
+    }
     const int XL = p.xrow;
     // The fused pad/swap keep each sample inside one wave, except with tile
     // staging (even row lengths), whose pieces take the row mean and write the

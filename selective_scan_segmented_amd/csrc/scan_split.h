@@ -49,12 +49,14 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 
-// DPP quad_perm control that gives every lane the value of lane J of its
-// group of G adjacent lanes.
+// DPP control that gives every lane the value of lane J of its group of G
+// adjacent lanes: quad_perm for groups of 2 and 4, row_newbcast:J (lane J of
+// each 16-lane row) for groups of 16.
 template <int G, int J>
 constexpr int bcast_ctrl() {
     if constexpr (G == 2) return J | (J << 2) | ((2 + J) << 4) | ((2 + J) << 6);
-    else return J * 0x55;
+    else if constexpr (G == 4) return J * 0x55;
+    else return 0x150 + J;
 }
 
 template <int G, int J>
@@ -64,12 +66,38 @@ __device__ __forceinline__ float bcast(float v) {
 }
 
 // Sum over the G adjacent lanes of a group, result in every lane of it
-// (quad_perm [1,0,3,2] then [2,3,0,1]).
+// (quad_perm [1,0,3,2] then [2,3,0,1]; for 16-lane groups then row_half_mirror,
+// which pairs the two quads of each half-row, and row_mirror, which pairs the
+// two halves).
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 16, "lane groups of 1, 2, 4 or 16");
     if constexpr (G >= 2) v += dpp<0xB1>(v);
     if constexpr (G >= 4) v += dpp<0x4E>(v);
+    if constexpr (G >= 16) {
+        v += dpp<0x141>(v);
+        v += dpp<0x140>(v);
+    }
     return v;
+}
+
+// Reduce-scatter over each 16-lane row: p[j] holds this lane's term of sum j;
+// lane i of the row returns the sum over the row's 16 lanes of p[i].  Four
+// butterfly steps whose partners differ in lane bits 0-3, 0-2, 0-1 and 0
+// (row_mirror, row_half_mirror, quad_perm [3,2,1,0] and [1,0,3,2]); at each
+// step a lane keeps the half of its values whose index bit matches its own
+// lane bit and sends the other half, so 8 + 4 + 2 + 1 DPP adds cover all 16
+// sums (against 4 per sum for an all-reduce).  The masks are lane-constant.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int lane) {
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+    float q8[8], q4[4], q2[2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) q8[m] = (b3 ? p[m + 8] : p[m]) + dpp<0x140>(b3 ? p[m] : p[m + 8]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) q4[m] = (b2 ? q8[m + 4] : q8[m]) + dpp<0x141>(b2 ? q8[m] : q8[m + 4]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) q2[m] = (b1 ? q4[m + 2] : q4[m]) + dpp<0x1B>(b1 ? q4[m] : q4[m + 2]);
+    return (b0 ? q2[1] : q2[0]) + dpp<0xB1>(b0 ? q2[0] : q2[1]);
 }
 
 // 4-byte direct global->LDS transfers of a tile: words [0, nw) of rows
@@ -125,7 +153,7 @@ struct SplitWave {
     static constexpr int NPL = NS / G;   // states per lane
     static constexpr int CPW = kWave / G;  // channels per wave
     static constexpr int NB = NPL / 2;   // float4 B/C reads per position ([B..., C...] per lane)
-    static_assert(NPL >= 2 && NPL % 2 == 0, "two or more states per lane");
+    static_assert(NPL == 1 || NPL % 2 == 0, "one or an even number of states per lane");
 
     const ScanParams& p;
     const int lane, c, g, d, rows;
@@ -212,13 +240,20 @@ struct SplitWave {
         const float du = dt * u;
         const float dpu = Dk * u;  // D*u of this lane's own token
         float yown = 0.0f;
+        float pj[NPL == 1 ? G : 1];  // one state per lane: this lane's C*h term of each position
         static_for<G>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
+            if constexpr (NPL == 1) pj[j] = 0.0f;
             if (FIRST || CHECK ? t0 + j < L : true) {
                 const float d2j = bcast<G, j>(d2);
                 const float duj = bcast<G, j>(du);
                 const float4* q4 = reinterpret_cast<const float4*>(bc + ((t0 + j) * G + g) * (2 * NPL));
                 float bv[NPL], cv[NPL];
+                if constexpr (NPL == 1) {
+                    const float2 v = *reinterpret_cast<const float2*>(bc + ((t0 + j) * G + g) * 2);
+                    bv[0] = v.x;
+                    cv[0] = v.y;
+                }
 #pragma unroll
                 for (int k = 0; k < NB; ++k) {
                     const float4 v = q4[k];
@@ -242,14 +277,81 @@ struct SplitWave {
                     }
                     yp = i == 0 ? cv[0] * h[0] : __builtin_fmaf(cv[i], h[i], yp);
                 }
-                yp = group_sum<G>(yp);
-                yown = (g == j) ? yp : yown;
+                if constexpr (NPL == 1) {
+                    pj[j] = yp;
+                } else {
+                    yp = group_sum<G>(yp);
+                    yown = (g == j) ? yp : yown;
+                }
             }
         });
+        if constexpr (NPL == 1) yown = row_reduce_scatter16(pj, lane);
         // (lanes past the tile's last channel work on LDS rows that were not
         // loaded and are not stored)
         yown += dpu;
         if (!CHECK || tau < L) dr[tau] = from_f32<IO>(yown);
+    }
+
+    // One state per lane: the LDS values of an unchecked block, read one block
+    // ahead so that their latency hides behind the previous block's arithmetic
+    // (with one or two waves per SIMD nothing else would hide it).
+    struct Ahead {
+        float2 bcv[G];  // B and C of this lane's state at t0 .. t0 + G - 1
+        IO tap[KW];     // conv taps (or the input itself without conv) of position t0 + g
+        IO dl;          // delta of position t0 + g
+    };
+
+    __device__ __forceinline__ void fetch(int t0, const IO* xr, const IO* dr, const float* bc, Ahead& a) const {
+        const int tau = t0 + g;
+        const int lo = p.pad_in ? 1 : 0;
+        const int P2 = p.P + KW - p.K;
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = 0; j < KW; ++j) a.tap[j] = xr[tau - P2 + j - lo];
+        } else {
+            a.tap[0] = xr[tau - lo];
+        }
+        a.dl = dr[tau];
+#pragma unroll
+        for (int j = 0; j < G; ++j) a.bcv[j] = *reinterpret_cast<const float2*>(bc + ((t0 + j) * G + g) * 2);
+    }
+
+    // The unchecked block of positions [t0, t0 + G) from fetched values; the
+    // same arithmetic as block<false, false>.
+    __device__ __forceinline__ void block_ahead(int t0, IO* dr, const Ahead& a, float (&h)[NPL], float (&win)[KW]) {
+        float u;
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = 0; j < KW; ++j) win[j] = to_f32(a.tap[j]);
+            float acc = cb;
+#pragma unroll
+            for (int j = 0; j < KW; ++j) acc = __builtin_fmaf(cw[j], win[j], acc);
+            u = SILU ? silu(acc) : acc;
+        } else {
+            u = to_f32(a.tap[0]);
+        }
+        const float dl = to_f32(a.dl) + dbias;
+        float d2, dt;
+        if constexpr (SP) {
+            d2 = softplus_log2e(dl);
+            dt = d2 * kLn2;
+        } else {
+            dt = dl;
+            d2 = dl * kLog2e;
+        }
+        const float du = dt * u;
+        const float dpu = Dk * u;
+        float pj[G];
+        static_for<G>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const float d2j = bcast<G, j>(d2);
+            const float duj = bcast<G, j>(du);
+            const float bx = duj * a.bcv[j].x;
+            const float e = exp2_fast(d2j * A2[0]);
+            h[0] = __builtin_fmaf(e, h[0], bx);
+            pj[j] = a.bcv[j].y * h[0];
+        });
+        dr[t0 + g] = from_f32<IO>(row_reduce_scatter16(pj, lane) + dpu);
     }
 
     // Blocks of a sample that need no checks, [kA, kB): every position < L and
@@ -293,11 +395,31 @@ struct SplitWave {
         }
         for (; k < kA && k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
         const int ke = min(kB, k1);
-        for (; k + 1 < ke; k += 2) {  // two blocks per trip: LDS offsets become immediates
-            block<false, false>(k * G, xr, dr, bc, h, win);
-            block<false, false>(k * G + G, xr, dr, bc, h, win);
+        if constexpr (NPL == 1) {
+            if (k < ke) {
+                // software-pipelined: block k + 1's LDS reads go out before block k computes
+                Ahead a0, a1;
+                fetch(k * G, xr, dr, bc, a0);
+                for (; k + 1 < ke; k += 2) {
+                    fetch((k + 1) * G, xr, dr, bc, a1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    block_ahead(k * G, dr, a0, h, win);
+                    fetch(min(k + 2, ke - 1) * G, xr, dr, bc, a0);  // (a re-read of block k + 1 on the last trip)
+                    __builtin_amdgcn_sched_barrier(0);
+                    block_ahead((k + 1) * G, dr, a1, h, win);
+                }
+                if (k < ke) {
+                    block_ahead(k * G, dr, a0, h, win);
+                    ++k;
+                }
+            }
+        } else {
+            for (; k + 1 < ke; k += 2) {  // two blocks per trip: LDS offsets become immediates
+                block<false, false>(k * G, xr, dr, bc, h, win);
+                block<false, false>(k * G + G, xr, dr, bc, h, win);
+            }
+            for (; k < ke; ++k) block<false, false>(k * G, xr, dr, bc, h, win);
         }
-        for (; k < ke; ++k) block<false, false>(k * G, xr, dr, bc, h, win);
         for (; k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
     }
 
@@ -615,9 +737,283 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_chunk_kernel(ScanParams
     (void)NPL;
 }
 
+// Streaming variant for long rows (one state per lane, G = NS = 16): nothing
+// is staged whole.  The wave's x rows (with the conv halo), its delta/y rows
+// and the sample's raw B/C rows move sq positions at a time by 4-byte
+// transfers into odd-pitch LDS tiles, in two stages: chunk i + 1's transfers
+// go out as soon as chunk i has landed and been widened, so they fly while
+// chunk i computes, and chunk i's y leaves from its tile at the start of chunk
+// i + 1 (after that chunk's wait, so no wait ever covers a fresh store).  The
+// chunks of the B2 samples of a folded row form one stream.  The interior
+// chunks of a sample all have the same tile shapes, so their per-lane transfer
+// and store offsets are computed once; the first and last chunk of a sample
+// (clamped halo, ragged end, swapped ends) take the general path.  With the
+// fused pad the row mean is taken first, straight from HBM: the 16 lanes of a
+// channel each add a contiguous piece of the row in float64, in index order,
+// and the 16 piece sums are added in piece order (the index-order sum whenever
+// the float64 sums are exact, as they are for bf16 rows whose magnitudes span
+// less than 2^33).
+constexpr int kFastInsts = 8;  // transfers (or y stores) per tile on the precomputed path
+
+template <typename IO, int NS, int G, int KW, bool CONV, bool SP, bool SILU>
+__global__ __launch_bounds__(kWave * kMaxWpg) void split_stream_kernel(ScanParams p) {
+    using W = SplitWave<IO, NS, G, KW, CONV, SP, SILU>;
+    constexpr int NPL = W::NPL;
+    constexpr int CPW = W::CPW;
+    constexpr int ew = 4 / (int)sizeof(IO);  // elements per 4-byte word
+    static_assert(NPL == 1 && G == 16, "one state per lane, 16 lanes per channel");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int NGRP = p.stiles * p.B1;
+    int gi = blockIdx.x;
+    if ((NGRP & 7) == 0) gi = (gi & 7) * (NGRP >> 3) + (gi >> 3);
+    const int b1 = gi / p.stiles;
+    const int tile = gi - b1 * p.stiles;
+    const int dw0 = (tile * p.wpg + wave) * CPW;
+    W w(p, lane, dw0);
+    const int L = p.L, XL = p.xrow, N = p.N, D = p.D, Q = p.sq;
+    const int lo = p.pad_in ? 1 : 0;
+    const int P2 = p.P + KW - p.K;  // pad_left of the KW-tap window
+    const uint32_t rowb = (uint32_t)L * sizeof(IO), xrowb = (uint32_t)XL * sizeof(IO);
+    float* bc = reinterpret_cast<float*>(smem + p.bc_off);  // [Q][G][B, C] float32
+    char* braw = smem + p.braw_off;                          // 2 stages x (B tile, C tile)
+    const int btb = p.btile_insts * 256;
+    double* part = reinterpret_cast<double*>(smem + p.mean_off) + wave * kWave;  // float64 piece sums
+    char* slab = smem + p.slab_off + (size_t)wave * p.slab_bytes;                // 2 stages x (x tile, delta tile)
+    const int xtb = p.xtile_insts * 256, dtb = p.dtile_insts * 256;
+    const int rows = w.rows;
+    const int nthr = p.wpg * kWave;
+    const int tid = threadIdx.x;
+    const int nch = (L + Q - 1) / Q;
+    const int total = p.B2 * nch;
+    // the B/C transfers of a chunk, split into contiguous per-wave ranges
+    const int bper = (p.btile_insts + p.wpg - 1) / p.wpg;
+    const int bk0 = min(p.btile_insts, wave * bper), bk1 = min(p.btile_insts, bk0 + bper);
+
+    // first 4-byte word of x staged for the chunk at t0 (its oldest conv tap)
+    auto xw0 = [&](int t0) __attribute__((always_inline)) { return max(0, t0 - P2 - lo) / ew; };
+    auto xnw_of = [&](int t0) __attribute__((always_inline)) {
+        const int iend = min(XL, t0 + Q - P2 + KW - 1 - lo);  // one past the newest tap (unpadded)
+        return (iend + ew - 1) / ew - xw0(t0);
+    };
+    // Interior chunks (0 < c < nch - 1 whose conv taps do not reach the row
+    // end): the same tile shapes every time.
+    const bool fast = nch > 2 && p.xtile_insts <= kFastInsts && p.dtile_insts <= kFastInsts && bper <= kFastInsts;
+    auto interior = [&](int c) __attribute__((always_inline)) {
+        return fast && c > 0 && c + 1 < nch && c * Q + Q - P2 + KW - 1 - lo <= XL;
+    };
+    uint32_t xo[kFastInsts], dof[kFastInsts], bo[kFastInsts], yo[kFastInsts];
+    if (fast) {
+        const int xnw = xnw_of(Q), dnw = Q / ew;
+        const float ix = 1.0f / (float)p.xpw, id = 1.0f / (float)p.dpw;
+        const uint32_t xmax = (uint32_t)(max(rows, 1) - 1) * xrowb + (uint32_t)(xnw - 1) * 4u;
+        const uint32_t dmax = (uint32_t)(max(rows, 1) - 1) * rowb + (uint32_t)(dnw - 1) * 4u;
+        const uint32_t bmax = (uint32_t)(N - 1) * rowb + (uint32_t)(dnw - 1) * 4u;
+#pragma unroll
+        for (int k = 0; k < kFastInsts; ++k) {
+            const int e = k * kWave + lane;
+            int r = div_small(e, ix), wd = e - r * p.xpw;
+            xo[k] = min((uint32_t)r * xrowb + (uint32_t)min(wd, xnw - 1) * 4u, xmax);
+            r = div_small(e, id);
+            wd = e - r * p.dpw;
+            dof[k] = min((uint32_t)r * rowb + (uint32_t)min(wd, dnw - 1) * 4u, dmax);
+            // y: word wd of tile row r goes to row r of y (0xffffffff: a slot past the rows or the chunk)
+            yo[k] = (r < rows && wd < dnw) ? (uint32_t)r * rowb + (uint32_t)wd * 4u : 0xffffffffu;
+            const int eb = (bk0 + k) * kWave + lane;
+            const int rb = div_small(eb, id), wb = eb - rb * p.dpw;
+            bo[k] = min((uint32_t)rb * rowb + (uint32_t)min(wb, dnw - 1) * 4u, bmax);
+        }
+    }
+
+    auto issue = [&](int idx) __attribute__((always_inline)) {
+        const int j = idx / nch, c = idx - j * nch;
+        const int b = b1 * p.B2 + j;
+        const int t0 = c * Q, len = min(Q, L - t0);
+        char* st = slab + (idx & 1) * (xtb + dtb);
+        char* bt = braw + (idx & 1) * 2 * btb;
+        const char* xg = reinterpret_cast<const char*>(static_cast<const IO*>(p.u) + ((size_t)b * D + dw0) * XL) +
+                         (size_t)xw0(t0) * 4;
+        const char* dg = reinterpret_cast<const char*>(static_cast<const IO*>(p.delta) + ((size_t)b * D + dw0) * L + t0);
+        const char* bg = reinterpret_cast<const char*>(static_cast<const IO*>(p.Bm) + ((size_t)b * N) * L + t0);
+        const char* cg = reinterpret_cast<const char*>(static_cast<const IO*>(p.Cm) + ((size_t)b * N) * L + t0);
+        if (interior(c)) {
+            // one LDS base per tile, the instruction offsets as immediates
+            static_for<kFastInsts>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if (rows > 0 && k < p.xtile_insts) dma_at<4, 256 * k>(xg + xo[k], st);
+            });
+            static_for<kFastInsts>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if (rows > 0 && k < p.dtile_insts) dma_at<4, 256 * k>(dg + dof[k], st + xtb);
+            });
+            char* bl = bt + bk0 * 256;
+            static_for<kFastInsts>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if (k < bk1 - bk0) dma_at<4, 256 * k>(bg + bo[k], bl);
+            });
+            static_for<kFastInsts>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if (k < bk1 - bk0) dma_at<4, 256 * k>(cg + bo[k], bl + btb);
+            });
+            return;
+        }
+        if (rows > 0) {
+            dma_tile4(xg, xrowb, rows, xnw_of(t0), p.xpw, st, lane, p.xtile_insts);
+            dma_tile4(dg, rowb, rows, (len + ew - 1) / ew, p.dpw, st + xtb, lane, p.dtile_insts);
+        }
+        const int nw = (len + ew - 1) / ew;
+        dma_tile4(bg, rowb, N, nw, p.bpw, bt, lane, p.btile_insts, wave, p.wpg);
+        dma_tile4(cg, rowb, N, nw, p.bpw, bt + btb, lane, p.btile_insts, p.wpg - 1 - wave, p.wpg);
+    };
+    IO y0 = Io<IO>::zero();  // fused swap: y at t = 0 of this lane's row, written with the sample's last chunk
+    auto store_y = [&](int idx) __attribute__((always_inline)) {
+        if (rows <= 0) return;
+        const int j = idx / nch, c = idx - j * nch;
+        const int b = b1 * p.B2 + j;
+        const int t0 = c * Q, len = min(Q, L - t0);
+        const char* dtile = slab + (idx & 1) * (xtb + dtb) + xtb;
+        IO* yg = static_cast<IO*>(p.y) + ((size_t)b * D + dw0) * L;
+        const uint32_t* tw = reinterpret_cast<const uint32_t*>(dtile);
+        if (interior(c)) {
+            char* yc = reinterpret_cast<char*>(yg + t0);
+            static_for<kFastInsts>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if (k < p.dtile_insts && yo[k] != 0xffffffffu)
+                    *reinterpret_cast<uint32_t*>(yc + yo[k]) = tw[k * kWave + lane];
+            });
+            return;
+        }
+        const bool sw = p.swap_out && L > 1;
+        const int nw = (len + ew - 1) / ew;
+        const int wlo = (sw && t0 == 0) ? 1 : 0;
+        const int whi = (sw && t0 + len == L) ? nw - 1 : nw;
+        const float inv = 1.0f / (float)p.dpw;
+        for (int k = 0; k < p.dtile_insts; ++k) {
+            const int e = k * kWave + lane;
+            const int r = div_small(e, inv), wd = e - r * p.dpw;
+            if (r < rows && wd >= wlo && wd < whi) reinterpret_cast<uint32_t*>(yg + (size_t)r * L + t0)[wd] = tw[e];
+        }
+        if (sw && w.g == 0 && w.c < rows) {
+            const IO* drow = reinterpret_cast<const IO*>(dtile) + w.c * p.dpw * ew;
+            IO* yr = yg + (size_t)w.c * L;
+            if (t0 == 0) {
+                y0 = drow[0];
+                for (int q = 1; q < min(ew, len); ++q) yr[q] = drow[q];
+            }
+            if (t0 + len == L) {
+                const int lw = (nw - 1) * ew;  // first position of the last word, relative to t0
+                for (int q = max(lw, t0 == 0 ? ew : 0); q < len - 1; ++q) yr[t0 + q] = drow[q];
+                yr[0] = drow[L - 1 - t0];
+                yr[L - 1] = y0;
+            }
+        }
+    };
+    // raw B/C words -> float32 [q][n][B, C]; thread -> (state n, word) without divisions
+    auto widen = [&](int idx, int len) __attribute__((always_inline)) {
+        const char* bt = braw + (idx & 1) * 2 * btb;
+        const uint32_t* bb = reinterpret_cast<const uint32_t*>(bt);
+        const uint32_t* cc = reinterpret_cast<const uint32_t*>(bt + btb);
+        const int nwd = (len + ew - 1) / ew;
+        const int n = tid & (G - 1);
+        if (n < N) {
+            for (int wd = tid / G; wd < nwd; wd += nthr / G) {
+                const uint32_t vb = bb[n * p.bpw + wd], vc = cc[n * p.bpw + wd];
+                if constexpr (ew == 2) {
+                    const int q = 2 * wd;
+                    *reinterpret_cast<float2*>(bc + (q * G + n) * 2) =
+                        float2{__builtin_bit_cast(float, vb << 16), __builtin_bit_cast(float, vc << 16)};
+                    *reinterpret_cast<float2*>(bc + ((q + 1) * G + n) * 2) =
+                        float2{__builtin_bit_cast(float, vb & 0xffff0000u), __builtin_bit_cast(float, vc & 0xffff0000u)};
+                } else {
+                    *reinterpret_cast<float2*>(bc + (wd * G + n) * 2) =
+                        float2{__builtin_bit_cast(float, vb), __builtin_bit_cast(float, vc)};
+                }
+            }
+        }
+    };
+    // Row mean of sample b for this lane's channel (fused pad), see above.
+    auto row_mean = [&](int b) __attribute__((always_inline)) {
+        double acc = 0.0;
+        if (w.c < rows) {
+            const int piece = ((XL + G - 1) / G + 7) & ~7;
+            const int i0 = min(XL, w.g * piece), i1 = min(XL, i0 + piece);
+            const IO* r = static_cast<const IO*>(p.u) + ((size_t)b * D + w.d) * XL;
+            int i = i0;
+            // rows of whole 16-byte units: sixteen units in flight per batch
+            // (a piece starts on a unit: its length is a multiple of 8 elements)
+            constexpr int EU = 16 / (int)sizeof(IO);
+            if (((size_t)XL * sizeof(IO)) % 16 == 0) {
+                for (; i + 16 * EU <= i1; i += 16 * EU) {
+                    uint4 v[16];
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) v[k] = reinterpret_cast<const uint4*>(r + i)[k];
+                    const IO* e = reinterpret_cast<const IO*>(v);
+#pragma unroll
+                    for (int k = 0; k < 16 * EU; ++k) acc += (double)to_f32(e[k]);
+                }
+                for (; i + EU <= i1; i += EU) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(r + i);
+                    const IO* e = reinterpret_cast<const IO*>(&v);
+#pragma unroll
+                    for (int k = 0; k < EU; ++k) acc += (double)to_f32(e[k]);
+                }
+            }
+            for (; i < i1; ++i) acc += (double)to_f32(r[i]);
+        }
+        part[lane] = acc;
+        wave_lds_sync();
+        double s = 0.0;
+#pragma unroll
+        for (int k = 0; k < G; ++k) s += part[w.c * G + k];
+        wave_lds_sync();  // the piece sums are read before the next sample's overwrite them
+        return w.c < rows ? to_f32(Io<IO>::from_f64(s / (double)XL)) : 0.0f;
+    };
+
+    issue(0);
+    w.load_params();
+    // states n >= N: B = C = 0 for the whole launch (widening never writes them)
+    if (N < NS) {
+        for (int e = tid; e < Q * NS; e += nthr) {
+            const int q = e / NS, n = e - q * NS;
+            if (n >= N) *reinterpret_cast<float2*>(bc + (q * G + n) * 2) = float2{0.0f, 0.0f};
+        }
+    }
+    int kA, kB, nblk;
+    w.bounds(kA, kB, nblk);
+    float h[NPL];
+    float win[KW];
+    for (int idx = 0; idx < total; ++idx) {
+        const int j = idx / nch, c = idx - j * nch;
+        const int t0 = c * Q, len = min(Q, L - t0);
+        if (c == 0 && p.pad_in) w.mean = row_mean(b1 * p.B2 + j);
+        wait_vmem();
+        __syncthreads();  // chunk idx has landed for every wave; chunk idx - 1 is done in every wave
+        if (idx > 0) store_y(idx - 1);
+        widen(idx, len);
+        __syncthreads();  // B/C of the chunk visible to the group; its raw tiles free again
+        if (idx + 1 < total) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's reads of the other stage are done
+            issue(idx + 1);
+        }
+        const char* st = slab + (idx & 1) * (xtb + dtb);
+        const IO* xr = reinterpret_cast<const IO*>(st) + w.c * p.xpw * ew - xw0(t0) * ew;
+        IO* dr = reinterpret_cast<IO*>(const_cast<char*>(st) + xtb) + w.c * p.dpw * ew - t0;
+        if (c == 0) w.start(xr, h, win);
+        const int k0 = t0 / G;
+        const int k1 = c + 1 == nch ? nblk : (t0 + len) / G;
+        w.blocks(k0, k1, kA, kB, xr, dr, bc - t0 * G * 2, h, win);
+    }
+    wave_lds_sync();
+    store_y(total - 1);
+    (void)NPL;
+}
+
 template <typename IO, int NS, int G, int KW, bool CONV, bool SP, bool SILU>
 hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
-    auto kern = p.sq > 0 ? split_chunk_kernel<IO, NS, G, KW, CONV, SP, SILU> : split_kernel<IO, NS, G, KW, CONV, SP, SILU>;
+    void (*kern)(ScanParams);
+    if constexpr (G == NS) kern = split_stream_kernel<IO, NS, G, KW, CONV, SP, SILU>;
+    else kern = p.sq > 0 ? split_chunk_kernel<IO, NS, G, KW, CONV, SP, SILU> : split_kernel<IO, NS, G, KW, CONV, SP, SILU>;
     static bool attr_set[2] = {false, false};
     if (!attr_set[p.sq > 0] && p.lds_bytes > 64 * 1024) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -651,12 +1047,22 @@ hipError_t launch_g(const ScanParams& p, hipStream_t s) {
 
 // One translation unit per (io type, state count):
 // SFM_SPLIT_INSTANCE(__bf16, bf16, 8, 2, 4) defines sfm::launch_split_bf16_n8
-// for lane groups of 2 and 4.
+// for lane groups of 2 and 4; SFM_SPLIT_INSTANCE3 adds a third group size
+// (16, the streaming kernel, with 16 states).
 #define SFM_SPLIT_INSTANCE(IOT, NAME, NSV, GA, GB)                                             \
     namespace sfm {                                                                           \
     hipError_t launch_split_##NAME##_n##NSV(const ScanParams& p, hipStream_t s) {             \
         if (p.split == GA) return split_detail::launch_g<IOT, NSV, GA>(p, s);                 \
         if (p.split == GB) return split_detail::launch_g<IOT, NSV, GB>(p, s);                 \
+        return hipErrorInvalidValue;                                                          \
+    }                                                                                         \
+    }
+#define SFM_SPLIT_INSTANCE3(IOT, NAME, NSV, GA, GB, GC)                                        \
+    namespace sfm {                                                                           \
+    hipError_t launch_split_##NAME##_n##NSV(const ScanParams& p, hipStream_t s) {             \
+        if (p.split == GA) return split_detail::launch_g<IOT, NSV, GA>(p, s);                 \
+        if (p.split == GB) return split_detail::launch_g<IOT, NSV, GB>(p, s);                 \
+        if (p.split == GC) return split_detail::launch_g<IOT, NSV, GC>(p, s);                 \
         return hipErrorInvalidValue;                                                          \
     }                                                                                         \
     }

@@ -143,13 +143,15 @@ static sfm_status fwd_check(const void* u, const void* delta, const float* A, co
 }
 
 // SFM_SCAN_SPLIT (diagnostics): 0 keeps the one-lane-per-channel kernel, 2 or
-// 4 asks for that many lanes per channel, unset lets the planner choose.
+// 4 asks for that many lanes per channel, 16 for the streaming kernel (one
+// state per lane), unset lets the planner choose.
 static int split_hint_env() {
     if (const char* e = std::getenv("SFM_SCAN_SPLIT")) return std::atoi(e);
     return -1;
 }
 // SFM_SCAN_SPLIT_CHUNK (diagnostics): 0 keeps the lane-split kernel's whole-row
-// staging, q > 0 asks for its chunked staging with q positions per chunk.
+// staging, q > 0 asks for its chunked staging with q positions per chunk (for
+// the streaming kernel: its chunk length, a multiple of 16 up to 256).
 static int split_chunk_hint_env() {
     if (const char* e = std::getenv("SFM_SCAN_SPLIT_CHUNK")) return std::atoi(e);
     return -1;

@@ -57,6 +57,9 @@ struct ScanParams {
     // raw B/C of sq positions at a time by 4-byte transfers into LDS rows of
     // dpw / bpw words (odd pitches), dtile_insts / btile_insts transfers each.
     int sq, dpw, bpw, dtile_insts, btile_insts;
+    // Streaming lane-split kernel (split = 16, one state per lane): x tiles too,
+    // xpw words per row, xtile_insts transfers, every tile in two stages.
+    int xpw, xtile_insts;
 };
 
 // Fills the plan fields; waves_hint / ch_hint <= 0 select automatically,
