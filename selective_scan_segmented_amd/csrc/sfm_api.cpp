@@ -548,12 +548,40 @@ extern "C" sfm_status sfm_selective_scan_bwd(
     return hip_status(sfm::launch_bwd(p, io_dtype, static_cast<hipStream_t>(stream)), who);
 }
 
+// True when the regular forward plans these rows for the streaming lane-split
+// kernel (long rows of 9 to 16 states), which runs them faster than the
+// split-row scheme and needs no workspace (the long rows: 236 vs 500 us).
+static bool regular_plan_streams(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L, int conv_k, int eb,
+                                 int flags) {
+    static const float dummy = 0.0f;
+    sfm::ScanParams p{};
+    p.conv_w = conv_k ? &dummy : nullptr;
+    p.B1 = (int)B1;
+    p.B2 = (int)B2;
+    p.D = (int)D;
+    p.N = (int)N;
+    p.L = (int)L;
+    p.K = conv_k ? conv_k : 1;
+    p.pad_in = (flags & SFM_FUSE_PAD) ? 1 : 0;
+    p.swap_out = (flags & SFM_FUSE_SWAP) ? 1 : 0;
+    p.xrow = p.pad_in ? (int)L - 2 : (int)L;
+    int waves_hint = 0, ch_hint = 0;
+    if (const char* e = std::getenv("SFM_SCAN_WAVES")) waves_hint = std::atoi(e);
+    if (const char* e = std::getenv("SFM_SCAN_CHUNK")) ch_hint = std::atoi(e);
+    return sfm::plan_scan(p, eb, waves_hint, ch_hint, -1, 0, split_hint_env(), split_chunk_hint_env()) &&
+           p.split == 16;
+}
+
 // Split-row forward plan (p.seg > 1) or none: channel-last rows, rows that the
-// chunked planner does not split, or no plan -> the regular forward.
+// chunked planner does not split, rows the regular forward streams (unless
+// SFM_BWD_SEGMENTS forces a split, for diagnostics), or no plan -> the regular
+// forward.
 static bool fwd_split_plan(sfm::BwdParams& p, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
                            const float* conv_w, int conv_k, int conv_pad_left, int conv_act, int delta_softplus,
                            int flags, int eb, size_t* need) {
     if (flags & SFM_LAYOUT_BLD) return false;
+    if (!std::getenv("SFM_BWD_SEGMENTS") && regular_plan_streams(B1, B2, D, N, L, conv_w ? conv_k : 0, eb, flags))
+        return false;
     fill_bwd(p, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, flags);
     p.fwd = 1;
     p.swap_out = (flags & SFM_FUSE_SWAP) ? 1 : 0;

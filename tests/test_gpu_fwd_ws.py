@@ -83,8 +83,28 @@ def test_fwd_ws_folded_rows_f32(monkeypatch):
 
 
 def test_fwd_ws_long_rows_bf16():
-    """The long workload's shape (L = 4002, N = 16) with the default split, two samples."""
-    run(2, 128, 16, 4000, 4, 1, 0, 3, "bf16", seed=17)
+    """Long rows (L = 4002) of 8 states, which only the split-row scheme spreads
+    over the GPU, with the default split, two samples."""
+    run(2, 128, 8, 4000, 4, 1, 0, 3, "bf16", seed=17)
+
+
+def test_fwd_ws_streamed_rows_take_the_regular_forward():
+    """Long rows of 16 states (the long workload's shape, two samples): the regular
+    forward streams them faster than the split-row scheme, so the workspace entry
+    point needs no workspace and gives the regular forward's bits."""
+    import torch
+    B, D, N, T = 2, 128, 16, 4000
+    assert sfm.sfm_selective_scan_fwd_ws_size(B, 1, D, N, T + 2, 4, "bf16", 3) == 0
+    assert "split=16" in sfm.sfm_scan_plan_string(B, 1, D, N, T + 2, 4, "bf16", 3)
+    w = synth.Workload("fws", B=B, D=D, N=N, T=T, io="bf16", B2_list=(1,), K=4)
+    li = synth.make_layer(w, seed=19)
+    args = (to_dev(li.x), to_dev(li.delta), torch.from_numpy(li.A).cuda(), to_dev(li.Bm), to_dev(li.Cm),
+            torch.from_numpy(li.Dskip).cuda(), torch.from_numpy(li.delta_bias).cuda())
+    kw = dict(conv_w=torch.from_numpy(li.conv_w).cuda(), conv_pad_left=1, flags=3)
+    a = sfm.sfm_selective_scan_fwd_ws(*args, **kw)
+    b = sfm.sfm_selective_scan_fwd_ex(*args, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(a), from_dev(b))
 
 
 def test_fwd_ws_falls_back_without_split():

@@ -35,7 +35,7 @@ def layer(B, D, N, T, io, seed):
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_noalloc_matches_fwd_ws_on_two_calls(io):
     import torch
-    for B, D, N, T in [(4, 128, 16, 4000), (2, 64, 8, 2000)]:  # the second call is smaller
+    for B, D, N, T in [(4, 128, 8, 4000), (2, 64, 8, 2000)]:  # the second call is smaller
         need = sfm.sfm_selective_scan_fwd_ws_size(B, 1, D, N, T + 2, 4, io, 3)
         say(f"noalloc B={B} D={D} N={N} T={T} io={io} scratch={need}")
         assert 0 < need <= sfm.SFM_NOALLOC_SCRATCH_BYTES
