@@ -333,10 +333,11 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets; 0 = enough for 2 GiB")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["step", "copy", "scan", "bwd", "block"], default="step",
+    ap.add_argument("--mode", choices=["step", "copy", "scan", "bwd", "block", "aux"], default="step",
                     help="step: the whole hot path (default); scan: the scan launch alone; "
                          "bwd: the backward of the fused step (one sfm_selective_scan_bwd call); "
                          "block: a random-weight mixer block around the channel-last scan, per fold ratio; "
+                         "aux: the standalone boundary-masked conv, aux pad and aux swap launches; "
                          "copy: a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as three launches (pad, conv+scan, swap) instead of one")
@@ -388,6 +389,9 @@ def main():
         return
 
     w = synth.WORKLOADS[a.workload]
+    if a.mode == "aux":
+        run_aux(a, w, hip, sp, dev)
+        return
     if a.mode == "block":
         run_block(a, w, hip, sp, dev)
         return
@@ -440,6 +444,81 @@ def main():
         del ctx3
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ctx.li, a.cpu_seconds)
+    print(json.dumps(out))
+
+
+def run_aux(a, w, hip, sp, dev):
+    """Time the standalone launches of the hot path's HBM-bound steps on one
+    workload's shapes: the boundary-masked depthwise conv over folded rows
+    (sfm_dwconv1d_fold, at the workload's fold ratio), the aux pad and the aux
+    swap (in place and out of place).  Inputs rotate over >= 2 GiB of sets, HIP
+    events bracket K back-to-back launches of each op.  Algorithmic bytes:
+    conv B*D*L read + B*D*L written; pad B*D*T read + B*D*L written; swap copy
+    B*D*L each way; swap in place the two end tokens of every row, read and
+    written (its rate is reported against the 128-byte lines it must touch)."""
+    import numpy as np
+    import torch
+    import selective_scan_segmented_amd as sfm
+    from selective_scan_segmented_amd import synth
+    lib = sfm.load_library()
+    io = 0 if w.io == "f32" else 1
+    eb = 4 if w.io == "f32" else 2
+    li = synth.make_layer(w, seed=synth.WORKLOAD_ORDER.index(w.name))
+    b2 = w.B // sfm.sfm_pick_b1(w.B, w.L, w.D, w.N) if a.b2 == 0 else a.b2
+
+    def dev_io(arr):
+        if arr.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+    rng = np.random.default_rng(11)
+    xl = rng.standard_normal((w.B, w.D, w.L)).astype(np.float32)
+    base = {"xt": dev_io(li.x), "xl": dev_io(synth.f32_to_bf16_bits(xl) if io else xl)}
+    cw = torch.from_numpy(li.conv_w).to(dev)
+    set_bytes = (w.B * w.D * (w.T + 2 * w.L)) * eb
+    nsets = a.sets if a.sets > 0 else max(2, math.ceil((2 << 30) / set_bytes))
+    sets = []
+    for _ in range(nsets):
+        st = {k: v.clone() for k, v in base.items()}
+        st["out"] = torch.empty_like(st["xl"])
+        sets.append(st)
+    torch.cuda.synchronize()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    K, W = a.steps, a.warmup
+    ops = {
+        "conv": (lib.sfm_dwconv1d_fold,
+                 [(vp(st["xl"]), vp(cw), None, vp(st["out"]), w.B // b2, b2, w.D, w.L, w.K, 1, 0, io, sp)
+                  for st in sets], 2 * w.B * w.D * w.L * eb),
+        "pad": (lib.sfm_aux_pad_swap, [(vp(st["xt"]), vp(st["out"]), w.B, w.D, w.T, 0, io, sp) for st in sets],
+                w.B * w.D * (w.T + w.L) * eb),
+        "swap_copy": (lib.sfm_aux_pad_swap,
+                      [(vp(st["xl"]), vp(st["out"]), w.B, w.D, w.T, 1, io, sp) for st in sets],
+                      2 * w.B * w.D * w.L * eb),
+        "swap_inplace": (lib.sfm_aux_pad_swap,
+                         [(vp(st["out"]), vp(st["out"]), w.B, w.D, w.T, 1, io, sp) for st in sets],
+                         4 * w.B * w.D * eb),
+    }
+    copy = copy_rate(hip, sp, dev)
+    out = {"mode": "aux", "workload": f"{w.name}: B={w.B} D={w.D} L={w.L} K={w.K}", "B2": b2, "dtype": w.io,
+           "input_sets": nsets, "steps": K, "copy_GBps": round(copy, 1)}
+    for name, (fn, args, alg) in ops.items():
+        for i in range(W):
+            rc = fn(*args[i % nsets])
+            if rc:
+                raise SystemExit(f"{name}: status {rc}")
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sp)
+        for i in range(K):
+            fn(*args[i % nsets])
+        hip.record(e1, sp)
+        ms = hip.elapsed_ms(e0, e1) / K
+        rec = {"ms": round(ms, 5), "alg_bytes": alg, "GBps": round(alg / ms / 1e6, 1),
+               "frac_of_8TBps": round(alg / ms / 1e6 / HBM_PEAK_GBPS, 4),
+               "frac_of_copy": round(alg / ms / 1e6 / copy, 4)}
+        if name == "swap_inplace":
+            lines = 2 * w.B * w.D * 128 * 2  # two 128-byte lines per row, read and written
+            rec["line_GBps"] = round(lines / ms / 1e6, 1)
+        out[name] = rec
     print(json.dumps(out))
 
 
