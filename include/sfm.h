@@ -250,11 +250,14 @@ sfm_status sfm_dwconv1d_fold(const void* x, const float* w, const float* bias, v
  * flags & SFM_LAYOUT_BLD: channel-last, as the forward: u, delta, dy, du,
  *   ddelta [B1*B2, L, D] (u [B1*B2, L-2, D] with SFM_FUSE_PAD), Bm, Cm, dBm, dCm
  *   [B1*B2, L, N]; D times the io element size must be a multiple of 16 bytes
- *   (else SHAPE), and each sample must fit the whole-sample kernel's LDS (else
- *   UNSUPPORTED).
+ *   (else SHAPE).  Samples that fit the whole-sample kernel's LDS run it in the
+ *   channel-last layout; longer ones run the channel-first chunked backward on
+ *   transposed copies that the workspace then also holds (x, delta, dy, B, C
+ *   in, du, ddelta, dB, dC out), with the results transposed back -- the same
+ *   bits as a channel-first call on the transposed tensors.
  * Two kernels: when every [rows][length] block of a sample and 64-channel tile
  * is a whole number of 16-byte units on 16-byte boundaries and fits in LDS,
- * each sample is staged once; otherwise chunk by chunk (channel-first only).
+ * each sample is staged once; otherwise chunk by chunk.
  * The chunked kernel splits rows along L when samples times tiles give fewer
  * than 1024 waves: segments of at least 64 positions, one wave each, after a
  * carry pass (per segment: the state reached from zero, the output gradient

@@ -464,6 +464,47 @@ void fill_bwd(sfm::BwdParams& p, int64_t B1, int64_t B2, int64_t D, int64_t N, i
     p.xrow = p.pad_in ? (int)L - 2 : (int)L;
 }
 
+// Channel-last rows that the whole-sample kernel cannot stage (too long for
+// its LDS): the backward runs channel-first on transposed copies.  The
+// workspace holds the channel-first plan's own workspace, then x, delta, dy, B
+// and C transposed to [B, D, *] / [B, N, L], then du, ddelta (io) and dB, dC
+// (float32) in the channel-first layout, which are transposed back into the
+// caller's tensors.  Offsets in bytes, each region on 256 bytes.
+struct ClAdapter {
+    size_t xT, dT, dyT, bT, cT, duT, ddT, dbT, dcT, total;
+};
+
+bool plan_cl_adapter(sfm::BwdParams& q, int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
+                     const float* conv_w, int conv_k, int conv_pad_left, int conv_act, int delta_softplus, int flags,
+                     int eb, ClAdapter& a) {
+    fill_bwd(q, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, flags & ~SFM_LAYOUT_BLD);
+    size_t ws = 0;
+    if (!sfm::plan_bwd(q, eb, &ws)) return false;
+    const size_t B = (size_t)(B1 * B2), XL = (flags & SFM_FUSE_PAD) ? (size_t)L - 2 : (size_t)L;
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    size_t off = up(ws);
+    a.xT = off;
+    off += up(B * D * XL * eb);
+    a.dT = off;
+    off += up(B * D * L * eb);
+    a.dyT = off;
+    off += up(B * D * L * eb);
+    a.bT = off;
+    off += up(B * N * L * eb);
+    a.cT = off;
+    off += up(B * N * L * eb);
+    a.duT = off;
+    off += up(B * D * L * eb);
+    a.ddT = off;
+    off += up(B * D * L * eb);
+    a.dbT = off;
+    off += up(B * N * L * 4);
+    a.dcT = off;
+    off += up(B * N * L * 4);
+    a.total = off;
+    return true;
+}
+
 }  // namespace
 
 extern "C" sfm_status sfm_selective_scan_bwd_workspace_size(int64_t B1, int64_t B2, int64_t D, int64_t N, int64_t L,
@@ -478,8 +519,14 @@ extern "C" sfm_status sfm_selective_scan_bwd_workspace_size(int64_t B1, int64_t 
     sfm::BwdParams p{};
     fill_bwd(p, B1, B2, D, N, L, conv_k ? &dummy : nullptr, conv_k ? conv_k : 1, 0, 0, 1, flags);
     size_t ws = 0;
-    if (!sfm::plan_bwd(p, io_bytes(io_dtype), &ws))
-        return fail(SFM_ERR_UNSUPPORTED, "sfm_selective_scan_bwd_workspace_size: no plan fits LDS");
+    if (!sfm::plan_bwd(p, io_bytes(io_dtype), &ws)) {
+        sfm::BwdParams q{};
+        ClAdapter a{};
+        if (!p.cl || !plan_cl_adapter(q, B1, B2, D, N, L, conv_k ? &dummy : nullptr, conv_k ? conv_k : 1, 0, 0, 1,
+                                      flags, io_bytes(io_dtype), a))
+            return fail(SFM_ERR_UNSUPPORTED, "sfm_selective_scan_bwd_workspace_size: no plan fits LDS");
+        ws = a.total;
+    }
     *bytes = (int64_t)ws;
     return ok();
 }
@@ -522,7 +569,51 @@ extern "C" sfm_status sfm_selective_scan_bwd(
     sfm::BwdParams p{};
     fill_bwd(p, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus, flags);
     size_t need = 0;
-    if (!sfm::plan_bwd(p, eb, &need)) return fail(SFM_ERR_UNSUPPORTED, "%s: no plan fits LDS", who);
+    if (!sfm::plan_bwd(p, eb, &need)) {
+        sfm::BwdParams q{};
+        ClAdapter a{};
+        if (!p.cl || !plan_cl_adapter(q, B1, B2, D, N, L, conv_w, conv_k, conv_pad_left, conv_act, delta_softplus,
+                                      flags, eb, a))
+            return fail(SFM_ERR_UNSUPPORTED, "%s: no plan fits LDS", who);
+        if (!workspace || workspace_bytes < (int64_t)a.total)
+            return fail(SFM_ERR_SHAPE, "%s: workspace of %lld bytes needed (see sfm_selective_scan_bwd_workspace_size)",
+                        who, (long long)a.total);
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        char* w = static_cast<char*>(workspace);
+        // channel-last -> channel-first: u [B, XL, D], delta/dy [B, L, D], B/C [B, L, N]
+        hipError_t e = sfm::launch_transpose(u, w + a.xT, B, XL, D, eb, s);
+        if (e == hipSuccess) e = sfm::launch_transpose(delta, w + a.dT, B, L, D, eb, s);
+        if (e == hipSuccess) e = sfm::launch_transpose(dy, w + a.dyT, B, L, D, eb, s);
+        if (e == hipSuccess) e = sfm::launch_transpose(Bm, w + a.bT, B, L, N, eb, s);
+        if (e == hipSuccess) e = sfm::launch_transpose(Cm, w + a.cT, B, L, N, eb, s);
+        if (e != hipSuccess) return hip_status(e, who);
+        q.u = w + a.xT;
+        q.delta = w + a.dT;
+        q.A = A;
+        q.Bm = w + a.bT;
+        q.Cm = w + a.cT;
+        q.Dskip = Dskip;
+        q.dbias = delta_bias;
+        q.conv_b = conv_b;
+        q.dy = w + a.dyT;
+        q.du = w + a.duT;
+        q.ddelta = w + a.ddT;
+        q.dA = dA;
+        q.dBm = reinterpret_cast<float*>(w + a.dbT);
+        q.dCm = reinterpret_cast<float*>(w + a.dcT);
+        q.dDskip = dDskip;
+        q.ddbias = ddelta_bias;
+        q.dconv_w = dconv_w;
+        q.dconv_b = dconv_b;
+        q.ws = reinterpret_cast<float*>(w);
+        e = sfm::launch_bwd(q, io_dtype, s);
+        // channel-first -> channel-last: du, ddelta [B, D, L] -> [B, L, D]; dB, dC [B, N, L] -> [B, L, N]
+        if (e == hipSuccess) e = sfm::launch_transpose(w + a.duT, du, B, D, L, eb, s);
+        if (e == hipSuccess) e = sfm::launch_transpose(w + a.ddT, ddelta, B, D, L, eb, s);
+        if (e == hipSuccess) e = sfm::launch_transpose(w + a.dbT, dBm, B, N, L, 4, s);
+        if (e == hipSuccess) e = sfm::launch_transpose(w + a.dcT, dCm, B, N, L, 4, s);
+        return hip_status(e, who);
+    }
     if (!workspace || workspace_bytes < (int64_t)need)
         return fail(SFM_ERR_SHAPE, "%s: workspace of %lld bytes needed (see sfm_selective_scan_bwd_workspace_size)",
                     who, (long long)need);

@@ -90,6 +90,9 @@ hipError_t launch_dwconv1d(const void* x, const float* w, const float* bias, voi
                            int64_t D, int64_t L, int K, int pad_left, int act, int io_dtype, hipStream_t stream);
 
 hipError_t launch_aux_pad(const void* in, void* out, int64_t rows, int64_t T, int io_dtype, hipStream_t stream);
+// [batch][R][C] -> [batch][C][R] for 2- or 4-byte elements (layout.hip)
+hipError_t launch_transpose(const void* in, void* out, int64_t batch, int64_t R, int64_t C, int elem_bytes,
+                            hipStream_t stream);
 hipError_t launch_aux_swap(const void* in, void* out, int64_t rows, int64_t L, int io_dtype, hipStream_t stream);
 
 }  // namespace sfm

@@ -199,6 +199,18 @@ def ws_expect_split(B, D, N, L, K, segs, cps, kw):
                 up(waves * (2 * ns + 2) * 64) + up(waves * 64 * 2) + up(waves * 2 * (kw - 1) * 64))
 
 
+def test_bwd_workspace_size_channel_last_long_rows():
+    """Channel-last rows too long for the whole-sample kernel run channel-first on
+    transposed copies: that plan's workspace, then x, delta, dy, B, C transposed,
+    then du, ddelta (io) and dB, dC (float32), each region on 256 bytes."""
+    up = lambda v: (v + 255) // 256 * 256
+    B, D, N, L, XL = 1, 64, 16, 4002, 4000
+    cf = ws_expect_split(B, D, N, L, 4, 63, 32, 4)
+    assert sfm.sfm_selective_scan_bwd_workspace_size(B, 1, D, N, L, 4, "bf16", 3) == cf
+    want = up(cf) + up(B * D * XL * 2) + 4 * up(B * D * L * 2) + 2 * up(B * N * L * 2) + 2 * up(B * N * L * 4)
+    assert sfm.sfm_selective_scan_bwd_workspace_size(B, 1, D, N, L, 4, "bf16", 3 | sfm.SFM_LAYOUT_BLD) == want
+
+
 def test_bwd_workspace_size_split_rows():
     """Few samples x tiles (here 1 x 1) on long rows: the chunked plan splits each
     row into segments of 64 positions or more; the reported size is that layout."""

@@ -229,6 +229,8 @@ def test_bwd_repeatable(chunked, monkeypatch):
     (2, 24, 16, 21, 1, 4, 3, 0, True, 0, "f32"),     # causal conv, N = 16
     (3, 16, 8, 9, 1, 0, 0, 0, True, 2, "f32"),       # no conv, swap only
     (64, 640, 8, 49, 1, 4, 1, 0, True, 3, "bf16"),   # stage-4 shape (64 of its 256 samples)
+    (2, 64, 8, 298, 1, 4, 1, 0, True, 3, "bf16"),    # rows too long for the whole-sample kernel:
+    (2, 24, 16, 700, 2, 4, 3, 1, True, 1, "f32"),    #   channel-first on transposed copies in the workspace
 ])
 def test_bwd_channel_last(B, D, N, T, B2, K, P, act, sp, flags, io):
     """Channel-last backward: bit-identical to channel-first on the transposed tensors
@@ -257,6 +259,12 @@ def test_bwd_channel_last_rejects_unaligned_rows():
     with pytest.raises(sfm.SFMError):
         sfm.sfm_selective_scan_bwd(z(B, L, D), z(B, L, D), z(D, N, dt=torch.float32), z(B, L, N), z(B, L, N),
                                    z(B, L, D), conv_w=z(D, 4, dt=torch.float32), flags=sfm.SFM_LAYOUT_BLD)
+
+
+def test_bwd_long_rows_channel_last_bf16():
+    """Channel-last rows of 4002 positions (N = 16): transposed into the workspace,
+    the chunked split-row backward, transposed back; bit-identical to channel-first."""
+    run_case(B=2, D=128, N=16, T=4000, B2=1, K=4, P=1, act=0, softplus=True, flags=3, io="bf16", seed=37, cl=True)
 
 
 def test_bwd_long_rows_bf16():
