@@ -152,7 +152,9 @@ sfm_status sfm_selective_scan_fwd_ex(const void* u, const void* delta, const flo
  * sfm_selective_scan_fwd_ws -- sfm_selective_scan_fwd_ex (same arguments, flags
  * and results within the parity tolerance) with a caller-owned device
  * workspace, for rows too long for the in-LDS carries: when samples times
- * 64-channel tiles give fewer than 1024 waves (channel-first only), each sample
+ * 64-channel tiles give fewer than 1024 waves (channel-first only) and the
+ * regular forward does not stream the rows (its streaming kernel takes long
+ * rows of 9 to 16 states, faster and without a workspace), each sample
  * row is split along L into segments of at least 64 positions, one wave each,
  * in three launches -- the fused pad's float64 token sums per segment, a carry
  * pass (each segment's state reached from zero and the sum of its steps), and
@@ -190,7 +192,7 @@ sfm_status sfm_selective_scan_fwd_ws_size(int64_t B1, int64_t B2, int64_t D, int
  * workspace, the call uses a static device array of SFM_NOALLOC_SCRATCH_BYTES
  * instead (one copy per GPU, held until the process ends); it calls no
  * allocator.  Rows that need more (sfm_selective_scan_fwd_ws_size above the
- * limit; the 16 x 320 x 4002-position long workload needs 12.7 MiB) return
+ * limit; 16 x 320 rows of 4002 positions and 8 states need 8.2 MiB) return
  * SFM_ERR_UNSUPPORTED with nothing launched.  Every call on one GPU shares that
  * GPU's array: calls that may overlap in time on one GPU (different streams)
  * race and must be serialised by the caller; nothing in it needs clearing
