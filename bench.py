@@ -13,13 +13,16 @@ Prints ONE JSON line.  `value` is token*channels per second (token*channels =
 B * D * (T + 2), aux tokens included) of the stage-4 step (L = 51).  The same
 line carries the stage-3 step (L = 198, `stage3`), a plain 1 GiB copy timed in
 the same process (the achievable HBM rate, `hbm.copy_GBps`) with each step's
-fraction of it, the folding speed-up t(B2 = 1) / t(B2) of both stages
-(`fold`), the `roofline` object of the scan kernel (timed live with HIP events
+fraction of it, the folding speed-up t(B2 = 1) / t(B2) of both stages and
+of the base model's stage-3 rows with the adaptive-B1 table's pick against the
+best swept B2 (`fold`), the `roofline` object of the scan kernel (timed live with HIP events
 on the stream it runs on) and `cpu_baseline`, the CPU oracle on one core and on
 all cores of the host.
 
     python bench.py [--steps K] [--warmup W] [--workload stage4] [--b2 B2]
     python bench.py --mode copy    # plain 1 GiB copy, used to calibrate HBM counters
+    python bench.py --mode aux     # the standalone conv, pad and swap launches
+    python bench.py --mode bwd     # the backward of the fused step
 """
 from __future__ import annotations
 
@@ -442,6 +445,11 @@ def main():
                        "note": "t(B2=1)/t(B2) per fold ratio of the fused step, same inputs, same process; "
                                "'chosen' is the adaptive-B1 table's pick"}
         del ctx3
+        # the adaptive-B1 table graded where folding is closest to neutral: the
+        # base model's stage-3 rows (512 x 512 channels, 16 states), chosen vs best B2
+        ctxb = Workload(a, synth.WORKLOADS["base_stage3"], hip, sp, dev)
+        out["fold"]["base_stage3"] = ctxb.fold_sweep([1, 2, 4, 8, 16, 32, 64], ks, a.warmup, ctxb.b2(0), None)
+        del ctxb
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ctx.li, a.cpu_seconds)
     print(json.dumps(out))
@@ -723,7 +731,8 @@ class Workload:
         for b2 in b2s:
             if self.w.B % b2:
                 continue
-            ms = chosen_ms if b2 == chosen else self.time_step(b2, "step", K, W)["ms_per_step"]
+            ms = chosen_ms if (b2 == chosen and chosen_ms is not None) else \
+                self.time_step(b2, "step", K, W)["ms_per_step"]
             rows[b2] = ms
         base = rows[1]
         best = min(rows, key=rows.get)
