@@ -289,14 +289,20 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     const int L = p.L, S = p.B2 * p.L;
     if (p.xrow <= 0) p.xrow = p.pad_in ? L - 2 : L;
     p.split = 0;
-    // The lane-split kernel when asked for, or when one wave per (sample,
-    // 64-channel tile) would give the SIMDs fewer than two waves each (measured
-    // on MI355X: stage-3 shapes 80.7 vs 102.6 us; at stage-4, 2.5 waves per
-    // SIMD, the one-lane kernel keeps the edge, 31.2 vs 32.4 us, by issuing
-    // fewer VALU instructions per token).
+    // The lane-split kernel when asked for; when one wave per (sample,
+    // 64-channel tile) would give the SIMDs fewer than two waves each; and, on
+    // unfolded rows, up to four each.  Measured on MI355X (same-process A/B):
+    // stage-3 shapes, 1.25 one-lane waves per SIMD: 67-71 vs 101-102 us;
+    // stage-4, 2.5 per SIMD, where the one-lane kernel leaves half the SIMDs
+    // with three waves: 29.8-32.7 vs 31.3-33.5 us with two lanes per channel
+    // (five balanced waves per SIMD); the base model's stage-3, 4 per SIMD:
+    // 312 vs 355 us.  Folded rows take their samples in turn on one lane-split
+    // wave but as separate pieces on the one-lane kernel: stage-4 at B2 = 2
+    // ties, at B2 = 4 the lane-split kernel loses (43.7 vs 35.6 us).
     const int cus = device_cus();
     const long long lane_waves = (long long)p.B1 * p.B2 * ((p.D + kWave - 1) / kWave);
-    const bool want_split = split_hint > 0 || (split_hint < 0 && lane_waves < 2LL * 4 * cus);
+    const bool want_split = split_hint > 0 ||
+                            (split_hint < 0 && (lane_waves < 2LL * 4 * cus || (lane_waves <= 4LL * 4 * cus && p.B2 == 1)));
     if (want_split && waves_hint <= 0 && ch_hint <= 0) {
         // G = 2 or 4 first (fewer instructions per token); the streaming
         // kernel where those cannot stage the rows (long rows) or when asked for

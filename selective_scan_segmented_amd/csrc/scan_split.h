@@ -292,13 +292,17 @@ struct SplitWave {
         if (!CHECK || tau < L) dr[tau] = from_f32<IO>(yown);
     }
 
-    // One state per lane: the LDS values of an unchecked block, read one block
-    // ahead so that their latency hides behind the previous block's arithmetic
-    // (with one or two waves per SIMD nothing else would hide it).
+    // The LDS values of an unchecked block, read one block ahead so that their
+    // latency hides behind the previous block's arithmetic (with few waves per
+    // SIMD nothing else hides it): the B/C of the G positions, the conv taps
+    // the block reads new (the others shift in from the previous block) or the
+    // input itself without conv, and delta of this lane's position.
+    static constexpr int kKeep = CONV ? (KW > G ? KW - G : 0) : 0;
     struct Ahead {
-        float2 bcv[G];  // B and C of this lane's state at t0 .. t0 + G - 1
-        IO tap[KW];     // conv taps (or the input itself without conv) of position t0 + g
-        IO dl;          // delta of position t0 + g
+        float2 bcv[NPL == 1 ? G : 1];       // one state per lane: (B, C) of t0 .. t0 + G - 1
+        float4 bq[NPL == 1 ? 1 : G * NB];   // several: [B.., C..] of each position
+        IO tap[KW];
+        IO dl;
     };
 
     __device__ __forceinline__ void fetch(int t0, const IO* xr, const IO* dr, const float* bc, Ahead& a) const {
@@ -307,13 +311,22 @@ struct SplitWave {
         const int P2 = p.P + KW - p.K;
         if constexpr (CONV) {
 #pragma unroll
-            for (int j = 0; j < KW; ++j) a.tap[j] = xr[tau - P2 + j - lo];
+            for (int j = kKeep; j < KW; ++j) a.tap[j] = xr[tau - P2 + j - lo];
         } else {
             a.tap[0] = xr[tau - lo];
         }
         a.dl = dr[tau];
+        if constexpr (NPL == 1) {
 #pragma unroll
-        for (int j = 0; j < G; ++j) a.bcv[j] = *reinterpret_cast<const float2*>(bc + ((t0 + j) * G + g) * 2);
+            for (int j = 0; j < G; ++j) a.bcv[j] = *reinterpret_cast<const float2*>(bc + ((t0 + j) * G + g) * 2);
+        } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float4* q4 = reinterpret_cast<const float4*>(bc + ((t0 + j) * G + g) * (2 * NPL));
+#pragma unroll
+                for (int k = 0; k < NB; ++k) a.bq[j * NB + k] = q4[k];
+            }
+        }
     }
 
     // The unchecked block of positions [t0, t0 + G) from fetched values; the
@@ -322,7 +335,9 @@ struct SplitWave {
         float u;
         if constexpr (CONV) {
 #pragma unroll
-            for (int j = 0; j < KW; ++j) win[j] = to_f32(a.tap[j]);
+            for (int j = 0; j < kKeep; ++j) win[j] = win[j + G];
+#pragma unroll
+            for (int j = kKeep; j < KW; ++j) win[j] = to_f32(a.tap[j]);
             float acc = cb;
 #pragma unroll
             for (int j = 0; j < KW; ++j) acc = __builtin_fmaf(cw[j], win[j], acc);
@@ -341,17 +356,49 @@ struct SplitWave {
         }
         const float du = dt * u;
         const float dpu = Dk * u;
-        float pj[G];
-        static_for<G>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            const float d2j = bcast<G, j>(d2);
-            const float duj = bcast<G, j>(du);
-            const float bx = duj * a.bcv[j].x;
-            const float e = exp2_fast(d2j * A2[0]);
-            h[0] = __builtin_fmaf(e, h[0], bx);
-            pj[j] = a.bcv[j].y * h[0];
-        });
-        dr[t0 + g] = from_f32<IO>(row_reduce_scatter16(pj, lane) + dpu);
+        if constexpr (NPL == 1) {
+            float pj[G];
+            static_for<G>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const float d2j = bcast<G, j>(d2);
+                const float duj = bcast<G, j>(du);
+                const float bx = duj * a.bcv[j].x;
+                const float e = exp2_fast(d2j * A2[0]);
+                h[0] = __builtin_fmaf(e, h[0], bx);
+                pj[j] = a.bcv[j].y * h[0];
+            });
+            dr[t0 + g] = from_f32<IO>(row_reduce_scatter16(pj, lane) + dpu);
+        } else {
+            float yown = 0.0f;
+            static_for<G>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const float d2j = bcast<G, j>(d2);
+                const float duj = bcast<G, j>(du);
+                float bv[NPL], cv[NPL];
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    const float4 v = a.bq[j * NB + k];
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int e = 4 * k + m;  // element of [B_0..B_{NPL-1}, C_0..C_{NPL-1}]
+                        if (e < NPL) bv[e] = vv[m];
+                        else cv[e - NPL] = vv[m];
+                    }
+                }
+                float yp = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NPL; ++i) {
+                    const float bx = duj * bv[i];
+                    const float e = exp2_fast(d2j * A2[i]);
+                    h[i] = __builtin_fmaf(e, h[i], bx);
+                    yp = i == 0 ? cv[0] * h[0] : __builtin_fmaf(cv[i], h[i], yp);
+                }
+                yp = group_sum<G>(yp);
+                yown = (g == j) ? yp : yown;
+            });
+            dr[t0 + g] = from_f32<IO>(yown + dpu);
+        }
     }
 
     // Blocks of a sample that need no checks, [kA, kB): every position < L and
@@ -395,30 +442,22 @@ struct SplitWave {
         }
         for (; k < kA && k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
         const int ke = min(kB, k1);
-        if constexpr (NPL == 1) {
+        if (k < ke) {
+            // software-pipelined: block k + 1's LDS reads go out before block k computes
+            Ahead a0, a1;
+            fetch(k * G, xr, dr, bc, a0);
+            for (; k + 1 < ke; k += 2) {
+                fetch((k + 1) * G, xr, dr, bc, a1);
+                __builtin_amdgcn_sched_barrier(0);
+                block_ahead(k * G, dr, a0, h, win);
+                fetch(min(k + 2, ke - 1) * G, xr, dr, bc, a0);  // (a re-read of block k + 1 on the last trip)
+                __builtin_amdgcn_sched_barrier(0);
+                block_ahead((k + 1) * G, dr, a1, h, win);
+            }
             if (k < ke) {
-                // software-pipelined: block k + 1's LDS reads go out before block k computes
-                Ahead a0, a1;
-                fetch(k * G, xr, dr, bc, a0);
-                for (; k + 1 < ke; k += 2) {
-                    fetch((k + 1) * G, xr, dr, bc, a1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    block_ahead(k * G, dr, a0, h, win);
-                    fetch(min(k + 2, ke - 1) * G, xr, dr, bc, a0);  // (a re-read of block k + 1 on the last trip)
-                    __builtin_amdgcn_sched_barrier(0);
-                    block_ahead((k + 1) * G, dr, a1, h, win);
-                }
-                if (k < ke) {
-                    block_ahead(k * G, dr, a0, h, win);
-                    ++k;
-                }
+                block_ahead(k * G, dr, a0, h, win);
+                ++k;
             }
-        } else {
-            for (; k + 1 < ke; k += 2) {  // two blocks per trip: LDS offsets become immediates
-                block<false, false>(k * G, xr, dr, bc, h, win);
-                block<false, false>(k * G + G, xr, dr, bc, h, win);
-            }
-            for (; k < ke; ++k) block<false, false>(k * G, xr, dr, bc, h, win);
         }
         for (; k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
     }

@@ -208,12 +208,17 @@ def test_split_deterministic_and_every_element_written():
 
 
 def test_planner_picks_the_kernel_by_waves_per_simd():
-    """One wave per (sample, 64-channel tile): 1280 at stage-3 (fewer than two per
-    SIMD, lane-split kernel with four lanes per channel), 2560 at stage-4 (the
-    one-lane kernel)."""
+    """One wave per (sample, 64-channel tile): 1280 at stage-3 (1.25 per SIMD:
+    four lanes per channel, at any fold), 2560 at stage-4 (2.5 per SIMD: two
+    lanes per channel unfolded, the one-lane kernel folded), 4096 at the base
+    model's stage-3 (4 per SIMD: two lanes per channel unfolded)."""
     with env(SFM_SCAN_SPLIT=-1):
         assert "split=4" in sfm.sfm_scan_plan_string(256, 1, 320, 8, 198, 4, "bf16", 3)
-        assert "mode=0" in sfm.sfm_scan_plan_string(256, 1, 640, 8, 51, 4, "bf16", 3)
+        assert "split=4" in sfm.sfm_scan_plan_string(64, 4, 320, 8, 198, 4, "bf16", 3)
+        assert "split=2" in sfm.sfm_scan_plan_string(256, 1, 640, 8, 51, 4, "bf16", 3)
+        assert "mode=" in sfm.sfm_scan_plan_string(64, 4, 640, 8, 51, 4, "bf16", 3)
+        assert "split=2" in sfm.sfm_scan_plan_string(512, 1, 512, 16, 198, 4, "bf16", 3)
+        assert "mode=" in sfm.sfm_scan_plan_string(128, 4, 512, 16, 198, 4, "bf16", 3)
 
 
 CHUNK_SHAPES = [
