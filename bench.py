@@ -17,7 +17,9 @@ fraction of it, the folding speed-up t(B2 = 1) / t(B2) of both stages and
 of the base model's stage-3 rows with the adaptive-B1 table's pick against the
 best swept B2 (`fold`), the `roofline` object of the scan kernel (timed live with HIP events
 on the stream it runs on) and `cpu_baseline`, the CPU oracle on one core and on
-all cores of the host.
+all cores of the host.  Every timed region is preceded by an untimed run of
+the same step for --device-warmup-ms (100 ms) of wall time and then the W
+warm-up steps: the GPU's clocks ramp up over the first ~15 ms of load.
 
     python bench.py [--steps K] [--warmup W] [--workload stage4] [--b2 B2]
     python bench.py --mode copy    # plain 1 GiB copy, used to calibrate HBM counters
@@ -48,6 +50,26 @@ HBM_PEAK_GBPS = 8000.0
 # about 4.2 cycles with four or more waves resident, v_exp_f32 about 8.3.
 VALU_PEAK_TSLOT = 256 * 4 * 16 * 2.4e9 / 1e12
 TRANS_SLOTS = 2  # v_exp_f32 / v_log_f32 occupy about twice the issue time of an fp32 fma
+
+
+def device_warmup(step, ms: float) -> int:
+    """Run step(i) untimed for ms of wall time (in batches of 16, synchronized);
+    returns the number of steps.  The GPU's clocks rise over the first ~15 ms
+    of load and fall back within a second of idle (a stage-4 step measured
+    32.9 us cold, 29.7 us warm), so every timed region is preceded by this
+    before its W warm-up steps."""
+    import torch
+    n = 0
+    if ms <= 0:
+        return n
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(16):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return n
 
 
 class Hip:
@@ -242,6 +264,7 @@ def run_bwd(a, w, li, sets, prm, lib, io, io_bytes, b2, hip, sp, dev, dev_io):
         if rc:
             raise RuntimeError(f"bwd failed: {lib.sfm_last_error().decode()}")
 
+    device_warmup(step, a.device_warmup_ms)
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -290,6 +313,7 @@ def run_block(a, w, hip, sp, dev):
     b2s = [pick] + [b for b in (1, 2, 4, 8, 16) if b != pick and w.B % b == 0]
     rows = []
     for b2 in b2s:
+        device_warmup(lambda i: blk.forward(B2=b2), a.device_warmup_ms)
         for _ in range(a.warmup):
             blk.forward(B2=b2)
         torch.cuda.synchronize()
@@ -331,6 +355,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--device-warmup-ms", type=float, default=100.0,
+                    help="untimed run of the step before the W warm-up steps of every timed region, in ms of "
+                         "wall time: the GPU's clocks ramp up over the first ~15 ms of load")
     ap.add_argument("--workload", default="stage4")
     ap.add_argument("--b2", type=int, default=0, help="fold ratio; 0 = adaptive-B1 table")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets; 0 = enough for 2 GiB")
@@ -416,6 +443,9 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "device_warmup": {"ms": a.device_warmup_ms, "steps": ctx.warm_steps,
+                          "note": "untimed steps before the W warm-up steps of each timed region, so that the "
+                                  "timed steps run at the GPU's loaded clocks"},
         "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -509,6 +539,7 @@ def run_aux(a, w, hip, sp, dev):
     out = {"mode": "aux", "workload": f"{w.name}: B={w.B} D={w.D} L={w.L} K={w.K}", "B2": b2, "dtype": w.io,
            "input_sets": nsets, "steps": K, "copy_GBps": round(copy, 1)}
     for name, (fn, args, alg) in ops.items():
+        device_warmup(lambda i: fn(*args[i % nsets]), a.device_warmup_ms)
         for i in range(W):
             rc = fn(*args[i % nsets])
             if rc:
@@ -652,6 +683,7 @@ class Workload:
             for st in self.sets:
                 self.sfm.sfm_aux_pad_swap(st["x"], out=st["xp"], mode="pad")
             self.padded = True
+        self.warm_steps = device_warmup(step, getattr(self.a, "device_warmup_ms", 0.0))
         for i in range(W):
             step(i)
         torch.cuda.synchronize()

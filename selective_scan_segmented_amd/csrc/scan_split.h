@@ -36,6 +36,9 @@
 //    values never cross a sample boundary; taps outside the sample read 0.
 #pragma once
 
+#include <algorithm>
+#include <atomic>
+
 #include "sfm_device.h"
 #include "sfm_internal.h"
 
@@ -480,11 +483,12 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_kernel(ScanParams p) {
     constexpr int CPW = W::CPW;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     if (p.stagger_ticks) {
-        // Staggered start: with the whole grid resident at once, dispatch
-        // round r = blockIdx / stagger_period issues its loads r ticks (10 ns)
-        // later, so early rounds compute while later rounds load.
+        // Staggered start: dispatch round r = blockIdx / stagger_period issues
+        // its loads r ticks (10 ns) later, so early rounds compute while later
+        // rounds load.  Rounds that were not resident at launch start late
+        // anyway and take no delay.
         const unsigned long long r = blockIdx.x / p.stagger_period;
-        if (r) {
+        if (r && r < (unsigned long long)p.stagger_rounds) {
             const unsigned long long until = __builtin_amdgcn_s_memrealtime() + r * p.stagger_ticks;
             while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(2);
         }
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_chunk_kernel(ScanParams
     extern __shared__ __attribute__((aligned(16))) char smem[];
     if (p.stagger_ticks) {
         const unsigned long long r = blockIdx.x / p.stagger_period;
-        if (r) {
+        if (r && r < (unsigned long long)p.stagger_rounds) {
             const unsigned long long until = __builtin_amdgcn_s_memrealtime() + r * p.stagger_ticks;
             while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(2);
         }
@@ -1062,7 +1066,33 @@ hipError_t launch_t(const ScanParams& p, hipStream_t stream) {
     }
     const unsigned grid = (unsigned)(p.stiles * p.B1);
     const unsigned block = (unsigned)(kWave * p.wpg);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(block), (size_t)p.lds_bytes, stream, p);
+    if (!p.stagger_ticks) {
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(block), (size_t)p.lds_bytes, stream, p);
+        return hipGetLastError();
+    }
+    // The staggered start delays only the dispatch rounds resident at launch:
+    // as many as workgroups of this kernel fit one CU (registers and LDS),
+    // asked of the runtime once per (LDS size, block size) and kept.
+    static std::atomic<unsigned long long> occ_cache{0};
+    const unsigned long long key =
+        ((unsigned long long)(unsigned)p.lds_bytes << 17) | ((unsigned long long)(p.sq > 0) << 16) | block;
+    unsigned long long c = occ_cache.load(std::memory_order_relaxed);
+    int occ;
+    if (c && (c >> 8) == key) {
+        occ = (int)(c & 0xff);
+    } else {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern), (int)block,
+                                                         (size_t)p.lds_bytes) != hipSuccess || nb <= 0) {
+            (void)hipGetLastError();
+            nb = 255;  // unknown: every round delays
+        }
+        occ = std::min(nb, 255);
+        occ_cache.store((key << 8) | (unsigned long long)occ, std::memory_order_relaxed);
+    }
+    ScanParams q = p;
+    q.stagger_rounds = occ;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(block), (size_t)q.lds_bytes, stream, q);
     return hipGetLastError();
 }
 

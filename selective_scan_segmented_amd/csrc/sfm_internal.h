@@ -47,6 +47,9 @@ struct ScanParams {
     // workgroups of dispatch round r = blockIdx / stagger_period issue their
     // loads r * stagger_ticks (10 ns ticks) after they start.
     int stagger_period, stagger_ticks;
+    // Lane-split kernels: only rounds r < stagger_rounds delay (the rounds
+    // resident at launch); set by the launcher from the kernel's occupancy.
+    int stagger_rounds;
     // Lane-split kernel (scan_split.h): split = G lanes per channel (0 = the
     // kernel above), wpg waves of 64/G channels per workgroup sharing one B/C
     // stage, stiles workgroups per folded row; LDS offsets of the float32
