@@ -68,6 +68,15 @@ __device__ __forceinline__ float bcast(float v) {
     else return dpp<bcast_ctrl<G, J>()>(v);
 }
 
+// bcast for a float64 value (its two halves by two DPP moves)
+template <int G, int J>
+__device__ __forceinline__ double bcast_f64(double v) {
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)b, bcast_ctrl<G, J>(), 0xf, 0xf, true);
+    const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(b >> 32), bcast_ctrl<G, J>(), 0xf, 0xf, true);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
 // Sum over the G adjacent lanes of a group, result in every lane of it
 // (quad_perm [1,0,3,2] then [2,3,0,1]; for 16-lane groups then row_half_mirror,
 // which pairs the two quads of each half-row, and row_mirror, which pairs the
@@ -477,7 +486,7 @@ struct SplitWave {
 };
 
 template <typename IO, int NS, int G, int KW, bool CONV, bool SP, bool SILU>
-__global__ __launch_bounds__(kWave * kMaxWpg) void split_kernel(ScanParams p) {
+__global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu(NS <= 8 && KW <= 4 ? 4 : 1))) void split_kernel(ScanParams p) {
     using W = SplitWave<IO, NS, G, KW, CONV, SP, SILU>;
     constexpr int NPL = W::NPL;
     constexpr int CPW = W::CPW;
@@ -550,37 +559,34 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_kernel(ScanParams p) {
         const int b = b1 * p.B2 + j;
         wait_vmem();
         __syncthreads();  // every wave's transfers (this wave's slabs, wave 0's raw B/C) have landed
-        // Set-up of the sample, shared by the group's waves.  With the fused
-        // pad the first nmean waves take the row means (one lane per channel of
-        // the group, so the float64 sums run on all 64 lanes) while the others
-        // widen B/C; without it every wave widens.
-        const int gch = p.wpg * CPW;  // channels of the group
-        const int nmean = p.pad_in ? min(p.wpg, (gch + kWave - 1) / kWave) : 0;
-        if (wave < nmean) {
-            const int r = wave * kWave + lane;  // channel row of the group
-            const int ow = r / CPW, oc = r - ow * CPW;
-            const int orows = max(0, min(CPW, D - (tile * p.wpg + ow) * CPW));
-            if (r < gch && oc < orows) {
-                // float64, index order, one rounding: bit-identical to the aux pad
-                const IO* row = reinterpret_cast<const IO*>(smem + p.slab_off + (size_t)ow * p.slab_bytes) + oc * XL;
-                means[r] = to_f32(Io<IO>::from_f64(row_sum_f64(row, XL) / (double)XL));
-            }
+        // Set-up of the sample.  With the fused pad every wave takes the row
+        // means of its own channels: lane g of a channel sums piece g of the
+        // row (ceil(XL / G) tokens) in float64 in index order, and every lane
+        // of the group adds the G piece sums in piece order and rounds once --
+        // the index-order sum of the aux pad whenever the float64 partial sums
+        // are exact.  Then all waves widen B/C.
+        if (p.pad_in) {
+            const int qp = (XL + G - 1) / G;
+            const int i0 = min(w.g * qp, XL), i1 = min(i0 + qp, XL);
+            const double part = row_sum_f64(xr + i0, i1 - i0);
+            double s = 0.0;
+            static_for<G>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                s += bcast_f64<G, j>(part);
+            });
+            w.mean = to_f32(Io<IO>::from_f64(s / (double)XL));
         }
-        // (with a single wave per group it does both in turn)
-        const int wb = nmean < p.wpg ? nmean : 0;  // first widening wave
-        if (wave >= wb) {
+        {
             // raw [2][N][L] -> float32 [t][g][B.., C..]
             const float invL = 1.0f / (float)L;
-            const int wthr = (p.wpg - wb) * kWave;
-            for (int e = tid - wb * kWave; e < N * L; e += wthr) {
+            for (int e = tid; e < N * L; e += nthr) {
                 const int n = div_small(e, invL), t = e - n * L;
                 float* q = bc + (t * G + n / NPL) * (2 * NPL) + n % NPL;
                 q[0] = to_f32(braw[e]);
                 q[NPL] = to_f32(braw[N * L + e]);
             }
         }
-        __syncthreads();  // B/C and the row means of sample b visible to the group
-        if (p.pad_in) w.mean = means[wave * CPW + w.c];
+        __syncthreads();  // B/C of sample b visible to the group
         w.sample(xr, dr, bc);
         wave_lds_sync();
         if (rows > 0) {
@@ -590,10 +596,19 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_kernel(ScanParams p) {
                 dr[L - 1] = a;
             }
             wave_lds_sync();
+            // y leaves by 16-byte stores, two LDS reads in flight per lane
             IO* yg = static_cast<IO*>(p.y) + ((size_t)b * D + dw0) * L;
             const int units = rows * L * (int)sizeof(IO) / 16;
-            for (int u = lane; u < units; u += kWave)
-                reinterpret_cast<uint4*>(yg)[u] = reinterpret_cast<const uint4*>(ds)[u];
+            const uint4* ys = reinterpret_cast<const uint4*>(ds);
+            uint4* yo = reinterpret_cast<uint4*>(yg);
+            for (int u0 = lane; u0 < units; u0 += 2 * kWave) {
+                const uint4 v0 = ys[u0];
+                const bool two = u0 + kWave < units;
+                uint4 v1;
+                if (two) v1 = ys[u0 + kWave];
+                yo[u0] = v0;
+                if (two) yo[u0 + kWave] = v1;
+            }
         }
         if (j + 1 < p.B2) {
             // this wave's LDS reads of y have completed before transfers rewrite the slab

@@ -109,6 +109,34 @@ def test_split_against_oracle(B, D, N, T, B2, K, P, act, bias, io, G, flags):
 
 
 @pytest.mark.parametrize("G", [2, 4])
+@pytest.mark.parametrize("T,io", [(49, "bf16"), (196, "bf16"), (21, "f32"), (3, "bf16"), (1, "f32")])
+def test_split_fused_pad_matches_the_pad_kernel(G, T, io):
+    """The fused aux pad of the whole-row kernel takes each row's mean as G
+    piece sums (lane g of a channel sums piece g in float64, in index order)
+    added in piece order: on rows whose float64 partial sums are exact it is
+    the pad kernel's index-order mean, so the fused step is bit-identical to
+    pad + scan + swap as three launches.  Pieces of unequal length (T not a
+    multiple of G) and rows shorter than the lane group (empty pieces)."""
+    import torch
+    B, D, N, K = 3, 96, 8, 4
+    L = T + 2
+    say(f"split fused pad G={G} T={T} io={io}")
+    x, delta, Bm, Cm, A, Dk, db, cw, _ = make(B, D, N, T, K, io, seed=G * 100 + T)
+    Tt = lambda a: torch.from_numpy(a).cuda()
+    xd, dd, Bd, Cd = map(to_dev, (x, delta, Bm, Cm))
+    with env(SFM_SCAN_SPLIT=G, SFM_SCAN_SPLIT_CHUNK=0):  # whole rows
+        plan = sfm.sfm_scan_plan_string(B, 1, D, N, L, K, io, 3)
+        assert f"split={G} chunk=0" in plan, plan
+        args = (dd, Tt(A), Bd, Cd, Tt(Dk), Tt(db))
+        fused = sfm.sfm_selective_scan_fwd_ex(xd, *args, conv_w=Tt(cw), conv_pad_left=1, flags=3)
+        xp = sfm.sfm_aux_pad_swap(xd, mode="pad")
+        y = sfm.sfm_selective_scan_fwd_ex(xp, *args, conv_w=Tt(cw), conv_pad_left=1, flags=0)
+        sfm.sfm_aux_pad_swap(y, out=y, mode="swap")
+        torch.cuda.synchronize()
+    assert np.array_equal(from_dev(fused), from_dev(y))
+
+
+@pytest.mark.parametrize("G", [2, 4])
 @pytest.mark.parametrize("softplus", [True, False])
 def test_split_no_conv(G, softplus):
     import torch
