@@ -208,102 +208,6 @@ struct SplitWave {
         return (q < 0 || q >= L) ? 0.0f : v;
     }
 
-    // One block of G positions [t0, t0 + G) (positions >= L are skipped):
-    // lane g's per-token work for position t0 + g, then the G state updates.
-    // win holds this lane's conv taps for position t0 + g - G on entry and
-    // for t0 + g on exit.  FIRST: t0 == 0 (the reset).  CHECK: taps may leave
-    // the staged interior.
-    template <bool FIRST, bool CHECK>
-    __device__ __forceinline__ void block(int t0, const IO* xr, IO* dr, const float* bc, float (&h)[NPL],
-                                          float (&win)[KW]) {
-        const int L = p.L;
-        const int tau = t0 + g;                 // this lane's token
-        const int tc = CHECK ? min(tau, L - 1) : tau;
-        const int P2 = p.P + KW - p.K;           // pad_left of the KW-tap window
-        // conv taps of tau: q = tau - P2 + j; the window moves by G per block
-        if constexpr (CONV) {
-            constexpr int keep = KW > G ? KW - G : 0;
-#pragma unroll
-            for (int j = 0; j < keep; ++j) win[j] = win[j + G];
-#pragma unroll
-            for (int j = keep; j < KW; ++j) {
-                const int q = tau - P2 + j;
-                win[j] = CHECK ? xq(xr, q) : to_f32(xr[q - (p.pad_in ? 1 : 0)]);
-            }
-        }
-        float u;
-        if constexpr (CONV) {
-            float acc = cb;
-#pragma unroll
-            for (int j = 0; j < KW; ++j) acc = __builtin_fmaf(cw[j], win[j], acc);
-            u = SILU ? silu(acc) : acc;
-        } else {
-            u = CHECK ? xq(xr, tc) : to_f32(xr[tc - (p.pad_in ? 1 : 0)]);
-        }
-        const float dl = to_f32(dr[tc]) + dbias;
-        float d2, dt;  // Delta * log2(e) and Delta
-        if constexpr (SP) {
-            d2 = softplus_log2e(dl);
-            dt = d2 * kLn2;
-        } else {
-            dt = dl;
-            d2 = dl * kLog2e;
-        }
-        const float du = dt * u;
-        const float dpu = Dk * u;  // D*u of this lane's own token
-        float yown = 0.0f;
-        float pj[NPL == 1 ? G : 1];  // one state per lane: this lane's C*h term of each position
-        static_for<G>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            if constexpr (NPL == 1) pj[j] = 0.0f;
-            if (FIRST || CHECK ? t0 + j < L : true) {
-                const float d2j = bcast<G, j>(d2);
-                const float duj = bcast<G, j>(du);
-                const float4* q4 = reinterpret_cast<const float4*>(bc + ((t0 + j) * G + g) * (2 * NPL));
-                float bv[NPL], cv[NPL];
-                if constexpr (NPL == 1) {
-                    const float2 v = *reinterpret_cast<const float2*>(bc + ((t0 + j) * G + g) * 2);
-                    bv[0] = v.x;
-                    cv[0] = v.y;
-                }
-#pragma unroll
-                for (int k = 0; k < NB; ++k) {
-                    const float4 v = q4[k];
-                    const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int e = 4 * k + m;  // element of [B_0..B_{NPL-1}, C_0..C_{NPL-1}]
-                        if (e < NPL) bv[e] = vv[m];
-                        else cv[e - NPL] = vv[m];
-                    }
-                }
-                float yp = 0.0f;
-#pragma unroll
-                for (int i = 0; i < NPL; ++i) {
-                    const float bx = duj * bv[i];
-                    if (FIRST && j == 0) {
-                        h[i] = bx;  // reset: the state is re-initialised at the sample start
-                    } else {
-                        const float a = exp2_fast(d2j * A2[i]);
-                        h[i] = __builtin_fmaf(a, h[i], bx);
-                    }
-                    yp = i == 0 ? cv[0] * h[0] : __builtin_fmaf(cv[i], h[i], yp);
-                }
-                if constexpr (NPL == 1) {
-                    pj[j] = yp;
-                } else {
-                    yp = group_sum<G>(yp);
-                    yown = (g == j) ? yp : yown;
-                }
-            }
-        });
-        if constexpr (NPL == 1) yown = row_reduce_scatter16(pj, lane);
-        // (lanes past the tile's last channel work on LDS rows that were not
-        // loaded and are not stored)
-        yown += dpu;
-        if (!CHECK || tau < L) dr[tau] = from_f32<IO>(yown);
-    }
-
     // The LDS values of an unchecked block, read one block ahead so that their
     // latency hides behind the previous block's arithmetic (with few waves per
     // SIMD nothing else hides it): the B/C of the G positions, the conv taps
@@ -341,23 +245,147 @@ struct SplitWave {
         }
     }
 
-    // The unchecked block of positions [t0, t0 + G) from fetched values; the
-    // same arithmetic as block<false, false>.
+    // LDS byte addresses of an unchecked block's reads (its first new conv
+    // tap, delta, and the lane's B/C of its first position) for the
+    // software-pipelined loop, which advances them by a constant per trip.
+    // They are held as plain 32-bit LDS addresses and re-pinned every trip
+    // (an empty asm), so the compiler keeps one register per stream and
+    // addresses the second block of a trip by instruction offsets instead of
+    // re-adding the LDS base of the array to a running offset.
+    struct Cursor {
+        uint32_t x, d, b;
+    };
+    static constexpr uint32_t kStepX = G * sizeof(IO);             // one block of taps / delta
+    static constexpr uint32_t kStepB = G * G * 2 * NPL * 4;        // one block of B/C
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    template <typename T>
+    static __device__ __forceinline__ T lds_ld(uint32_t a) {
+        return *(const __attribute__((address_space(3))) T*)(size_t)a;
+    }
+    static __device__ __forceinline__ __attribute__((address_space(3))) IO* lds_yp(uint32_t a) {
+        return (__attribute__((address_space(3))) IO*)(size_t)a;
+    }
+    static __device__ __forceinline__ uint32_t lds_addr(const void* q) {
+        return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)q;
+    }
+    __device__ __forceinline__ Cursor cursor(int t0, const IO* xr, const IO* dr, const float* bc) const {
+        const int lo = p.pad_in ? 1 : 0;
+        const int P2 = p.P + KW - p.K;
+        const int tau = t0 + g;
+        Cursor c;
+        c.x = CONV ? lds_addr(xr + (tau - P2 + kKeep - lo)) : lds_addr(xr + (tau - lo));
+        c.d = lds_addr(dr + tau);
+        c.b = lds_addr(bc + (t0 * G + g) * (NPL == 1 ? 2 : 2 * NPL));
+        return c;
+    }
+    static __device__ __forceinline__ void pin(Cursor& c) { asm volatile("" : "+v"(c.x), "+v"(c.d), "+v"(c.b)); }
+    // fetch() of the block BLK blocks after the cursor's
+    template <int BLK>
+    __device__ __forceinline__ void fetch_at(const Cursor& c, Ahead& a) const {
+        const uint32_t ox = c.x + BLK * kStepX, od = c.d + BLK * kStepX, ob = c.b + BLK * kStepB;
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = kKeep; j < KW; ++j) a.tap[j] = lds_ld<IO>(ox + (j - kKeep) * (uint32_t)sizeof(IO));
+        } else {
+            a.tap[0] = lds_ld<IO>(ox);
+        }
+        a.dl = lds_ld<IO>(od);
+        if constexpr (NPL == 1) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const f32x2 v = lds_ld<f32x2>(ob + j * G * 2 * 4);
+                a.bcv[j] = make_float2(v.x, v.y);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+#pragma unroll
+                for (int k = 0; k < NB; ++k) {
+                    const f32x4 v = lds_ld<f32x4>(ob + (j * G * 2 * NPL + 4 * k) * 4);
+                    a.bq[j * NB + k] = make_float4(v.x, v.y, v.z, v.w);
+                }
+            }
+        }
+    }
+
+    // The unchecked block of positions [t0, t0 + G) from fetched values.
     __device__ __forceinline__ void block_ahead(int t0, IO* dr, const Ahead& a, float (&h)[NPL], float (&win)[KW]) {
+        block_ahead_y(dr + t0 + g, a, h, win);
+    }
+    // block_ahead with y of this lane's position stored at yout
+    template <typename YP>
+    __device__ __forceinline__ void block_ahead_y(YP yout, const Ahead& a, float (&h)[NPL], float (&win)[KW]) {
+        float tn[KW];
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = kKeep; j < KW; ++j) tn[j] = to_f32(a.tap[j]);
+        } else {
+            tn[0] = to_f32(a.tap[0]);
+        }
+        compute<false>(yout, true, tn, to_f32(a.dl), a, h, win);
+    }
+
+    // An edge block: the first block of a sample, or one whose new conv taps
+    // or positions leave the staged interior.  The taps come through xq (zero
+    // outside the sample, the aux value at its ends); delta and B/C of a
+    // position >= L are read at L - 1 (in bounds) and its results discarded: y
+    // is stored for positions < L only, and the state after the sample's last
+    // position is never used.  Then the arithmetic of the pipelined blocks.
+    template <bool FIRST>
+    __device__ __forceinline__ void block_edge(int t0, const IO* xr, IO* dr, const float* bc, float (&h)[NPL],
+                                               float (&win)[KW]) {
+        const int L = p.L;
+        const int tau = t0 + g;
+        const int tc = min(tau, L - 1);
+        const int P2 = p.P + KW - p.K;
+        float tn[KW];
+        if constexpr (CONV) {
+#pragma unroll
+            for (int j = kKeep; j < KW; ++j) tn[j] = xq(xr, tau - P2 + j);
+        } else {
+            tn[0] = xq(xr, tc);
+        }
+        Ahead a;
+        if constexpr (NPL == 1) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                a.bcv[j] = *reinterpret_cast<const float2*>(bc + (min(t0 + j, L - 1) * G + g) * 2);
+        } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float4* q4 = reinterpret_cast<const float4*>(bc + (min(t0 + j, L - 1) * G + g) * (2 * NPL));
+#pragma unroll
+                for (int k = 0; k < NB; ++k) a.bq[j * NB + k] = q4[k];
+            }
+        }
+        compute<FIRST>(dr + tc, tau < L, tn, to_f32(dr[tc]), a, h, win);
+    }
+
+    // The arithmetic of a block of G positions [t0, t0 + G): lane g's
+    // per-token work for position t0 + g (new conv taps tn[kKeep..KW), or the
+    // input itself in tn[0] without conv; raw delta dl0), then the G state
+    // updates with the B/C of the positions in a; y of this lane's position
+    // goes to yout when store is set.  win holds this lane's conv taps for
+    // position t0 + g - G on entry and for t0 + g on exit.  FIRST: the block
+    // starts the sample (the state is re-initialised at its first position).
+    template <bool FIRST, typename YP>
+    __device__ __forceinline__ void compute(YP yout, bool store, const float (&tn)[KW], float dl0, const Ahead& a,
+                                            float (&h)[NPL], float (&win)[KW]) {
         float u;
         if constexpr (CONV) {
 #pragma unroll
             for (int j = 0; j < kKeep; ++j) win[j] = win[j + G];
 #pragma unroll
-            for (int j = kKeep; j < KW; ++j) win[j] = to_f32(a.tap[j]);
+            for (int j = kKeep; j < KW; ++j) win[j] = tn[j];
             float acc = cb;
 #pragma unroll
             for (int j = 0; j < KW; ++j) acc = __builtin_fmaf(cw[j], win[j], acc);
             u = SILU ? silu(acc) : acc;
         } else {
-            u = to_f32(a.tap[0]);
+            u = tn[0];
         }
-        const float dl = to_f32(a.dl) + dbias;
+        const float dl = dl0 + dbias;
         float d2, dt;
         if constexpr (SP) {
             d2 = softplus_log2e(dl);
@@ -375,11 +403,16 @@ struct SplitWave {
                 const float d2j = bcast<G, j>(d2);
                 const float duj = bcast<G, j>(du);
                 const float bx = duj * a.bcv[j].x;
-                const float e = exp2_fast(d2j * A2[0]);
-                h[0] = __builtin_fmaf(e, h[0], bx);
+                if (FIRST && j == 0) {
+                    h[0] = bx;  // reset: the state is re-initialised at the sample start
+                } else {
+                    const float e = exp2_fast(d2j * A2[0]);
+                    h[0] = __builtin_fmaf(e, h[0], bx);
+                }
                 pj[j] = a.bcv[j].y * h[0];
             });
-            dr[t0 + g] = from_f32<IO>(row_reduce_scatter16(pj, lane) + dpu);
+            const float yv = row_reduce_scatter16(pj, lane) + dpu;
+            if (store) *yout = from_f32<IO>(yv);
         } else {
             float yown = 0.0f;
             static_for<G>([&](auto jc) {
@@ -402,14 +435,18 @@ struct SplitWave {
 #pragma unroll
                 for (int i = 0; i < NPL; ++i) {
                     const float bx = duj * bv[i];
-                    const float e = exp2_fast(d2j * A2[i]);
-                    h[i] = __builtin_fmaf(e, h[i], bx);
+                    if (FIRST && j == 0) {
+                        h[i] = bx;  // reset: the state is re-initialised at the sample start
+                    } else {
+                        const float e = exp2_fast(d2j * A2[i]);
+                        h[i] = __builtin_fmaf(e, h[i], bx);
+                    }
                     yp = i == 0 ? cv[0] * h[0] : __builtin_fmaf(cv[i], h[i], yp);
                 }
                 yp = group_sum<G>(yp);
                 yown = (g == j) ? yp : yown;
             });
-            dr[t0 + g] = from_f32<IO>(yown + dpu);
+            if (store) *yout = from_f32<IO>(yown + dpu);
         }
     }
 
@@ -449,29 +486,46 @@ struct SplitWave {
                                            float (&h)[NPL], float (&win)[KW]) {
         int k = k0;
         if (k == 0 && k < k1) {
-            block<true, true>(0, xr, dr, bc, h, win);
+            block_edge<true>(0, xr, dr, bc, h, win);
             k = 1;
         }
-        for (; k < kA && k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
+        for (; k < kA && k < k1; ++k) block_edge<false>(k * G, xr, dr, bc, h, win);
         const int ke = min(kB, k1);
         if (k < ke) {
-            // software-pipelined: block k + 1's LDS reads go out before block k computes
+            // software-pipelined: block k + 1's LDS reads go out before block k
+            // computes.  Every trip of the loop reads two blocks ahead of the
+            // previous one at a fixed stride (the next trip's first block always
+            // exists), so the compiler keeps one running address per stream;
+            // the last one or two blocks are peeled.
             Ahead a0, a1;
-            fetch(k * G, xr, dr, bc, a0);
-            for (; k + 1 < ke; k += 2) {
+            Cursor cur = cursor(k * G, xr, dr, bc);
+            pin(cur);
+            fetch_at<0>(cur, a0);
+            for (; k + 2 < ke; k += 2) {
+                fetch_at<1>(cur, a1);
+                __builtin_amdgcn_sched_barrier(0);
+                block_ahead_y(lds_yp(cur.d), a0, h, win);
+                fetch_at<2>(cur, a0);
+                __builtin_amdgcn_sched_barrier(0);
+                block_ahead_y(lds_yp(cur.d + kStepX), a1, h, win);
+                cur.x += 2 * kStepX;
+                cur.d += 2 * kStepX;
+                cur.b += 2 * kStepB;
+                pin(cur);
+            }
+            if (k + 1 < ke) {
                 fetch((k + 1) * G, xr, dr, bc, a1);
                 __builtin_amdgcn_sched_barrier(0);
                 block_ahead(k * G, dr, a0, h, win);
-                fetch(min(k + 2, ke - 1) * G, xr, dr, bc, a0);  // (a re-read of block k + 1 on the last trip)
                 __builtin_amdgcn_sched_barrier(0);
                 block_ahead((k + 1) * G, dr, a1, h, win);
-            }
-            if (k < ke) {
+                k += 2;
+            } else {
                 block_ahead(k * G, dr, a0, h, win);
                 ++k;
             }
         }
-        for (; k < k1; ++k) block<false, true>(k * G, xr, dr, bc, h, win);
+        for (; k < k1; ++k) block_edge<false>(k * G, xr, dr, bc, h, win);
     }
 
     // Whole sample: positions [0, L) from the staged rows; y replaces delta.
@@ -524,22 +578,33 @@ __global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu
     const int nthr = p.wpg * kWave;
     const int tid = threadIdx.x;
 
+    // Transfers in the order the set-up needs them: the raw B/C (wave 0) and
+    // the x slab, then the delta slab last, so the row means and the B/C
+    // widening run while delta is still landing.  nd = the delta slab's
+    // transfer instructions (the last ones a wave issues).
+    const int nd = rows > 0 ? (rows * L * (int)sizeof(IO) / 16 + kWave - 1) / kWave : 0;
     auto issue = [&](int b) __attribute__((always_inline)) {
-        if (rows > 0) {
-            const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + dw0) * XL;
-            const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + dw0) * L;
-            dma_to_lds(xg, xs, rows * XL * (int)sizeof(IO), lane);
-            dma_to_lds(dg, ds, rows * L * (int)sizeof(IO), lane);
-        }
         if (wave == 0) {
             const int nbc = N * L * (int)sizeof(IO) / 16;
             dma2_to_lds(static_cast<const IO*>(p.Bm) + (size_t)b * N * L, nbc,
                         static_cast<const IO*>(p.Cm) + (size_t)b * N * L, nbc, braw, lane);
         }
+        if (rows > 0) {
+            const IO* xg = static_cast<const IO*>(p.u) + ((size_t)b * D + dw0) * XL;
+            dma_to_lds(xg, xs, rows * XL * (int)sizeof(IO), lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (rows > 0) {
+            const IO* dg = static_cast<const IO*>(p.delta) + ((size_t)b * D + dw0) * L;
+            dma_to_lds(dg, ds, rows * L * (int)sizeof(IO), lane);
+        }
     };
 
-    issue(b1 * p.B2);
+    // the parameters' loads go out first, so that the last nd vector-memory
+    // operations of a wave are its delta transfers
     w.load_params();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b1 * p.B2);
     // states n >= N: B = C = 0 for the whole launch (widening never writes them)
     if (N < NS) {
         for (int e = tid; e < L * NS; e += nthr) {
@@ -555,10 +620,16 @@ __global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu
     // the rows of channels past D are never loaded nor stored
     const IO* xr = xs + w.c * XL;
     IO* dr = ds + w.c * L;
-    for (int j = 0; j < p.B2; ++j) {
+    // One sample of the folded row.  The first sample runs outside the loop:
+    // a loop that issues transfers and uses registers loaded before it makes
+    // the compiler wait for every outstanding transfer in its preheader, which
+    // would undo the early start of the set-up.
+    auto run_sample = [&](int j) __attribute__((always_inline)) {
         const int b = b1 * p.B2 + j;
-        wait_vmem();
-        __syncthreads();  // every wave's transfers (this wave's slabs, wave 0's raw B/C) have landed
+        // at most the delta transfers outstanding (they complete in issue
+        // order): this wave's x slab and wave 0's raw B/C have landed
+        wait_vmem_at_most(nd);
+        lds_barrier();  // every wave's x slab and the raw B/C are visible to the group
         // Set-up of the sample.  With the fused pad every wave takes the row
         // means of its own channels: lane g of a channel sums piece g of the
         // row (ceil(XL / G) tokens) in float64 in index order, and every lane
@@ -587,6 +658,7 @@ __global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu
             }
         }
         __syncthreads();  // B/C of sample b visible to the group
+        wait_vmem();      // this wave's delta slab has landed
         w.sample(xr, dr, bc);
         wave_lds_sync();
         if (rows > 0) {
@@ -615,7 +687,9 @@ __global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             issue(b + 1);
         }
-    }
+    };
+    run_sample(0);
+    for (int j = 1; j < p.B2; ++j) run_sample(j);
     (void)NPL;
 }
 

@@ -94,6 +94,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete,
+// then s_barrier.  __syncthreads() also waits for every outstanding global
+// access (its fence covers global memory), which would drain direct
+// global->LDS transfers that the caller still wants in flight; data that such
+// transfers bring in must be waited for with wait_vmem / wait_vmem_at_most
+// before this barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- memory movement
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
