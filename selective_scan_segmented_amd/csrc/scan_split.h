@@ -112,6 +112,19 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&p)[16], int 
     return (b0 ? q2[1] : q2[0]) + dpp<0xB1>(b0 ? q2[0] : q2[1]);
 }
 
+// Reduce-scatter over each quad: p[j] holds this lane's term of sum j; lane
+// i of the quad returns the sum over the quad's four lanes of p[i & 3].  Two
+// butterfly steps (partners differ in lane bit 0, then bit 1), each keeping the
+// values whose index bit matches the lane's bit: 3 DPP adds and 6 selects,
+// against 8 DPP adds and 4 selects for four all-reduces.
+__device__ __forceinline__ float quad_reduce_scatter(const float (&p)[4], int lane) {
+    const bool b1 = lane & 2, b0 = lane & 1;
+    float q[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) q[m] = (b0 ? p[2 * m + 1] : p[2 * m]) + dpp<0xB1>(b0 ? p[2 * m] : p[2 * m + 1]);
+    return (b1 ? q[1] : q[0]) + dpp<0x4E>(b1 ? q[0] : q[1]);
+}
+
 // 4-byte direct global->LDS transfers of a tile: words [0, nw) of rows
 // [0, rows) of a region whose rows start rowb bytes apart at g, into LDS rows of
 // pw words at l.  LDS word e = 64 k + lane of instruction k holds word e % pw of
@@ -415,6 +428,7 @@ struct SplitWave {
             if (store) *yout = from_f32<IO>(yv);
         } else {
             float yown = 0.0f;
+            float pj[G];  // this lane's C.h term of each position (groups of 4: summed after the block)
             static_for<G>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 const float d2j = bcast<G, j>(d2);
@@ -443,9 +457,14 @@ struct SplitWave {
                     }
                     yp = i == 0 ? cv[0] * h[0] : __builtin_fmaf(cv[i], h[i], yp);
                 }
-                yp = group_sum<G>(yp);
-                yown = (g == j) ? yp : yown;
+                if constexpr (G == 4) {
+                    pj[j] = yp;
+                } else {
+                    yp = group_sum<G>(yp);
+                    yown = (g == j) ? yp : yown;
+                }
             });
+            if constexpr (G == 4) yown = quad_reduce_scatter(pj, lane);
             if (store) *yout = from_f32<IO>(yown + dpu);
         }
     }
