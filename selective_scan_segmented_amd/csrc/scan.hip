@@ -3,7 +3,6 @@
 #include "scan_kernel.h"
 
 #include <algorithm>
-#include <cstdlib>
 
 namespace sfm {
 
@@ -155,14 +154,15 @@ bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, i
         p.lds_bytes = w_lds;
     }
     p.slab_bytes = p.xs_bytes + p.ds_bytes;
-    // Staggered start (whole rows) when the whole grid is resident at once:
-    // dispatch round r (one workgroup per CU) delays its loads by r times the
-    // time HBM needs for one round's inputs at about 6.5 TB/s (65000 bytes per
-    // 10 ns tick).
+    // Staggered start (whole rows): dispatch round r (one workgroup per CU)
+    // of the rounds resident at launch delays its loads by r times the time
+    // HBM needs for one round's inputs at about 6.5 TB/s (65000 bytes per 10 ns
+    // tick); workgroups that start later, when a slot frees, take no delay (the
+    // launcher counts the resident rounds).  Stage-3 rows (two resident rounds
+    // of 2.5): 56.7 -> 56.2 us.
     p.stagger_period = 0;
     p.stagger_ticks = 0;
-    const int wg_per_cu = res / wpg;
-    if (!chunk && stagger_hint != 0 && grid > cus && grid <= (long long)cus * wg_per_cu) {
+    if (!chunk && stagger_hint != 0 && grid > cus) {
         const long long wg_bytes = (long long)wpg * cpw * (XL + L) * io_bytes + 2LL * N * L * io_bytes;
         long long ticks = stagger_hint > 0 ? stagger_hint : (long long)cus * wg_bytes / 65000;
         if (ticks > 500) ticks = 500;
