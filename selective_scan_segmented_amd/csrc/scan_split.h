@@ -625,16 +625,6 @@ __global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu
     __builtin_amdgcn_sched_barrier(0);
     issue(b1 * p.B2);
     // states n >= N: B = C = 0 for the whole launch (widening never writes them)
-    if (N < NS) {
-        for (int e = tid; e < L * NS; e += nthr) {
-            const int t = e / NS, n = e - t * NS;
-            if (n >= N) {
-                float* q = bc + (t * G + n / NPL) * (2 * NPL) + n % NPL;
-                q[0] = 0.0f;
-                q[NPL] = 0.0f;
-            }
-        }
-    }
     // every lane has a row of its own in the slabs (CPW rows are allocated);
     // the rows of channels past D are never loaded nor stored
     const IO* xr = xs + w.c * XL;
@@ -666,14 +656,34 @@ __global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu
             });
             w.mean = to_f32(Io<IO>::from_f64(s / (double)XL));
         }
-        {
-            // raw [2][N][L] -> float32 [t][g][B.., C..]
+        // raw [2][N][L] -> float32 [t][g][B.., C..] (states n >= N get B = C = 0).
+        // Four-lane groups (the planner's choice for long rows such as stage-3's):
+        // thread t widens position t, whose 2 NS floats are contiguous, by
+        // 16-byte stores (stage-3: 56.1 -> 54.9 us).  Two-lane groups spread the
+        // elements over every thread: at stage-4's 51 positions the per-position
+        // form leaves the work to one wave and its registers push the kernel's
+        // count from 110 to 125 (26.3 -> 27.3 us); both forms in one instance
+        // spill.
+        if constexpr (G == 4) {
+            for (int t = tid; t < L; t += nthr) {
+                float v[2 * NS];
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const int o = (n / NPL) * (2 * NPL) + n % NPL;
+                    v[o] = n < N ? to_f32(braw[n * L + t]) : 0.0f;
+                    v[o + NPL] = n < N ? to_f32(braw[(N + n) * L + t]) : 0.0f;
+                }
+                float4* q = reinterpret_cast<float4*>(bc + t * (2 * NS));
+#pragma unroll
+                for (int k = 0; k < NS / 2; ++k) q[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+            }
+        } else {
             const float invL = 1.0f / (float)L;
-            for (int e = tid; e < N * L; e += nthr) {
+            for (int e = tid; e < NS * L; e += nthr) {
                 const int n = div_small(e, invL), t = e - n * L;
                 float* q = bc + (t * G + n / NPL) * (2 * NPL) + n % NPL;
-                q[0] = to_f32(braw[e]);
-                q[NPL] = to_f32(braw[N * L + e]);
+                q[0] = n < N ? to_f32(braw[e]) : 0.0f;
+                q[NPL] = n < N ? to_f32(braw[N * L + e]) : 0.0f;
             }
         }
         __syncthreads();  // B/C of sample b visible to the group
