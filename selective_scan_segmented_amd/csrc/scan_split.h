@@ -779,30 +779,29 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_chunk_kernel(ScanParams
         const char* dg = reinterpret_cast<const char*>(static_cast<const IO*>(p.delta) + ((size_t)b * D + dw0) * L + t0);
         dma_tile4(dg, rowb, rows, nw, p.dpw, dtile, lane, p.dtile_insts);
     };
+    // raw B/C tiles -> float32 [q][g][B.., C..]: work item (q, g) widens the
+    // NPL states of lane-group member g at chunk position q, 2 NPL contiguous
+    // floats stored by 16-byte writes (states n >= N get B = C = 0)
     auto widen = [&](int len, int first_wave) __attribute__((always_inline)) {
         const int wthr = (p.wpg - first_wave) * kWave;
-        const float inv = 1.0f / (float)len;
         const IO* bt = reinterpret_cast<const IO*>(btile);
         const IO* ct = reinterpret_cast<const IO*>(ctile);
-        for (int e = tid - first_wave * kWave; e < N * len; e += wthr) {
-            const int n = div_small(e, inv), q = e - n * len;
-            float* o = bc + (q * G + n / NPL) * (2 * NPL) + n % NPL;
-            o[0] = to_f32(bt[n * p.bpw * ew + q]);
-            o[NPL] = to_f32(ct[n * p.bpw * ew + q]);
+        for (int e = tid - first_wave * kWave; e < len * G; e += wthr) {
+            const int q = e / G, gg = e - q * G;
+            float v[2 * NPL];
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+                const int n = gg * NPL + i;
+                v[i] = n < N ? to_f32(bt[n * p.bpw * ew + q]) : 0.0f;
+                v[NPL + i] = n < N ? to_f32(ct[n * p.bpw * ew + q]) : 0.0f;
+            }
+            float4* o = reinterpret_cast<float4*>(bc + e * (2 * NPL));
+#pragma unroll
+            for (int k = 0; k < NPL / 2; ++k) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
         }
     };
 
     w.load_params();
-    if (N < NS) {  // states n >= N: B = C = 0 for the whole launch (widening never writes them)
-        for (int e = tid; e < Q * NS; e += nthr) {
-            const int q = e / NS, n = e - q * NS;
-            if (n >= N) {
-                float* o = bc + (q * G + n / NPL) * (2 * NPL) + n % NPL;
-                o[0] = 0.0f;
-                o[NPL] = 0.0f;
-            }
-        }
-    }
     const IO* xr = xs + w.c * XL;
     IO* drow = reinterpret_cast<IO*>(dtile) + w.c * p.dpw * ew;  // this lane's delta/y tile row
     const int nch = (L + Q - 1) / Q;
