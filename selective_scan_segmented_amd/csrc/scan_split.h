@@ -589,7 +589,6 @@ __global__ __launch_bounds__(kWave * kMaxWpg) __attribute__((amdgpu_waves_per_eu
     const int L = p.L, XL = p.xrow, N = p.N, D = p.D;
     float* bc = reinterpret_cast<float*>(smem + p.bc_off);
     IO* braw = reinterpret_cast<IO*>(smem + p.braw_off);
-    float* means = reinterpret_cast<float*>(smem + p.mean_off);  // [wpg * 64/G]
     char* slab = smem + p.slab_off + (size_t)wave * p.slab_bytes;
     IO* xs = reinterpret_cast<IO*>(slab);
     IO* ds = reinterpret_cast<IO*>(slab + p.xs_bytes);
@@ -759,12 +758,10 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_chunk_kernel(ScanParams
     float* bc = reinterpret_cast<float*>(smem + p.bc_off);        // [Q][G][B.., C..] float32
     char* btile = smem + p.braw_off;                              // raw B rows [N][bpw words]
     char* ctile = btile + p.btile_insts * 256;                    // raw C rows
-    float* means = reinterpret_cast<float*>(smem + p.mean_off);
     char* slab = smem + p.slab_off + (size_t)wave * p.slab_bytes;
     IO* xs = reinterpret_cast<IO*>(slab);                         // [CPW][XL] whole rows
     char* dtile = slab + p.xs_bytes;                              // [CPW][dpw words]
     const int rows = w.rows;
-    const int nthr = p.wpg * kWave;
     const int tid = threadIdx.x;
 
     auto issue_bc = [&](int b, int t0, int len) __attribute__((always_inline)) {
@@ -824,33 +821,27 @@ __global__ __launch_bounds__(kWave * kMaxWpg) void split_chunk_kernel(ScanParams
             const int t0 = c * Q, len = min(Q, L - t0);
             wait_vmem();
             __syncthreads();  // this chunk's delta and raw B/C (and at c = 0 the x rows) have landed
-            if (c == 0) {
-                // the row means (first waves, one lane per channel of the group)
-                // and the first chunk's B/C (the others)
-                const int gch = p.wpg * CPW;
-                const int nmean = p.pad_in ? min(p.wpg, (gch + kWave - 1) / kWave) : 0;
-                if (wave < nmean) {
-                    const int r = wave * kWave + lane;
-                    const int ow = r / CPW, oc = r - ow * CPW;
-                    const int orows = max(0, min(CPW, D - (tile * p.wpg + ow) * CPW));
-                    if (r < gch && oc < orows) {
-                        const IO* row = reinterpret_cast<const IO*>(smem + p.slab_off + (size_t)ow * p.slab_bytes) +
-                                        oc * XL;
-                        // float64, index order, one rounding: bit-identical to the aux pad
-                        means[r] = to_f32(Io<IO>::from_f64(row_sum_f64(row, XL) / (double)XL));
-                    }
-                }
-                const int wb = nmean < p.wpg ? nmean : 0;
-                if (wave >= wb) widen(len, wb);
-            } else {
-                widen(len, 0);
+            if (c == 0 && p.pad_in) {
+                // the row means of this wave's channels, as the whole-row kernel
+                // takes them: lane g of a channel sums piece g of the row in
+                // float64 in index order, the G piece sums are added in piece
+                // order and rounded once (it replaced one lane per channel summing
+                // whole rows on the first waves while the others widened: base
+                // stage-3 275.3 -> 274.3 us)
+                const int qp = (XL + G - 1) / G;
+                const int i0 = min(w.g * qp, XL), i1 = min(i0 + qp, XL);
+                const double part = row_sum_f64(xr + i0, i1 - i0);
+                double s2 = 0.0;
+                static_for<G>([&](auto jc) {
+                    constexpr int jj = decltype(jc)::value;
+                    s2 += bcast_f64<G, jj>(part);
+                });
+                w.mean = to_f32(Io<IO>::from_f64(s2 / (double)XL));
             }
-            __syncthreads();  // B/C of the chunk (and the row means) visible to the group
+            widen(len, 0);
+            __syncthreads();  // B/C of the chunk visible to the group
             if (c + 1 < nch) issue_bc(b, t0 + Q, min(Q, L - t0 - Q));  // the raw B/C tiles are free again
-            if (c == 0) {
-                if (p.pad_in) w.mean = means[wave * CPW + w.c];
-                w.start(xr, h, win);
-            }
+            if (c == 0) w.start(xr, h, win);
             const int k0 = t0 / G;
             const int k1 = c + 1 == nch ? nblk : (t0 + len) / G;
             w.blocks(k0, k1, kA, kB, xr, drow - t0, bc - t0 * G * (2 * NPL), h, win);
