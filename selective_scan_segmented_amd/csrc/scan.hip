@@ -60,8 +60,11 @@ bool plan_split(ScanParams& p, int io_bytes, int split_hint, int stagger_hint, i
         if (((long long)cpw * XL * io_bytes) % 16) continue;
         if (whole_ok && !chunk_ok && ((long long)cpw * L * io_bytes) % 16) continue;
         G = g;
+        // about four waves per SIMD, a wave of a folded row counting once per
+        // sample it walks (stage-4 at B2 = 2: two lanes 32.8 us, four 34.0 us;
+        // stage-3 at B2 = 2: four lanes 69.6 us, two 104.6 us)
         const long long waves = (long long)p.B1 * ((D + cpw - 1) / cpw);
-        if (waves >= 4LL * 4 * cus) break;  // about four waves per SIMD
+        if (waves * p.B2 >= 4LL * 4 * cus) break;
     }
     if (!G) return false;
     const int cpw = kWave / G;
@@ -291,18 +294,19 @@ bool plan_scan(ScanParams& p, int io_bytes, int waves_hint, int ch_hint, int sta
     p.split = 0;
     // The lane-split kernel when asked for; when one wave per (sample,
     // 64-channel tile) would give the SIMDs fewer than two waves each; and, on
-    // unfolded rows, up to four each.  Measured on MI355X (same-process A/B):
-    // stage-3 shapes, 1.25 one-lane waves per SIMD: 67-71 vs 101-102 us;
-    // stage-4, 2.5 per SIMD, where the one-lane kernel leaves half the SIMDs
-    // with three waves: 29.8-32.7 vs 31.3-33.5 us with two lanes per channel
-    // (five balanced waves per SIMD); the base model's stage-3, 4 per SIMD:
-    // 312 vs 355 us.  Folded rows take their samples in turn on one lane-split
-    // wave but as separate pieces on the one-lane kernel: stage-4 at B2 = 2
-    // ties, at B2 = 4 the lane-split kernel loses (43.7 vs 35.6 us).
+    // rows of at most two samples, up to four each.  Measured on MI355X
+    // (same-process A/B): stage-3 shapes, 1.25 one-lane waves per SIMD: 67-71
+    // vs 101-102 us; stage-4, 2.5 per SIMD, where the one-lane kernel leaves
+    // half the SIMDs with three waves: 29.8-32.7 vs 31.3-33.5 us with two lanes
+    // per channel (five balanced waves per SIMD); the base model's stage-3, 4
+    // per SIMD: 312 vs 355 us.  Folded rows take their samples in turn on one
+    // lane-split wave but as separate pieces on the one-lane kernel: at B2 = 2
+    // the lane-split kernel wins (stage-4 32.8 vs 38.5 us, base stage-3 280.8
+    // vs 313.6 us), at B2 = 4 it loses (stage-4 40.9 vs 34.6 us).
     const int cus = device_cus();
     const long long lane_waves = (long long)p.B1 * p.B2 * ((p.D + kWave - 1) / kWave);
     const bool want_split = split_hint > 0 ||
-                            (split_hint < 0 && (lane_waves < 2LL * 4 * cus || (lane_waves <= 4LL * 4 * cus && p.B2 == 1)));
+                            (split_hint < 0 && (lane_waves < 2LL * 4 * cus || (lane_waves <= 4LL * 4 * cus && p.B2 <= 2)));
     if (want_split && waves_hint <= 0 && ch_hint <= 0) {
         // G = 2 or 4 first (fewer instructions per token); the streaming
         // kernel where those cannot stage the rows (long rows) or when asked for

@@ -284,7 +284,8 @@ def test_plans_of_the_benchmark_workloads():
     stage-3 rows whole on the four-lane kernel, the stagger also covering the
     two resident rounds of a grid larger than one round; the base model's
     stage-3 rows chunked on the two-lane kernel; the long rows streamed (16
-    lanes per channel); stage-4 folded pairs on the one-lane kernel."""
+    lanes per channel); stage-4 folded pairs on the two-lane kernel, folded
+    fours on the one-lane kernel (one piece per sample)."""
     plan = lambda *a: sfm.sfm_scan_plan_string(*a)
     assert plan(256, 1, 640, 8, 51, 4, "bf16", 3) == \
         "split=2 chunk=0 ns=8 wpg=4 lds=31008 grid=1280 block=256 stagger=107/256"
@@ -292,7 +293,8 @@ def test_plans_of_the_benchmark_workloads():
         "split=4 chunk=0 ns=8 wpg=4 lds=69696 grid=1280 block=256 stagger=223/256"
     assert plan(512, 1, 512, 16, 198, 4, "bf16", 3).startswith("split=2 chunk=64 ns=16 ")
     assert plan(16, 1, 320, 16, 4002, 4, "bf16", 3).startswith("split=16 chunk=240 ns=16 wpg=8 ")
-    assert plan(128, 2, 640, 8, 51, 4, "bf16", 3).startswith("mode=0 ch=51 pieces=2 ")
+    assert plan(128, 2, 640, 8, 51, 4, "bf16", 3).startswith("split=2 chunk=0 ")
+    assert plan(64, 4, 640, 8, 51, 4, "bf16", 3).startswith("mode=0 ch=51 pieces=4 ")
     # SFM_SCAN_STAGGER=0 turns the staggered start off
     import os
     os.environ["SFM_SCAN_STAGGER"] = "0"
